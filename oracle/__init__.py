@@ -1,0 +1,201 @@
+"""HiSparse CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Python access to the plain C oracle in ``hisparse_oracle.c``. Only the tests,
+``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may import
+this package. The GPU library and its binding never do.
+
+Every function takes and returns host numpy arrays. The swap-in updates the
+caller's state arrays (``slot_tokens``, ``lru``, ``hot``) in place, as the GPU
+call updates device state.
+
+Parity pins (the tests under ``tests/test_oracle_*.py``):
+  * an ``OrderedDict`` LRU model and, at top_k = 1, the textbook LRU cache;
+  * closed forms for a cold start, a repeated step and a disjoint step;
+  * invariants after every step of every workload trace;
+  * hand-derived worked examples under ``tests/golden/``;
+  * numpy fancy indexing for both row copies.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hisparse_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_hisparse.so")
+
+ORACLE_OK = 0
+ERRORS = {
+    -1: "ORACLE_EARG", -2: "ORACLE_EDUP_ID", -3: "ORACLE_ELRU", -4: "ORACLE_EROWS",
+    -5: "ORACLE_EHOT", -6: "ORACLE_ESTATE", -7: "ORACLE_EINDEX",
+}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle precondition failed: {ERRORS.get(code, code)}")
+        self.code = code
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C11, -O2)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+            os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "hisparse_oracle.h"))):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared",
+                               "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _SwapArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("S_r", ctypes.c_int64), ("R", ctypes.c_int64),
+        ("topk", ctypes.c_void_p), ("topk_stride", ctypes.c_int64),
+        ("req_rows", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("num_real", ctypes.c_int32),
+        ("slot_tokens", ctypes.c_void_p), ("lru", ctypes.c_void_p),
+        ("slot_rows", ctypes.c_void_p), ("pool_rows", ctypes.c_void_p),
+        ("ctx_stride", ctypes.c_int64),
+        ("pool", ctypes.c_void_p), ("pool_nrows", ctypes.c_int64),
+        ("hot", ctypes.c_void_p), ("hot_nrows", ctypes.c_int64),
+        ("row_bytes", ctypes.c_int64),
+        ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def _load(path: Optional[str] = None):
+    global _lib
+    if _lib is None or path is not None:
+        lib = ctypes.CDLL(path or build())
+        lib.oracle_swap_in.argtypes = [ctypes.POINTER(_SwapArgs)]
+        lib.oracle_swap_in.restype = ctypes.c_int
+        lib.oracle_transfer_rows_all_layer.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
+        lib.oracle_transfer_rows_all_layer.restype = ctypes.c_int64
+        lib.oracle_store_kv_scatter.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_store_kv_scatter.restype = ctypes.c_int64
+        lib.oracle_state_reset.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_state_reset.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def use_library(path: Optional[str]) -> None:
+    """Point this module at another build of the oracle source (the mutation
+    tests load copies with planted mistakes); ``None`` returns to the real one."""
+    global _lib
+    _lib = None
+    if path is not None:
+        _load(path)
+
+
+def _ptr(a: Optional[np.ndarray], dtype, writable: bool = False) -> Optional[int]:
+    if a is None:
+        return None
+    assert a.dtype == dtype, (a.dtype, dtype)
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    if writable:
+        assert a.flags["WRITEABLE"]
+    return a.ctypes.data
+
+
+def _rows_ptr(a: np.ndarray, dtype) -> int:
+    """Pointer to a 2-D array whose rows may be strided but whose columns are contiguous."""
+    assert a.dtype == dtype and a.ndim == 2 and (a.strides[1] == a.itemsize or a.shape[1] <= 1)
+    if a.shape[0] > 1:
+        assert a.strides[0] % a.itemsize == 0 and a.strides[0] >= a.shape[1] * a.itemsize
+    return a.ctypes.data
+
+
+def _row_stride(a: np.ndarray) -> int:
+    return a.strides[0] // a.itemsize if a.shape[0] > 1 else a.shape[1]
+
+
+def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
+            slot_tokens: np.ndarray, lru: np.ndarray, pool: np.ndarray, hot: np.ndarray,
+            ctx_stride: int, num_real: int = -1, slot_rows: Optional[np.ndarray] = None,
+            pool_rows: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None,
+            miss_counts: Optional[np.ndarray] = None):
+    """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``.
+
+    ``pool`` and ``hot`` are ``uint8[nrows, row_bytes]``. State arrays are updated in place.
+    """
+    B, K = topk.shape
+    R, S_r = slot_tokens.shape
+    H = lru.shape[1]
+    assert lru.shape[0] == R and pool.shape[1] == hot.shape[1]
+    if out_rows is None:
+        out_rows = np.empty((B, K), dtype=np.int32)
+    if miss_counts is None:
+        miss_counts = np.empty(B, dtype=np.int32)
+    a = _SwapArgs(
+        B=B, K=K, H=H, S_r=S_r, R=R,
+        topk=_rows_ptr(topk, np.int32), topk_stride=_row_stride(topk),
+        req_rows=_ptr(req_rows, np.int64), seq_lens=_ptr(seq_lens, np.int64),
+        num_real=num_real,
+        slot_tokens=_ptr(slot_tokens, np.int32, True), lru=_ptr(lru, np.int16, True),
+        slot_rows=_ptr(slot_rows, np.int32), pool_rows=_ptr(pool_rows, np.int64),
+        ctx_stride=ctx_stride,
+        pool=_ptr(pool, np.uint8), pool_nrows=pool.shape[0],
+        hot=_ptr(hot, np.uint8, True), hot_nrows=hot.shape[0],
+        row_bytes=pool.shape[1],
+        out_rows=_ptr(out_rows, np.int32, True), miss_counts=_ptr(miss_counts, np.int32, True))
+    rc = _load().oracle_swap_in(ctypes.byref(a))
+    if rc != ORACLE_OK:
+        raise OracleError(rc)
+    return out_rows, miss_counts
+
+
+def transfer_rows_all_layer(src_layers: Sequence[np.ndarray], dst_layers: Sequence[np.ndarray],
+                            src_idx: np.ndarray, dst_idx: np.ndarray) -> int:
+    """``dst_layers[l][dst_idx[i]] = src_layers[l][src_idx[i]]``; returns the pairs skipped."""
+    L = len(src_layers)
+    assert len(dst_layers) == L and L > 0
+    rb = src_layers[0].shape[1]
+    for s, d in zip(src_layers, dst_layers):
+        assert s.shape[1] == rb and d.shape[1] == rb
+        assert s.shape[0] == src_layers[0].shape[0] and d.shape[0] == dst_layers[0].shape[0]
+    sp = (ctypes.c_void_p * L)(*[_ptr(s, np.uint8) for s in src_layers])
+    dp = (ctypes.c_void_p * L)(*[_ptr(d, np.uint8, True) for d in dst_layers])
+    r = _load().oracle_transfer_rows_all_layer(
+        sp, dp, src_layers[0].shape[0], dst_layers[0].shape[0], _ptr(src_idx, np.int64),
+        _ptr(dst_idx, np.int64), src_idx.shape[0], L, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
+
+
+def store_kv_scatter(src: np.ndarray, dst: np.ndarray, loc: np.ndarray) -> int:
+    """``dst[loc[j]] = src[j]`` over rows of ``src.shape[1]`` bytes; returns rows skipped."""
+    n, rb = src.shape
+    assert dst.shape[1] >= rb and src.strides[1] == 1 and dst.strides[1] == 1
+    r = _load().oracle_store_kv_scatter(
+        src.ctypes.data, src.strides[0], dst.ctypes.data, dst.strides[0], dst.shape[0],
+        _ptr(loc, np.int64), n, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
+
+
+def state_reset(slot_tokens: np.ndarray, lru: np.ndarray, rows: Sequence[int]) -> None:
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R, S_r = slot_tokens.shape
+    rc = _load().oracle_state_reset(_ptr(slot_tokens, np.int32, True), _ptr(lru, np.int16, True),
+                                    rows.ctypes.data, rows.shape[0], lru.shape[1], S_r, R)
+    if rc != ORACLE_OK:
+        raise OracleError(rc)

@@ -1,0 +1,245 @@
+/*
+ * HiSparse CPU oracle -- TEST INFRASTRUCTURE ONLY (see hisparse_oracle.h).
+ *
+ * Written for a reader checking it against the pages by eye: one batch row at
+ * a time, the steps in the order the pages' swap-in kernels take them, plain
+ * arrays and libc qsort/bsearch for membership. The GPU library shares no code
+ * with this file.
+ *
+ * Readings where the pages are silent or disagree (each also applies to the
+ * GPU path):
+ *  - Membership instead of a hash. Both pages insert the top-k ids into an
+ *    open-addressing table and probe it with each resident slot's token; the
+ *    result they use is only "is this token among the pending ids, and at
+ *    which top-k index". A sorted array answers the same question.
+ *  - Invalid ids. An id outside [0, seq_len), at or past ctx_stride, or whose
+ *    pool row falls outside the pool, is output as -1, is not copied and is
+ *    not counted (the vLLM page maps out-of-range ids to -1 the same way).
+ *  - Padding. A batch row at or past num_real, or whose state row lies
+ *    outside [0, R), gets -1 in every output and a miss count of 0 (the vLLM
+ *    page's choice for padded rows; the SGLang page writes nothing).
+ *  - The newest token is bound to slot H of its region (SGLang page,
+ *    "newest_slot"), is never hashed, copied or counted, and slot H never
+ *    enters the LRU.
+ */
+#include "hisparse_oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t token;  /* in-request position */
+  int32_t index;  /* top-k column */
+  int32_t hit;    /* set when an LRU slot holds this token */
+} pending_t;
+
+static int cmp_by_token(const void *x, const void *y) {
+  const pending_t *a = (const pending_t *)x, *b = (const pending_t *)y;
+  return (a->token > b->token) - (a->token < b->token);
+}
+
+static int cmp_by_index(const void *x, const void *y) {
+  const pending_t *a = (const pending_t *)x, *b = (const pending_t *)y;
+  return (a->index > b->index) - (a->index < b->index);
+}
+
+/* Row(r, s): the hot-buffer row of slot s of state row r. The SGLang page
+ * reads it from device_buffer_locs; with no table it is the flat region. */
+static int64_t hot_row(const oracle_swap_in_args *a, int64_t r, int64_t s) {
+  return a->slot_rows ? (int64_t)a->slot_rows[r * a->S_r + s] : r * a->S_r + s;
+}
+
+/* The pool row holding token t of state row r (SGLang page: host_cache_locs). */
+static int64_t pool_row(const oracle_swap_in_args *a, int64_t r, int64_t t) {
+  return a->pool_rows ? a->pool_rows[r * a->ctx_stride + t] : r * a->ctx_stride + t;
+}
+
+static int check_args(const oracle_swap_in_args *a) {
+  if (!a || a->B < 0 || a->K < 0 || a->H < 0 || a->R < 0) return ORACLE_EARG;
+  if (a->B == 0 || a->K == 0) return ORACLE_OK;
+  if (!a->topk || !a->req_rows || !a->seq_lens || !a->slot_tokens || !a->lru ||
+      !a->pool || !a->hot || !a->out_rows)
+    return ORACLE_EARG;
+  if (a->H < a->K || a->S_r < (int64_t)a->H + 1 || a->topk_stride < a->K || a->row_bytes <= 0 ||
+      a->ctx_stride <= 0)
+    return ORACLE_EARG;
+  return ORACLE_OK;
+}
+
+/* Preconditions the pages state or imply, checked up front so a broken input
+ * never produces a plausible-looking answer. */
+static int check_state_rows(const oracle_swap_in_args *a, int32_t nreal) {
+  /* One block owns one request's region (SGLang page, one block per request):
+   * real rows must name distinct state rows. */
+  for (int32_t b = 0; b < nreal; ++b) {
+    int64_t r = a->req_rows[b];
+    if (r < 0 || r >= a->R) continue;
+    for (int32_t c = b + 1; c < nreal; ++c)
+      if (a->req_rows[c] == r) return ORACLE_EROWS;
+    /* The LRU row is a permutation of the H slot ids. */
+    char *seen = (char *)calloc((size_t)a->H, 1);
+    if (!seen) return ORACLE_EARG;
+    for (int32_t p = 0; p < a->H; ++p) {
+      int32_t s = a->lru[r * a->H + p];
+      if (s < 0 || s >= a->H || seen[s]) { free(seen); return ORACLE_ELRU; }
+      seen[s] = 1;
+    }
+    free(seen);
+    /* Every hot row a slot can name lies inside the hot buffer. */
+    for (int64_t s = 0; s <= a->H; ++s) {
+      int64_t hr = hot_row(a, r, s);
+      if (hr < 0 || hr >= a->hot_nrows) return ORACLE_EHOT;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swap_in(const oracle_swap_in_args *a) {
+  int rc = check_args(a);
+  if (rc != ORACLE_OK || a->B == 0 || a->K == 0) return rc;
+  const int32_t B = a->B, K = a->K, H = a->H;
+  const int32_t nreal = (a->num_real >= 0 && a->num_real < B) ? a->num_real : B;
+  rc = check_state_rows(a, nreal);
+  if (rc != ORACLE_OK) return rc;
+
+  pending_t *pending = (pending_t *)malloc(sizeof(pending_t) * (size_t)K);
+  int16_t *hits = (int16_t *)malloc(sizeof(int16_t) * (size_t)H);
+  int16_t *evict = (int16_t *)malloc(sizeof(int16_t) * (size_t)H);
+  int16_t *new_lru = (int16_t *)malloc(sizeof(int16_t) * (size_t)H);
+  if (!pending || !hits || !evict || !new_lru) {
+    free(pending); free(hits); free(evict); free(new_lru);
+    return ORACLE_EARG;
+  }
+
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t *out = a->out_rows + (int64_t)b * K;
+    const int32_t *ids = a->topk + (int64_t)b * a->topk_stride;
+    const int64_t r = a->req_rows[b];
+
+    /* Padding rows: -1 outputs and a zero count (vLLM page, V2 padding). */
+    if (b >= nreal || r < 0 || r >= a->R) {
+      for (int32_t i = 0; i < K; ++i) out[i] = -1;
+      if (a->miss_counts) a->miss_counts[b] = 0;
+      continue;
+    }
+    const int64_t L = a->seq_lens[b];
+    const int64_t newest = L - 1;
+    int32_t *tokens = a->slot_tokens + r * a->S_r;
+    int16_t *lru = a->lru + r * H;
+
+    /* Step 1 (both pages' first loop): classify each top-k entry. The newest
+     * token binds to slot H; everything else valid becomes pending. */
+    int32_t np = 0;
+    for (int32_t i = 0; i < K; ++i) {
+      const int64_t t = ids[i];
+      if (t < 0 || t >= L || t >= a->ctx_stride) { out[i] = -1; continue; }
+      const int64_t pr = pool_row(a, r, t);
+      if (pr < 0 || pr >= a->pool_nrows) { out[i] = -1; continue; }
+      if (t == newest) { out[i] = (int32_t)hot_row(a, r, H); continue; }
+      pending[np].token = (int32_t)t;
+      pending[np].index = i;
+      pending[np].hit = 0;
+      ++np;
+    }
+    qsort(pending, (size_t)np, sizeof(pending_t), cmp_by_token);
+    for (int32_t j = 1; j < np; ++j)
+      if (pending[j].token == pending[j - 1].token) { rc = ORACLE_EDUP_ID; goto done; }
+
+    /* Step 2 (both pages' LRU scan): walk slots oldest first. A slot whose
+     * token is pending is a hit and serves that entry; every other slot is
+     * evictable. Both lists keep LRU order. */
+    int32_t nh = 0, ne = 0;
+    for (int32_t p = 0; p < H; ++p) {
+      const int16_t s = lru[p];
+      const int32_t tok = tokens[s];
+      pending_t key = {tok, 0, 0};
+      pending_t *f = tok >= 0 ? (pending_t *)bsearch(&key, pending, (size_t)np, sizeof(pending_t),
+                                                     cmp_by_token)
+                              : NULL;
+      if (f) {
+        if (f->hit) { rc = ORACLE_ESTATE; goto done; }
+        f->hit = 1;
+        out[f->index] = (int32_t)hot_row(a, r, s);
+        hits[nh++] = s;
+      } else {
+        evict[ne++] = s;
+      }
+    }
+
+    /* Step 3 (both pages' miss pass): pending entries that were not hit, in
+     * ascending top-k index; miss m takes the m-th oldest evictable slot,
+     * the table records the new owner and the row is copied in. */
+    qsort(pending, (size_t)np, sizeof(pending_t), cmp_by_index);
+    int32_t M = 0;
+    for (int32_t j = 0; j < np; ++j) {
+      if (pending[j].hit) continue;
+      const int16_t v = evict[M];   /* M < ne because H >= K */
+      const int64_t dst = hot_row(a, r, v);
+      const int64_t src = pool_row(a, r, pending[j].token);
+      out[pending[j].index] = (int32_t)dst;
+      tokens[v] = pending[j].token;
+      memcpy(a->hot + dst * a->row_bytes, a->pool + src * a->row_bytes, (size_t)a->row_bytes);
+      ++M;
+    }
+
+    /* Step 4 (LRU write-back): stale evictables first, then the slots just
+     * filled in miss order, then the hits, each group in its old order. */
+    int32_t q = 0;
+    for (int32_t e = M; e < ne; ++e) new_lru[q++] = evict[e];
+    for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];
+    for (int32_t h = 0; h < nh; ++h) new_lru[q++] = hits[h];
+    memcpy(lru, new_lru, sizeof(int16_t) * (size_t)H);
+
+    if (a->miss_counts) a->miss_counts[b] = M;
+  }
+
+done:
+  free(pending); free(hits); free(evict); free(new_lru);
+  return rc;
+}
+
+int64_t oracle_transfer_rows_all_layer(const uint8_t *const *src_layers, uint8_t *const *dst_layers,
+                                       int64_t src_nrows, int64_t dst_nrows,
+                                       const int64_t *src_idx, const int64_t *dst_idx, int64_t n,
+                                       int32_t num_layers, int64_t row_bytes) {
+  if (n < 0 || num_layers < 0 || row_bytes <= 0) return ORACLE_EARG;
+  if (n == 0 || num_layers == 0) return 0;
+  if (!src_layers || !dst_layers || !src_idx || !dst_idx) return ORACLE_EARG;
+  int64_t skipped = 0;
+  /* tokenspeed page, all-layer MLA transfer: for every index pair, for every
+   * layer, copy one row. */
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t s = src_idx[i], d = dst_idx[i];
+    if (s < 0 || s >= src_nrows || d < 0 || d >= dst_nrows) { ++skipped; continue; }
+    for (int32_t l = 0; l < num_layers; ++l)
+      memcpy(dst_layers[l] + d * row_bytes, src_layers[l] + s * row_bytes, (size_t)row_bytes);
+  }
+  return skipped;
+}
+
+int64_t oracle_store_kv_scatter(const uint8_t *src, int64_t src_row_stride_bytes,
+                                uint8_t *dst, int64_t dst_row_stride_bytes, int64_t dst_nrows,
+                                const int64_t *loc, int64_t n, int64_t row_bytes) {
+  if (n < 0 || row_bytes <= 0) return ORACLE_EARG;
+  if (n == 0) return 0;
+  if (!src || !dst || !loc) return ORACLE_EARG;
+  int64_t skipped = 0;
+  /* tokenspeed page, _store_kv_cache_kernel (K half): row j goes to loc[j]. */
+  for (int64_t j = 0; j < n; ++j) {
+    if (loc[j] < 0 || loc[j] >= dst_nrows) { ++skipped; continue; }
+    memcpy(dst + loc[j] * dst_row_stride_bytes, src + j * src_row_stride_bytes, (size_t)row_bytes);
+  }
+  return skipped;
+}
+
+int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,
+                       int32_t H, int64_t S_r, int64_t R) {
+  if (!slot_tokens || !lru || !rows || n_rows < 0 || H < 0 || S_r < H) return ORACLE_EARG;
+  for (int64_t j = 0; j < n_rows; ++j) {
+    const int64_t r = rows[j];
+    if (r < 0 || r >= R) return ORACLE_EARG;
+    for (int64_t s = 0; s < S_r; ++s) slot_tokens[r * S_r + s] = -1;
+    for (int32_t p = 0; p < H; ++p) lru[r * H + p] = (int16_t)p;
+  }
+  return ORACLE_OK;
+}

@@ -1,0 +1,88 @@
+/*
+ * HiSparse CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C reference of what the HiSparse decode-time
+ * swap-in, the fused all-layer indexed row transfer and the KV-row scatter
+ * compute. Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load it. The GPU library neither includes nor links it, and
+ * this file shares no code with the GPU library.
+ *
+ * Sources (cited by page title and function):
+ *   [SGL]  SGLang hisparse.cuh, load_cache_to_device_buffer_kernel and
+ *          transfer_cache_dsv4_mla_kernel.
+ *   [VLLM] vLLM hisparse_kernels.cu, hisparse_resolve_residency_kernel,
+ *          hisparse_gather_compact_kernel.
+ *   [TS]   tokenspeed kvcache/triton.py, _store_kv_cache_kernel and
+ *          _kv_transfer_all_layer_mla_kernel.
+ *
+ * All arrays are host memory and row-major. Nothing here is floating point.
+ */
+#ifndef HISPARSE_ORACLE_H
+#define HISPARSE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_EARG = -1,      /* bad sizes or NULL pointers */
+  ORACLE_EDUP_ID = -2,   /* a valid top-k id repeats within one batch row */
+  ORACLE_ELRU = -3,      /* lru row is not a permutation of [0, H) */
+  ORACLE_EROWS = -4,     /* two real batch rows share one state row */
+  ORACLE_EHOT = -5,      /* a hot-row index falls outside the hot buffer */
+  ORACLE_ESTATE = -6,    /* one valid token resident in two LRU slots */
+  ORACLE_EINDEX = -7     /* transfer/scatter index outside its buffer */
+};
+
+typedef struct {
+  int32_t B, K, H;          /* batch rows, top_k, hot_size */
+  int64_t S_r, R;           /* region_stride (>= H+1), state rows */
+  const int32_t *topk;      /* [B, topk_stride] in-request token positions */
+  int64_t topk_stride;
+  const int64_t *req_rows;  /* [B] state row of each batch row */
+  const int64_t *seq_lens;  /* [B]; newest token = seq_len - 1 */
+  int32_t num_real;         /* rows b >= num_real are padding; < 0 = none */
+  int32_t *slot_tokens;     /* [R, S_r] in/out, -1 = empty */
+  int16_t *lru;             /* [R, H] in/out, LRU first */
+  const int32_t *slot_rows; /* [R, S_r] or NULL: hot row = r*S_r + s */
+  const int64_t *pool_rows; /* [R, ctx_stride] or NULL: pool row = r*ctx_stride + t */
+  int64_t ctx_stride;
+  const uint8_t *pool;      /* [pool_nrows, row_bytes] */
+  int64_t pool_nrows;
+  uint8_t *hot;             /* [hot_nrows, row_bytes] */
+  int64_t hot_nrows;
+  int64_t row_bytes;
+  int32_t *out_rows;        /* [B, K] */
+  int32_t *miss_counts;     /* [B] or NULL */
+} oracle_swap_in_args;
+
+/* One decode-step swap-in call. Returns ORACLE_OK or a negative code when a
+ * precondition of the pages is broken; outputs are then unspecified. */
+int oracle_swap_in(const oracle_swap_in_args *a);
+
+/* dst_layers[l][dst_idx[i]] <- src_layers[l][src_idx[i]] for every pair i and
+ * layer l (row_bytes bytes each). Pairs with an index outside [0, nrows) are
+ * skipped and counted; returns the number skipped, or ORACLE_EARG. */
+int64_t oracle_transfer_rows_all_layer(const uint8_t *const *src_layers, uint8_t *const *dst_layers,
+                                       int64_t src_nrows, int64_t dst_nrows,
+                                       const int64_t *src_idx, const int64_t *dst_idx, int64_t n,
+                                       int32_t num_layers, int64_t row_bytes);
+
+/* dst row loc[j] <- src row j for j < n; entries with loc outside
+ * [0, dst_nrows) are skipped. Returns the number skipped, or ORACLE_EARG. */
+int64_t oracle_store_kv_scatter(const uint8_t *src, int64_t src_row_stride_bytes,
+                                uint8_t *dst, int64_t dst_row_stride_bytes, int64_t dst_nrows,
+                                const int64_t *loc, int64_t n, int64_t row_bytes);
+
+/* Initial state of the listed state rows: every token -1, LRU = 0..H-1. */
+int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,
+                       int32_t H, int64_t S_r, int64_t R);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

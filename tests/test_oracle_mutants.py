@@ -1,0 +1,87 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies ``oracle/hisparse_oracle.c``, plants one mistake by text
+substitution, builds it with gcc into a temporary library, points the oracle
+module at it and runs a quick subset of the pins. Every mutant must fail at
+least one pin. Nothing here touches the real oracle build."""
+
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hisparse_oracle.c")
+
+MUTANTS = {
+    "victim_from_newest_end": ("const int16_t v = evict[M];", "const int16_t v = evict[ne - 1 - M];"),
+    "hits_before_fills": ("for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];\n"
+                          "    for (int32_t h = 0; h < nh; ++h) new_lru[q++] = hits[h];",
+                          "for (int32_t h = 0; h < nh; ++h) new_lru[q++] = hits[h];\n"
+                          "    for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];"),
+    "fills_before_stale": ("for (int32_t e = M; e < ne; ++e) new_lru[q++] = evict[e];\n"
+                           "    for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];",
+                           "for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];\n"
+                           "    for (int32_t e = M; e < ne; ++e) new_lru[q++] = evict[e];"),
+    "newest_not_bound": ("if (t == newest) {", "if (t == L) {"),
+    "pool_row_off_by_one": ("const int64_t src = pool_row(a, r, pending[j].token);",
+                            "const int64_t src = pool_row(a, r, pending[j].token) + 1;"),
+    "misses_in_token_order": ("qsort(pending, (size_t)np, sizeof(pending_t), cmp_by_index);", ""),
+    "table_not_updated": ("tokens[v] = pending[j].token;", ""),
+    "seq_len_bound_inclusive": ("if (t < 0 || t >= L || t >= a->ctx_stride)",
+                                "if (t < 0 || t > L || t >= a->ctx_stride)"),
+    "newest_slot_off_by_one": ("out[i] = (int32_t)hot_row(a, r, H);", "out[i] = (int32_t)hot_row(a, r, H - 1);"),
+    "hit_output_wrong_slot": ("out[f->index] = (int32_t)hot_row(a, r, s);",
+                              "out[f->index] = (int32_t)hot_row(a, r, p);"),
+    "lru_transposed_index": ("const int16_t s = lru[p];", "const int16_t s = (int16_t)p;"),
+    "no_padding": ("if (b >= nreal || r < 0 || r >= a->R) {", "if (r < 0 || r >= a->R) {"),
+}
+
+
+def _pins():
+    """A quick subset of the pins; returns the names of those that failed."""
+    import test_oracle_closed_forms as cf
+    import test_oracle_golden as g
+    import test_oracle_model as m
+    failed = []
+    checks = [
+        ("golden1", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_1.json")),
+        ("golden2", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_2.json")),
+        ("model_random", lambda: m.test_random_multirow_with_tables(0)),
+        ("textbook_lru", lambda: m.test_topk1_is_textbook_lru(4, 9, 1)),
+        ("cold", lambda: cf.test_cold_start(64, 16)),
+        ("disjoint", lambda: cf.test_disjoint_step_evicts_oldest(0)),
+    ]
+    for name, fn in checks:
+        try:
+            fn()
+        except (AssertionError, oracle.OracleError):
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_passes_pins():
+    oracle.use_library(None)
+    assert _pins() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "mutant.c")
+        open(c, "w").write(src.replace(old, new))
+        lib = os.path.join(d, "libmutant.so")
+        subprocess.check_call(["gcc", "-std=c11", "-O1", "-w", "-fPIC", "-shared",
+                               "-I", os.path.dirname(SRC), "-o", lib, c])
+        oracle.use_library(lib)
+        try:
+            failed = _pins()
+        finally:
+            oracle.use_library(None)
+    assert failed, f"mutant {name} passed every pin"
