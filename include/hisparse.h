@@ -1,0 +1,195 @@
+/*
+ * hisparse.h -- C ABI of the MI355X HiSparse swap-in library (libhisparse.so).
+ *
+ * HiSparse keeps each request's whole KV cache in a pool (pinned host memory
+ * or HBM) and only a small per-request working set of rows in an HBM "hot
+ * buffer". Every decode step, sparse attention names the top-k token ids it
+ * will read; the swap-in makes those rows resident and returns the hot-buffer
+ * row of each one.
+ *
+ * Sources, cited by page title and the function on it:
+ *   SGLang hisparse.cuh        -- load_cache_to_device_buffer_kernel (the swap-in),
+ *                                 transfer_cache_dsv4_mla_kernel (all-layer copy).
+ *   vLLM hisparse_kernels.cu   -- hisparse_resolve_residency_kernel (the swap-in's
+ *                                 resolution half), hisparse_gather_compact_kernel
+ *                                 (its copy half), host argument checks.
+ *   tokenspeed kvcache/triton.py -- _kv_transfer_all_layer_mla_kernel,
+ *                                 _store_kv_cache_kernel.
+ *
+ * Conventions for every call:
+ *   - All pointers are caller-owned. The library allocates no device memory
+ *     and keeps no state between calls beyond a per-device attribute cache.
+ *   - "device" pointers are HBM allocations of the current HIP device. The
+ *     swap-in pool may instead be pinned host memory (hipHostMalloc), which
+ *     kernels read directly over the host link.
+ *   - Work is enqueued on `stream` and is asynchronous: outputs and updated
+ *     state are valid once the stream reaches that point.
+ *   - Host-side validation failures return a negative hs_status, enqueue
+ *     nothing, and leave a message for hisparse_last_error(). Nothing else is
+ *     reported from the device: entries a kernel cannot serve are written as -1.
+ *   - Everything is integer or opaque bytes; there is no floating point.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_EINVAL = -1,      /* a NULL pointer, bad size, stride or alignment */
+  HS_ERANGE = -2,      /* sizes beyond what the kernels support (see each call) */
+  HS_EMEMKIND = -3,    /* pool is neither device memory nor pinned host memory */
+  HS_ELAUNCH = -4,     /* the HIP runtime rejected a launch */
+  HS_EWORKSPACE = -5   /* workspace missing, too small or misaligned */
+} hs_status;
+
+/*
+ * Arguments of one swap-in call.
+ *
+ * Per-request state, one row per request ("state row"), persists across calls:
+ *   slot_tokens [R, S_r] int32 : token held by each slot of the request's hot
+ *                                region, -1 = empty. Slots 0..H-1 are managed by
+ *                                the LRU; slot H holds the request's newest token
+ *                                and is written by the caller (store_kv_scatter),
+ *                                never by the swap-in (SGLang hisparse.cuh,
+ *                                region comment and newest_slot).
+ *   lru         [R, H]   int16 : permutation of 0..H-1, least recently used first
+ *                                (both pages' lru_slots).
+ * Initial state: slot_tokens all -1, lru = 0..H-1 (hisparse_state_reset).
+ *
+ * Row(r, s) = slot_rows ? slot_rows[r*S_r + s] : r*S_r + s   is the hot-buffer
+ * row of slot s of state row r (SGLang: device_buffer_locs).
+ * pool_row(r, t) = pool_rows ? pool_rows[r*ctx_stride + t] : r*ctx_stride + t
+ * is the pool row holding token t of state row r (SGLang: host_cache_locs).
+ */
+typedef struct hs_swap_in_args {
+  int32_t B;                 /* batch rows in this call                          */
+  int32_t K;                 /* top_k ids per batch row, 0 < K <= H              */
+  int32_t H;                 /* hot_size: LRU slots per request, H <= 32768      */
+  int64_t S_r;               /* region_stride of slot_tokens / slot_rows, >= H+1 */
+  int64_t R;                 /* state rows in slot_tokens / lru                  */
+
+  const int32_t* topk_ids;   /* device [B, topk_stride]: in-request token ids    */
+  int64_t topk_stride;       /* elements between batch rows, >= K                */
+  const int64_t* req_rows;   /* device [B]: state row of each batch row          */
+  const int64_t* seq_lens;   /* device [B]: tokens so far; newest id = seq_len-1 */
+  const int32_t* num_real;   /* device [1] or NULL: rows b >= *num_real are      */
+                             /* padding (all outputs -1, count 0)                */
+
+  int32_t* slot_tokens;      /* device [R, S_r], in/out                          */
+  int16_t* lru;              /* device [R, H], in/out                            */
+  const int32_t* slot_rows;  /* device [R, S_r] or NULL (flat regions)           */
+  const int64_t* pool_rows;  /* device [R, ctx_stride] or NULL (flat pool)       */
+  int64_t ctx_stride;        /* pool rows per request; ids >= ctx_stride invalid */
+
+  const void* pool;          /* [pool_nrows, row_bytes] pinned host or device    */
+  int64_t pool_nrows;
+  void* hot;                 /* device [hot_nrows, row_bytes]                    */
+  int64_t hot_nrows;
+  int64_t row_bytes;         /* opaque row size, > 0 and a multiple of 4         */
+
+  int32_t* out_rows;         /* device [B, K] out: hot row per entry, or -1      */
+  int32_t* miss_counts;      /* device [B] out, or NULL: rows copied per row     */
+} hs_swap_in_args;
+
+/* Bytes of device workspace hisparse_swap_in needs for B rows of K ids
+ * (the compacted miss list handed from resolution to the copy). */
+size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K);
+
+/*
+ * hisparse_swap_in -- one decode step of the HiSparse swap-in.
+ * SGLang hisparse.cuh, load_cache_to_device_buffer_kernel; vLLM
+ * hisparse_kernels.cu, hisparse_resolve_residency_kernel +
+ * hisparse_gather_compact_kernel.
+ *
+ * For each real batch row b with state row r and seq_len L:
+ *   1. id t is invalid if t < 0, t >= L, t >= ctx_stride, or pool_row(r,t) is
+ *      outside [0, pool_nrows): out = -1. t == L-1 (the newest token) gets
+ *      out = Row(r, H). Every other id is pending.
+ *   2. Walking lru[r] oldest first, a slot whose token is pending is a hit: that
+ *      entry gets out = Row(r, slot). All other slots are evictable, in LRU order.
+ *   3. Pending ids that were not hit, in ascending top-k index, are misses; miss
+ *      m takes the m-th oldest evictable slot v: out = Row(r, v),
+ *      slot_tokens[r][v] = t, and row_bytes bytes are copied from pool row
+ *      pool_row(r, t) to hot row Row(r, v).
+ *   4. lru[r] becomes: remaining evictables, then the filled slots in miss order,
+ *      then the hits, each group in its previous order.
+ *   5. miss_counts[b] = number of misses.
+ *
+ * Preconditions the caller guarantees (not checked on the device): valid ids
+ * are unique within a batch row; real rows name distinct state rows; lru rows
+ * are permutations; resident tokens in slots 0..H-1 are distinct; pool, hot
+ * buffer and state arrays do not overlap. Breaking them cannot make a kernel
+ * access memory outside the buffers described here, but results are then
+ * unspecified.
+ *
+ * workspace: device memory of at least hs_swap_in_workspace_bytes(B, K) bytes,
+ * 256-byte aligned, owned by the caller, contents need not be initialised.
+ * Calls that share a workspace must be ordered on one stream.
+ *
+ * Returns HS_OK; HS_EINVAL / HS_ERANGE / HS_EMEMKIND / HS_EWORKSPACE on bad
+ * arguments (nothing enqueued); HS_ELAUNCH if a launch failed. B == 0 or
+ * K == 0 returns HS_OK with nothing enqueued.
+ */
+int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * transfer_rows_all_layer -- fused multi-layer indexed row copy.
+ * tokenspeed kvcache/triton.py, _kv_transfer_all_layer_mla_kernel; SGLang
+ * hisparse.cuh, transfer_cache_dsv4_mla_kernel (generic row layout).
+ *
+ * For every pair i < n and layer l < num_layers:
+ *   dst_layer_ptrs[l] + dst_idx[i]*row_bytes  <-  src_layer_ptrs[l] + src_idx[i]*row_bytes
+ * src_layer_ptrs / dst_layer_ptrs: device uint64 [num_layers] arrays of layer
+ * base addresses; each layer holds src_nrows (dst_nrows) rows of row_bytes.
+ * Every layer base must be 4-byte aligned (16-byte aligned bases take the
+ * 16-byte copy path when row_bytes is a multiple of 16).
+ * Either side may be pinned host memory (offload and load directions).
+ * src_idx / dst_idx: device int64 [n]; indices stay 64-bit (no truncation).
+ * Pairs with an index outside [0, src_nrows) / [0, dst_nrows) are skipped.
+ * dst indices must be unique and source and destination rows must not overlap.
+ * row_bytes > 0, multiple of 4; n == 0 or num_layers == 0 returns HS_OK.
+ */
+int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
+                            const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
+                            int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
+                            int64_t dst_nrows, hipStream_t stream);
+
+/*
+ * store_kv_scatter -- write rows into a cache at given row indices.
+ * tokenspeed kvcache/triton.py, _store_kv_cache_kernel (one cache, the MLA case).
+ *
+ * For j < n with 0 <= loc[j] < dst_nrows:
+ *   dst + loc[j]*dst_row_stride_bytes  <-  src + j*src_row_stride_bytes  (row_bytes bytes)
+ * src, dst: device; strides in bytes, >= row_bytes, multiples of 4; loc: device
+ * int64 [n], unique among entries that are written. Entries with loc < 0 (the
+ * pages' padding value) or loc >= dst_nrows are skipped. n == 0 returns HS_OK.
+ */
+int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
+                     int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
+                     int64_t n, int64_t row_bytes, hipStream_t stream);
+
+/*
+ * hisparse_state_reset -- put state rows into the initial state: every entry
+ * of slot_tokens[r][0..S_r) = -1 and lru[r] = 0..H-1, for r in rows[0..n_rows).
+ * rows: device int64 [n_rows]; rows outside [0, R) are skipped.
+ */
+int hisparse_state_reset(int32_t* slot_tokens, int16_t* lru, const int64_t* rows, int64_t n_rows,
+                         int32_t H, int64_t S_r, int64_t R, hipStream_t stream);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* hisparse_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

@@ -1,0 +1,122 @@
+"""MI355X HiSparse swap-in: Python binding of libhisparse.so.
+
+Argument marshalling only. Each function takes torch tensors, checks
+dtype/device/shape enough to pass correct pointers, and calls the C ABI of
+``include/hisparse.h`` on torch's current HIP stream. All work runs in the
+library's HIP kernels; nothing here computes, and nothing falls back.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import EXPORTS, HisparseError, SwapInArgs, check, load
+
+__all__ = ["hisparse_swap_in", "transfer_rows_all_layer", "store_kv_scatter",
+           "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _opt(t: Optional[torch.Tensor], dtype, name) -> Optional[int]:
+    return None if t is None else _dev(t, dtype, name)
+
+
+def swap_in_workspace_bytes(B: int, K: int) -> int:
+    return int(load().hs_swap_in_workspace_bytes(B, K))
+
+
+def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: torch.Tensor,
+                     slot_tokens: torch.Tensor, lru: torch.Tensor, pool: torch.Tensor,
+                     hot: torch.Tensor, out_rows: torch.Tensor, ctx_stride: int,
+                     workspace: torch.Tensor, miss_counts: Optional[torch.Tensor] = None,
+                     num_real: Optional[torch.Tensor] = None,
+                     slot_rows: Optional[torch.Tensor] = None,
+                     pool_rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
+
+    topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
+    slot_tokens int32 [R, S_r], lru int16 [R, H], pool uint8 [rows, row_bytes]
+    (pinned host or device), hot uint8 [rows, row_bytes] (device), out_rows int32 [B, K],
+    workspace uint8 device tensor of at least ``swap_in_workspace_bytes(B, K)`` bytes.
+    """
+    B, K = out_rows.shape
+    if topk.dim() != 2 or topk.shape[0] != B or topk.shape[1] < K or topk.stride(1) != 1:
+        raise ValueError("topk must be [B, >=K] with contiguous columns")
+    for t, n in ((slot_tokens, "slot_tokens"), (lru, "lru"), (out_rows, "out_rows")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if pool.dim() != 2 or hot.dim() != 2 or pool.shape[1] != hot.shape[1] or \
+            not pool.is_contiguous() or not hot.is_contiguous():
+        raise ValueError("pool and hot must be contiguous [rows, row_bytes] with equal row_bytes")
+    if pool.dtype != torch.uint8 or hot.dtype != torch.uint8:
+        raise ValueError("pool and hot are uint8 byte rows")
+    if not hot.is_cuda:
+        raise ValueError("hot must be a device tensor")
+    R, S_r = slot_tokens.shape
+    a = SwapInArgs(
+        B=B, K=K, H=lru.shape[1], S_r=S_r, R=R,
+        topk_ids=_dev(topk, torch.int32, "topk"), topk_stride=topk.stride(0),
+        req_rows=_dev(req_rows, torch.int64, "req_rows"),
+        seq_lens=_dev(seq_lens, torch.int64, "seq_lens"),
+        num_real=_opt(num_real, torch.int32, "num_real"),
+        slot_tokens=_dev(slot_tokens, torch.int32, "slot_tokens"),
+        lru=_dev(lru, torch.int16, "lru"),
+        slot_rows=_opt(slot_rows, torch.int32, "slot_rows"),
+        pool_rows=_opt(pool_rows, torch.int64, "pool_rows"),
+        ctx_stride=ctx_stride, pool=pool.data_ptr(), pool_nrows=pool.shape[0],
+        hot=hot.data_ptr(), hot_nrows=hot.shape[0], row_bytes=hot.shape[1],
+        out_rows=_dev(out_rows, torch.int32, "out_rows"),
+        miss_counts=_opt(miss_counts, torch.int32, "miss_counts"))
+    ws = _dev(workspace, torch.uint8, "workspace")
+    check("hisparse_swap_in", load().hisparse_swap_in(ctypes.byref(a), ws, workspace.numel(),
+                                                      _stream(stream)))
+
+
+def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: torch.Tensor,
+                            src_idx: torch.Tensor, dst_idx: torch.Tensor, row_bytes: int,
+                            src_nrows: int, dst_nrows: int, stream=None) -> None:
+    """All-layer indexed row copy; layer pointer arrays are device uint64 (torch int64) [L]."""
+    L = src_layer_ptrs.numel()
+    if dst_layer_ptrs.numel() != L or src_idx.numel() != dst_idx.numel():
+        raise ValueError("pointer arrays / index arrays must have equal lengths")
+    check("transfer_rows_all_layer", load().transfer_rows_all_layer(
+        _dev(src_layer_ptrs, torch.int64, "src_layer_ptrs"),
+        _dev(dst_layer_ptrs, torch.int64, "dst_layer_ptrs"),
+        _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
+        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, _stream(stream)))
+
+
+def store_kv_scatter(*, src: torch.Tensor, dst: torch.Tensor, loc: torch.Tensor, row_bytes: int = 0,
+                     stream=None) -> None:
+    """``dst[loc[j]] = src[j]`` for uint8 row tensors whose leading axis may be strided."""
+    if src.dtype != torch.uint8 or dst.dtype != torch.uint8 or src.dim() != 2 or dst.dim() != 2:
+        raise ValueError("src and dst are 2-D uint8 row tensors")
+    if src.stride(1) != 1 or dst.stride(1) != 1:
+        raise ValueError("rows must be contiguous")
+    rb = row_bytes or src.shape[1]
+    check("store_kv_scatter", load().store_kv_scatter(
+        _dev(src, torch.uint8, "src"), src.stride(0), _dev(dst, torch.uint8, "dst"), dst.stride(0),
+        dst.shape[0], _dev(loc, torch.int64, "loc"), loc.numel(), rb, _stream(stream)))
+
+
+def hisparse_state_reset(*, slot_tokens: torch.Tensor, lru: torch.Tensor, rows: torch.Tensor,
+                         stream=None) -> None:
+    R, S_r = slot_tokens.shape
+    check("hisparse_state_reset", load().hisparse_state_reset(
+        _dev(slot_tokens, torch.int32, "slot_tokens"), _dev(lru, torch.int16, "lru"),
+        _dev(rows, torch.int64, "rows"), rows.numel(), lru.shape[1], S_r, R, _stream(stream)))

@@ -1,0 +1,226 @@
+// Indexed row copies that share the swap-in's copy engine:
+//   transfer_rows_all_layer -- tokenspeed kvcache/triton.py,
+//     _kv_transfer_all_layer_mla_kernel; SGLang hisparse.cuh,
+//     transfer_cache_dsv4_mla_kernel (generic row layout);
+//   store_kv_scatter -- tokenspeed kvcache/triton.py, _store_kv_cache_kernel;
+//   hisparse_state_reset -- initial per-request state.
+//
+// Work is one flat stream of (pair, layer, chunk) items rather than one warp
+// per item looping over layers: every lane moves one 16-byte chunk, lanes of a
+// wave cover consecutive chunks of consecutive rows, and a grid-stride loop
+// with several independent loads in flight per lane keeps enough bytes
+// outstanding to cover host-link latency as well as HBM latency.
+#include <hip/hip_runtime.h>
+
+#include "hs_common.hpp"
+
+namespace hs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kMaxStagedLayers = 256;
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void transfer_kernel(
+    const uint64_t* __restrict__ src_layers, const uint64_t* __restrict__ dst_layers,
+    const int64_t* __restrict__ src_idx, const int64_t* __restrict__ dst_idx, uint32_t total,
+    int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows, FastDiv cdiv,
+    FastDiv ldiv) {
+  typedef Chunk<W> C;
+  __shared__ uint64_t s_src[kMaxStagedLayers];
+  __shared__ uint64_t s_dst[kMaxStagedLayers];
+  const bool staged = num_layers <= kMaxStagedLayers;
+  if (staged) {
+    for (int l = threadIdx.x; l < num_layers; l += kThreads) {
+      s_src[l] = src_layers[l];
+      s_dst[l] = dst_layers[l];
+    }
+    __syncthreads();
+  }
+  const uint32_t step = gridDim.x * kThreads * kUnroll;
+  for (uint32_t j0 = blockIdx.x * kThreads * kUnroll + threadIdx.x; j0 < total; j0 += step) {
+    typename C::T v[kUnroll];
+    char* d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t j = j0 + u * kThreads;
+      d[u] = nullptr;
+      if (j < total) {
+        const uint32_t row = fdiv(j, cdiv);          // (pair, layer) row
+        const uint32_t c = j - row * cdiv.d;        // chunk in the row
+        const uint32_t i = fdiv(row, ldiv);          // pair
+        const uint32_t l = row - i * ldiv.d;        // layer
+        const int64_t si = src_idx[i], di = dst_idx[i];
+        if (si >= 0 && si < src_nrows && di >= 0 && di < dst_nrows) {
+          const uint64_t sb = staged ? s_src[l] : src_layers[l];
+          const uint64_t db = staged ? s_dst[l] : dst_layers[l];
+          const int64_t off = static_cast<int64_t>(c) * W;
+          const char* sp = reinterpret_cast<const char*>(sb) + si * row_bytes + off;
+          char* dp = reinterpret_cast<char*>(db) + di * row_bytes + off;
+          if (W == 4 || ((sb | db) & 15) == 0) {
+            v[u] = C::load(sp);
+            d[u] = dp;
+          } else {
+            // A layer base that is only 4-byte aligned: move this chunk as dwords.
+#pragma unroll
+            for (int k = 0; k < W; k += 4) Chunk<4>::store(dp + k, Chunk<4>::load(sp + k));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (d[u]) C::store(d[u], v[u]);
+  }
+}
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(
+    const char* __restrict__ src, int64_t src_stride, char* __restrict__ dst, int64_t dst_stride,
+    int64_t dst_nrows, const int64_t* __restrict__ loc, uint32_t total, FastDiv cdiv) {
+  typedef Chunk<W> C;
+  const uint32_t step = gridDim.x * kThreads * kUnroll;
+  for (uint32_t j0 = blockIdx.x * kThreads * kUnroll + threadIdx.x; j0 < total; j0 += step) {
+    typename C::T v[kUnroll];
+    char* d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t j = j0 + u * kThreads;
+      d[u] = nullptr;
+      if (j < total) {
+        const uint32_t row = fdiv(j, cdiv);
+        const uint32_t c = j - row * cdiv.d;
+        const int64_t to = loc[row];
+        if (to >= 0 && to < dst_nrows) {
+          const int64_t off = static_cast<int64_t>(c) * W;
+          v[u] = C::load(src + static_cast<int64_t>(row) * src_stride + off);
+          d[u] = dst + to * dst_stride + off;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (d[u]) C::store(d[u], v[u]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void state_reset_kernel(int32_t* slot_tokens, int16_t* lru,
+                                                               const int64_t* rows, int32_t H,
+                                                               int64_t S_r, int64_t R) {
+  const int64_t r = rows[blockIdx.x];
+  if (r < 0 || r >= R) return;
+  for (int64_t s = threadIdx.x; s < S_r; s += kThreads) slot_tokens[r * S_r + s] = -1;
+  for (int32_t p = threadIdx.x; p < H; p += kThreads) lru[r * H + p] = static_cast<int16_t>(p);
+}
+
+// Workgroups for a grid-stride copy of `items` chunks: enough to fill every
+// CU several times over, never more than the work needs.
+inline unsigned copy_grid(uint64_t items, int num_cus) {
+  const uint64_t need = (items + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const uint64_t cap = 16ull * static_cast<uint64_t>(num_cus > 0 ? num_cus : 256);
+  return static_cast<unsigned>(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+}  // namespace
+}  // namespace hs
+
+using namespace hs;
+
+extern "C" int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
+                                       const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
+                                       int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
+                                       int64_t dst_nrows, hipStream_t stream) {
+  if (n < 0 || num_layers < 0) return set_error(HS_EINVAL, "n and num_layers must be >= 0");
+  if (n == 0 || num_layers == 0) return HS_OK;
+  if (!src_layer_ptrs || !dst_layer_ptrs || !src_idx || !dst_idx)
+    return set_error(HS_EINVAL, "a required pointer is NULL");
+  if (row_bytes <= 0 || (row_bytes & 3) != 0)
+    return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
+  if (row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
+  if (src_nrows < 0 || dst_nrows < 0) return set_error(HS_EINVAL, "row counts must be >= 0");
+  // Layer base addresses live on the device; rows are 16-byte chunks when
+  // row_bytes allows (layer bases are checked by the kernel's caller contract:
+  // cache allocations are at least 256-byte aligned).
+  const int W = (row_bytes & 15) == 0 ? 16 : 4;
+  const int64_t C = row_bytes / W;
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc != HS_OK) return rc;
+  const FastDiv cdiv = make_fastdiv(static_cast<uint32_t>(C));
+  const FastDiv ldiv = make_fastdiv(static_cast<uint32_t>(num_layers));
+  // Items must stay below 2^31 per launch: split the pairs into batches.
+  const int64_t per_pair = C * num_layers;
+  const int64_t max_pairs = ((1ll << 30) / per_pair) > 0 ? ((1ll << 30) / per_pair) : 0;
+  if (max_pairs == 0) return set_error(HS_ERANGE, "one pair spans more than 2^30 chunks");
+  for (int64_t p0 = 0; p0 < n; p0 += max_pairs) {
+    const int64_t np = (n - p0) < max_pairs ? (n - p0) : max_pairs;
+    const uint32_t total = static_cast<uint32_t>(np * per_pair);
+    const unsigned grid = copy_grid(total, di.num_cus);
+    if (W == 16)
+      hipLaunchKernelGGL(transfer_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, src_layer_ptrs,
+                         dst_layer_ptrs, src_idx + p0, dst_idx + p0, total, num_layers, row_bytes,
+                         src_nrows, dst_nrows, cdiv, ldiv);
+    else
+      hipLaunchKernelGGL(transfer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, src_layer_ptrs,
+                         dst_layer_ptrs, src_idx + p0, dst_idx + p0, total, num_layers, row_bytes,
+                         src_nrows, dst_nrows, cdiv, ldiv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(HS_ELAUNCH, "transfer launch: %s", hipGetErrorString(e));
+  }
+  return HS_OK;
+}
+
+extern "C" int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
+                                int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
+                                int64_t n, int64_t row_bytes, hipStream_t stream) {
+  if (n < 0) return set_error(HS_EINVAL, "n must be >= 0");
+  if (n == 0) return HS_OK;
+  if (!src || !dst || !loc) return set_error(HS_EINVAL, "a required pointer is NULL");
+  if (row_bytes <= 0 || (row_bytes & 3) != 0)
+    return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
+  if (row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
+  if (src_row_stride_bytes < row_bytes || dst_row_stride_bytes < row_bytes ||
+      (src_row_stride_bytes & 3) || (dst_row_stride_bytes & 3))
+    return set_error(HS_EINVAL, "row strides must be >= row_bytes and multiples of 4");
+  if (!aligned(src, 4) || !aligned(dst, 4)) return set_error(HS_EINVAL, "src/dst must be 4-byte aligned");
+  if (dst_nrows < 0) return set_error(HS_EINVAL, "dst_nrows must be >= 0");
+  const bool w16 = aligned(src, 16) && aligned(dst, 16) && (row_bytes & 15) == 0 &&
+                   (src_row_stride_bytes & 15) == 0 && (dst_row_stride_bytes & 15) == 0;
+  const int W = w16 ? 16 : 4;
+  const int64_t C = row_bytes / W;
+  if (n * C >= (1ll << 31)) return set_error(HS_ERANGE, "n * chunks per row exceeds 2^31");
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc != HS_OK) return rc;
+  const uint32_t total = static_cast<uint32_t>(n * C);
+  const FastDiv cdiv = make_fastdiv(static_cast<uint32_t>(C));
+  const unsigned grid = copy_grid(total, di.num_cus);
+  if (W == 16)
+    hipLaunchKernelGGL(scatter_kernel<16>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const char*>(src), src_row_stride_bytes, static_cast<char*>(dst),
+                       dst_row_stride_bytes, dst_nrows, loc, total, cdiv);
+  else
+    hipLaunchKernelGGL(scatter_kernel<4>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const char*>(src), src_row_stride_bytes, static_cast<char*>(dst),
+                       dst_row_stride_bytes, dst_nrows, loc, total, cdiv);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(HS_ELAUNCH, "scatter launch: %s", hipGetErrorString(e));
+  return HS_OK;
+}
+
+extern "C" int hisparse_state_reset(int32_t* slot_tokens, int16_t* lru, const int64_t* rows,
+                                    int64_t n_rows, int32_t H, int64_t S_r, int64_t R,
+                                    hipStream_t stream) {
+  if (n_rows < 0 || H < 0 || R < 0) return set_error(HS_EINVAL, "sizes must be >= 0");
+  if (n_rows == 0) return HS_OK;
+  if (!slot_tokens || !lru || !rows) return set_error(HS_EINVAL, "a required pointer is NULL");
+  if (H > 32768) return set_error(HS_ERANGE, "H exceeds 32768 (int16 slots)");
+  if (S_r < static_cast<int64_t>(H) + 1) return set_error(HS_EINVAL, "S_r must be >= H+1");
+  if (n_rows > 0x7fffffffll) return set_error(HS_ERANGE, "too many rows for one launch");
+  hipLaunchKernelGGL(state_reset_kernel, dim3(static_cast<unsigned>(n_rows)), dim3(kThreads), 0,
+                     stream, slot_tokens, lru, rows, H, S_r, R);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(HS_ELAUNCH, "reset launch: %s", hipGetErrorString(e));
+  return HS_OK;
+}

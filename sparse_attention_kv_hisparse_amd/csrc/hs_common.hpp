@@ -1,0 +1,94 @@
+// Shared pieces of the gfx950 HiSparse kernels: the copy engine's 16-byte /
+// 4-byte chunk movers, exact division by a run-time constant, and host-side
+// status/error helpers. Everything here is integer or opaque bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "hisparse.h"
+
+namespace hs {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ---------------------------------------------------------------------------
+// Exact unsigned division by a run-time divisor d for numerators n < 2^31:
+// q = (n * m) >> s with s = 31 + ceil(log2 d) and m = ceil(2^s / d).
+// m < 2^33 so n*m < 2^64, and the rounding error n*(m*d - 2^s)/(d*2^s) stays
+// below 1/d, so the quotient is exact (round-up reciprocal method).
+// ---------------------------------------------------------------------------
+struct FastDiv {
+  uint32_t d;
+  uint32_t s;
+  uint64_t m;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint32_t s = 31 + l;
+  const uint64_t m = ((1ull << s) + d - 1) / d;
+  return FastDiv{d, s, m};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> f.s);
+}
+
+// ---------------------------------------------------------------------------
+// Copy engine: rows are moved as independent 16-byte (or 4-byte) chunks, one
+// per lane, with consecutive lanes on consecutive chunks of a row so a wave's
+// accesses coalesce. Loads and stores are nontemporal: pool rows are read once
+// and hot rows are not re-read by the copy, so neither should displace other
+// data in L2/MALL.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int W>
+struct Chunk;
+
+template <>
+struct Chunk<16> {
+  typedef u32x4 T;
+  static __device__ __forceinline__ T load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  static __device__ __forceinline__ void store(char* p, T v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  }
+};
+
+template <>
+struct Chunk<4> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ T load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+  static __device__ __forceinline__ void store(char* p, T v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+  }
+};
+
+// Chunks a row of `row_bytes` splits into at width W.
+inline int64_t chunks_per_row(int64_t row_bytes, int W) { return row_bytes / W; }
+
+// ---------------------------------------------------------------------------
+// Host helpers.
+// ---------------------------------------------------------------------------
+int set_error(int status, const char* fmt, ...);
+
+// Largest dynamic LDS (bytes) one workgroup may use on the current device, and
+// the compute-unit count; cached per device.
+struct DeviceInfo {
+  int device;
+  int max_lds;
+  int num_cus;
+};
+int device_info(DeviceInfo* out);
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace hs

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every function include/hisparse.h declares,
+and rejects bad arguments on the host before touching the GPU (no compute
+calls here: these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisparse.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_kv_hisparse_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_kv_hisparse_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_calls():
+    from sparse_attention_kv_hisparse_amd._lib import EXPORTS
+    assert declared_functions() == sorted(EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _args(**kw):
+    from sparse_attention_kv_hisparse_amd._lib import SwapInArgs
+    fake = 0x100000   # never dereferenced: validation fails first
+    base = dict(B=2, K=4, H=8, S_r=9, R=2, topk_ids=fake, topk_stride=4, req_rows=fake,
+                seq_lens=fake, num_real=None, slot_tokens=fake, lru=fake, slot_rows=None,
+                pool_rows=None, ctx_stride=100, pool=fake, pool_nrows=200, hot=fake,
+                hot_nrows=18, row_bytes=16, out_rows=fake, miss_counts=None)
+    base.update(kw)
+    return SwapInArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1),
+    (dict(H=3), -1),                      # H < K
+    (dict(H=40000, K=4), -2),             # H above int16 slots
+    (dict(S_r=8), -1),                    # no newest slot
+    (dict(row_bytes=6), -1),
+    (dict(row_bytes=0), -1),
+    (dict(topk_stride=3), -1),
+    (dict(ctx_stride=0), -1),
+    (dict(pool=None), -1),
+    (dict(out_rows=None), -1),
+    (dict(hot_nrows=17), -1),             # flat regions need R*S_r rows
+    (dict(pool=0x100002), -1),            # not 4-byte aligned
+    (dict(row_bytes=1 << 21), -2),
+])
+def test_swap_in_rejects_bad_arguments(lib, kw, status):
+    a = _args(**kw)
+    rc = lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None)
+    assert rc == status
+    assert lib.hisparse_last_error()
+
+
+def test_swap_in_rejects_small_workspace(lib):
+    a = _args()
+    need = lib.hs_swap_in_workspace_bytes(2, 4)
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), need - 1, None) == -5
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200010), need, None) == -5
+    assert lib.hisparse_swap_in(ctypes.byref(a), None, need, None) == -5
+    assert lib.hisparse_swap_in(None, None, 0, None) == -1
+
+
+def test_swap_in_empty_is_ok(lib):
+    assert lib.hisparse_swap_in(ctypes.byref(_args(B=0)), None, 0, None) == 0
+    assert lib.hisparse_swap_in(ctypes.byref(_args(K=0)), None, 0, None) == 0
+
+
+def test_workspace_size(lib):
+    assert lib.hs_swap_in_workspace_bytes(0, 5) == 0
+    b, k = 32, 2048
+    size = lib.hs_swap_in_workspace_bytes(b, k)
+    assert size >= b * 4 + b * k * 12 and size % 256 == 0
+
+
+def test_transfer_rejects(lib):
+    f = 0x100000
+    assert lib.transfer_rows_all_layer(f, f, f, f, -1, 3, 16, 10, 10, None) == -1
+    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 6, 10, 10, None) == -1
+    assert lib.transfer_rows_all_layer(None, f, f, f, 5, 3, 16, 10, 10, None) == -1
+    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 16, -1, 10, None) == -1
+    assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, None) == 0
+    assert lib.transfer_rows_all_layer(None, None, None, None, 4, 0, 16, 10, 10, None) == 0
+
+
+def test_scatter_rejects(lib):
+    f = 0x100000
+    assert lib.store_kv_scatter(f, 8, f, 16, 10, f, 3, 16, None) == -1      # src stride < rb
+    assert lib.store_kv_scatter(f, 16, f, 16, 10, f, 3, 10, None) == -1     # rb % 4
+    assert lib.store_kv_scatter(f + 2, 16, f, 16, 10, f, 3, 16, None) == -1  # misaligned
+    assert lib.store_kv_scatter(None, 16, f, 16, 10, f, 3, 16, None) == -1
+    assert lib.store_kv_scatter(None, 16, None, 16, 10, None, 0, 16, None) == 0
+
+
+def test_reset_rejects(lib):
+    f = 0x100000
+    assert lib.hisparse_state_reset(f, f, f, 3, 8, 8, 4, None) == -1        # S_r < H+1
+    assert lib.hisparse_state_reset(f, f, f, 3, 40000, 40001, 4, None) == -2
+    assert lib.hisparse_state_reset(None, None, None, 0, 8, 9, 4, None) == 0
+
+
+def test_fastdiv_is_exact():
+    """The copy kernels' division by a run-time constant: q = (n*m) >> s with
+    s = 31 + ceil(log2 d), m = ceil(2^s/d), claimed exact for n < 2^31."""
+    import random
+    rnd = random.Random(5)
+    divisors = list(range(1, 2100)) + [rnd.randrange(1, 1 << 31) for _ in range(300)] + [(1 << 31) - 1]
+    for d in divisors:
+        l = (d - 1).bit_length()
+        s = 31 + l
+        m = ((1 << s) + d - 1) // d
+        assert m < (1 << 33)
+        ns = [0, 1, d - 1, d, d + 1, (1 << 31) - 1, (1 << 31) - 2] + \
+             [rnd.randrange(0, 1 << 31) for _ in range(40)] + \
+             [k * d - 1 for k in (1, 2, 1000) if k * d - 1 < (1 << 31)]
+        for n in ns:
+            if 0 <= n < (1 << 31):
+                assert ((n * m) & ((1 << 64) - 1)) >> s == n // d, (n, d)

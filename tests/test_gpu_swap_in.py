@@ -1,0 +1,205 @@
+"""GPU parity of hisparse_swap_in against the CPU oracle, bit for bit.
+
+Full-size traces of the five workloads (tiny; DeepSeek-V3.2-like pinned-host
+pool; device pool; cold/adversarial at 1152 B and 132 B rows), plus edge
+cases: padding rows, permuted and sparse state rows, slot-row and pool-row
+tables, invalid ids, K == H, ragged H and K, the 4-byte copy path, strided
+top-k rows, hash clustering, empty calls and exact replays.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import sparse_attention_kv_hisparse_amd as hs
+    hs.load()
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+
+
+def _harness():
+    import gpu_harness
+    return gpu_harness
+
+
+def test_tiny_trace_with_invariants():
+    h = _harness()
+    counts = h.run_trace(gen.TINY, full_hot_steps=range(gen.TINY.steps), check_invariants=True)
+    assert (counts[0] == gen.TINY.K).all()
+
+
+def test_dsv32_like_host_pool_full():
+    h = _harness()
+    cfg = gen.DSV32
+    counts = h.run_trace(cfg, full_hot_steps=(0, cfg.steps // 2))
+    assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
+
+
+def test_device_pool_full():
+    h = _harness()
+    cfg = gen.DEVPOOL
+    counts = h.run_trace(cfg, full_hot_steps=(0, cfg.steps // 2))
+    assert (counts[0] == cfg.K).all()
+
+
+@pytest.mark.parametrize("cfg", [gen.ADVERSARIAL, gen.ADVERSARIAL_132], ids=["1152B", "132B"])
+def test_adversarial_full(cfg):
+    h = _harness()
+    counts = h.run_trace(cfg, full_hot_steps=(0,))
+    assert (counts[0] == cfg.K).all()
+
+
+def _small(**kw):
+    base = dict(name="edge", B=3, H=40, K=12, ctx=300, row_bytes=48, steps=6, rho=0.5,
+                dist="uniform", pool_kind="host", seed=99)
+    base.update(kw)
+    return gen.SwapConfig(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(H=64, K=64, ctx=500),                  # K == H, exact wave multiples
+    dict(H=1000, K=999, ctx=3000, B=2),         # ragged, K just below H
+    dict(H=5000, K=3000, ctx=9000, B=2),        # several LDS scan words, H > 4096
+    dict(H=1, K=1, ctx=50, B=4),                # degenerate sizes
+    dict(row_bytes=4), dict(row_bytes=132),     # 4-byte path
+    dict(row_bytes=1152, pool_kind="device"),
+    dict(B=1, H=2048, K=2048, ctx=4096),        # one request, all K = H
+], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single"])
+def test_edge_traces(kw):
+    h = _harness()
+    cfg = _small(**kw)
+    h.run_trace(cfg, full_hot_steps=range(cfg.steps), check_invariants=cfg.K * cfg.B <= 4096)
+
+
+def test_padding_permuted_rows_tables_invalid_ids():
+    """R > B, permuted state rows, num_real < B, slot_rows/pool_rows tables,
+    invalid ids (negative, >= seq_len, >= ctx_stride, pool row out of range)."""
+    h = _harness()
+    rng = np.random.default_rng(7)
+    cfg = _small(B=4, H=30, K=10, ctx=100, row_bytes=32)
+    R = 9
+    S_r = cfg.S_r
+    hot_nrows = R * S_r + 5
+    slot_rows = rng.permutation(hot_nrows)[:R * S_r].astype(np.int32).reshape(R, S_r)
+    pool_nrows = R * cfg.ctx - 17            # the last ids of the last row have no pool row
+    pool_rows = rng.permutation(R * cfg.ctx)[:R * cfg.ctx].astype(np.int64).reshape(R, cfg.ctx)
+    run = h.ParityRun(cfg, R=R, req_rows=np.asarray([7, 2, 5, 0], dtype=np.int64),
+                      slot_rows=slot_rows, pool_rows=pool_rows, hot_nrows=hot_nrows,
+                      pool_nrows=pool_nrows)
+    for t in range(10):
+        rows, seq, topk = gen.random_case(rng, B=4, R=R, H=cfg.H, K=cfg.K, ctx=cfg.ctx,
+                                          n_invalid=int(rng.integers(0, 3)))
+        run.req_rows = rows
+        num_real = int(rng.integers(1, 5)) if t % 3 == 2 else -1
+        run.step(topk, seq, num_real=num_real, full_hot=True, check_invariants=True)
+
+
+def test_state_row_out_of_range_is_padding():
+    h = _harness()
+    cfg = _small(B=3)
+    run = h.ParityRun(cfg, R=3, req_rows=np.asarray([0, 5, -1], dtype=np.int64))
+    rng = np.random.default_rng(3)
+    for _ in range(3):
+        _, seq, topk = gen.random_case(rng, B=3, R=3, H=cfg.H, K=cfg.K, ctx=cfg.ctx)
+        out, cnt = run.step(topk, seq, full_hot=True)
+        assert (out[1:] == -1).all() and (cnt[1:] == 0).all()
+
+
+def test_strided_topk_rows():
+    h = _harness()
+    cfg = _small(B=5, H=70, K=33, ctx=400)
+    run = h.ParityRun(cfg)
+    for t, topk in enumerate(gen.topk_trace(cfg, 4)):
+        run.step(topk, gen.seq_lens(cfg, t), full_hot=True, topk_pad=11)
+
+
+def test_misaligned_hot_uses_4byte_path():
+    h = _harness()
+    cfg = _small(row_bytes=64)
+    run = h.ParityRun(cfg, hot_misalign=True)
+    for t, topk in enumerate(gen.topk_trace(cfg, 4)):
+        run.step(topk, gen.seq_lens(cfg, t), full_hot=True)
+
+
+def test_clusters_under_the_kernel_hash():
+    """Ids that share the top bits of the multiplicative hash (long probe chains
+    in the LDS table) still resolve exactly."""
+    h = _harness()
+    K, H = 512, 1024
+    T = 1024                                        # table entries for K = 512
+    ids = np.arange(200000, dtype=np.uint64)
+    home = ((ids * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - 10)
+    cand = ids[home < 8].astype(np.int64)           # ~1600 ids in 8 home buckets of 1024
+    ctx = int(cand.max()) + 2
+    cfg = _small(B=2, H=H, K=K, ctx=ctx, row_bytes=16)
+    run = h.ParityRun(cfg)
+    rng = np.random.default_rng(11)
+    prev = None
+    for t in range(4):
+        rows = np.arange(2, dtype=np.int64)
+        seq = np.full(2, ctx, dtype=np.int64)
+        topk = np.stack([rng.choice(cand, size=K, replace=False) for _ in range(2)]).astype(np.int32)
+        if prev is not None:
+            topk[:, :K // 2] = prev[:, :K // 2]
+            for b in range(2):
+                fresh = np.setdiff1d(cand, prev[b])
+                topk[b, K // 2:] = rng.choice(fresh, size=K - K // 2, replace=False)
+        prev = topk.copy()
+        run.step(topk, seq, full_hot=True)
+
+
+def test_empty_calls_are_noops():
+    import sparse_attention_kv_hisparse_amd as hs
+    cfg = _small()
+    from workloads import device as wdev
+    st = wdev.DeviceSwapState(cfg)
+    pool = wdev.make_pool(cfg)
+    before = st.lru.clone()
+    out = torch.empty((0, cfg.K), dtype=torch.int32, device="cuda")
+    hs.hisparse_swap_in(topk=torch.empty((0, cfg.K), dtype=torch.int32, device="cuda"),
+                        req_rows=torch.empty(0, dtype=torch.int64, device="cuda"),
+                        seq_lens=torch.empty(0, dtype=torch.int64, device="cuda"),
+                        slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                        out_rows=out, ctx_stride=cfg.ctx, workspace=st.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(before, st.lru)
+
+
+def test_replay_from_restored_state_is_identical():
+    """Restoring the state and replaying a call reproduces every output bit:
+    nothing depends on scheduling order."""
+    import sparse_attention_kv_hisparse_amd as hs
+    from workloads import device as wdev
+    cfg = gen.DEVPOOL.with_(B=16)
+    st = wdev.DeviceSwapState(cfg)
+    pool = wdev.make_pool(cfg)
+    rows = torch.arange(cfg.B, dtype=torch.int64, device="cuda")
+    trace = list(gen.topk_trace(cfg, 3))
+    for t, topk in enumerate(trace[:2]):
+        hs.hisparse_swap_in(topk=torch.as_tensor(topk).cuda(), req_rows=rows,
+                            seq_lens=torch.as_tensor(gen.seq_lens(cfg, t)).cuda(),
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+                            miss_counts=st.counts)
+    snap = (st.slot_tokens.clone(), st.lru.clone(), st.hot.clone())
+    results = []
+    for _ in range(3):
+        st.slot_tokens.copy_(snap[0]); st.lru.copy_(snap[1]); st.hot.copy_(snap[2])
+        hs.hisparse_swap_in(topk=torch.as_tensor(trace[2]).cuda(), req_rows=rows,
+                            seq_lens=torch.as_tensor(gen.seq_lens(cfg, 2)).cuda(),
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+                            miss_counts=st.counts)
+        torch.cuda.synchronize()
+        results.append([x.clone() for x in (st.out, st.counts, st.slot_tokens, st.lru, st.hot)])
+    for r in results[1:]:
+        for a, b in zip(results[0], r):
+            assert torch.equal(a, b)
