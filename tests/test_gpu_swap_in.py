@@ -46,14 +46,15 @@ def test_device_pool_full():
     h = _harness()
     cfg = gen.DEVPOOL
     counts = h.run_trace(cfg, full_hot_steps=(0, cfg.steps // 2))
-    assert (counts[0] == cfg.K).all()
+    # cold step: every id misses except the newest token when a row drew it
+    assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
 
 @pytest.mark.parametrize("cfg", [gen.ADVERSARIAL, gen.ADVERSARIAL_132], ids=["1152B", "132B"])
 def test_adversarial_full(cfg):
     h = _harness()
     counts = h.run_trace(cfg, full_hot_steps=(0,))
-    assert (counts[0] == cfg.K).all()
+    assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
 
 def _small(**kw):
