@@ -62,7 +62,7 @@ class Trace:
 
 
 def run_gpu(cfg, warmup, steps, torch, hs, wdev):
-    """Returns per-call µs (timed steps), miss counts per timed step, wall seconds."""
+    """Returns event-timed µs over the K timed calls, miss counts per timed step, wall seconds."""
     from workloads import gen  # noqa: F401
     log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})")
     pool = wdev.make_pool(cfg)
@@ -81,20 +81,20 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
         call(t)
     torch.cuda.synchronize()
     log(f"[bench] {cfg.name}: {warmup} warm-up steps done, timing {steps}")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev[0].record(stream)
+    e0.record(stream)
     for k in range(steps):
         call(warmup + k)
-        ev[k + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    us = np.asarray([ev[k].elapsed_time(ev[k + 1]) * 1000.0 for k in range(steps)])
+    us_total = e0.elapsed_time(e1) * 1000.0
     c = counts.cpu().numpy()[warmup:]
     del pool, st, tr
     torch.cuda.empty_cache()
-    return us, c, wall
+    return us_total, c, wall
 
 
 def host_link_ceiling(torch, hs):
@@ -179,10 +179,10 @@ def main():
     if link:
         log(f"[bench] host link: {json.dumps({k: round(v, 2) for k, v in link.items()})}")
 
-    us, counts, wall = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev)
+    us_total, counts, wall = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev)
     rows = int(counts.sum())
     bytes_link = rows * cfg.row_bytes
-    total_s = us.sum() * 1e-6
+    total_s = us_total * 1e-6
     value = rows / wall
     achieved = bytes_link / total_s / 1e9
     peak = link["h2d_ceiling_gbs"] if link else None
@@ -203,11 +203,10 @@ def main():
                    "context": cfg.ctx, "hot_size": cfg.H, "top_k": cfg.K,
                    "row_bytes": cfg.row_bytes, "pool": "pinned_host", "retention": cfg.rho,
                    "new_ids": "zipf1.1_recency"},
-        "us_per_call": {"median": round(float(np.median(us)), 2), "mean": round(float(us.mean()), 2),
-                        "min": round(float(us.min()), 2), "max": round(float(us.max()), 2)},
+        "us_per_call": round(us_total / args.steps, 2),
         "rows_per_call": round(rows / args.steps, 1),
         "effective_GBps": round(achieved, 2),
-        "roofline": {"bound": "host_link", "kernel": "hisparse_swap_in (resolve_kernel + swap_copy_kernel)",
+        "roofline": {"bound": "host_link", "kernel": "hisparse_swap_in call (resolve_kernel + swap_copy_kernel)",
                      "achieved": round(achieved, 2), "peak": round(peak, 2) if peak else None,
                      "unit": "GB/s", "frac": round(achieved / peak, 4) if peak else None,
                      "peak_published": PCIE5_X16_GBS, "traffic": None},
@@ -216,19 +215,19 @@ def main():
 
     if not args.no_device_pool:
         dcfg = gen.DEVPOOL
-        dus, dcounts, dwall = run_gpu(dcfg, 1, args.device_pool_steps, torch, hs, wdev)
+        dus_total, dcounts, dwall = run_gpu(dcfg, 1, args.device_pool_steps, torch, hs, wdev)
         drows = int(dcounts.sum())
         # algorithmic HBM bytes: each row read once and written once, plus the
         # per-request metadata (top-k ids, LRU read+write, slot tokens gathered,
         # outputs written, new owners written)
         meta = dcfg.B * (4 * dcfg.K * 2 + 2 * dcfg.H * 2 + 4 * dcfg.H) + 4 * drows / args.device_pool_steps
         dbytes = 2 * drows * dcfg.row_bytes + meta * args.device_pool_steps
-        dach = dbytes / (dus.sum() * 1e-6) / 1e9
+        dach = dbytes / (dus_total * 1e-6) / 1e9
         out["device_pool"] = {
             "workload": "device_pool_swap_in_hbm", "batch": dcfg.B, "context": dcfg.ctx,
             "hot_size": dcfg.H, "top_k": dcfg.K, "row_bytes": dcfg.row_bytes, "steps": args.device_pool_steps,
             "rows_per_s": round(drows / dwall, 1), "rows_per_call": round(drows / args.device_pool_steps, 1),
-            "us_per_call": {"median": round(float(np.median(dus)), 2), "mean": round(float(dus.mean()), 2)},
+            "us_per_call": round(dus_total / args.device_pool_steps, 2),
             "roofline": {"bound": "hbm", "achieved": round(dach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dach / HBM_PEAK_GBS, 4), "traffic": None},
         }

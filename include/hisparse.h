@@ -131,8 +131,9 @@ size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K);
  * unspecified.
  *
  * workspace: device memory of at least hs_swap_in_workspace_bytes(B, K) bytes,
- * 256-byte aligned, owned by the caller, contents need not be initialised.
- * Calls that share a workspace must be ordered on one stream.
+ * 256-byte aligned, owned by the caller; its contents need not be initialised
+ * (it carries each request's miss list from the resolve kernel to the copy
+ * kernel). Calls that share a workspace must be ordered on one stream.
  *
  * Returns HS_OK; HS_EINVAL / HS_ERANGE / HS_EMEMKIND / HS_EWORKSPACE on bad
  * arguments (nothing enqueued); HS_ELAUNCH if a launch failed. B == 0 or

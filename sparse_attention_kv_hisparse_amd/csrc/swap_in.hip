@@ -3,33 +3,39 @@
 // What is computed follows SGLang hisparse.cuh (load_cache_to_device_buffer_kernel)
 // and vLLM hisparse_kernels.cu (hisparse_resolve_residency_kernel +
 // hisparse_gather_compact_kernel): classify the top-k ids, find which are
-// resident in the request's LRU slots, hand the misses the oldest non-hit
+// resident in the request's LRU slots, give the misses the oldest non-hit
 // slots in top-k order, rewrite the LRU order, copy the missed rows in.
 //
 // How it is laid out here (MI355X-first, not a translation):
-//  * resolve_kernel: one 1024-lane workgroup (16 wave64) per batch row. All
-//    per-request scratch lives in LDS: a packed 64-bit (token, index) open
-//    addressing table, the staged LRU row, the victim list, hit/pending bit
-//    sets. Compaction never walks the LRU in wave-sized chunks with a running
-//    scan (the pages' structure, whose wave64 window needs special care);
-//    instead each position's rank is popcount(hit bits below it) plus one
-//    block-wide exclusive scan over 64-bit words, so every position is placed
-//    independently and the global loads of a phase are all issued up front.
+//  * resolve_kernel: one 1024-lane workgroup (16 wave64) per batch row. A
+//    request's resolution runs entirely out of LDS: the top-k ids, the LRU
+//    row and the slot-token row are staged with coalesced loads in one round
+//    trip, outputs are built in LDS and written once at the end, so no global
+//    store ever sits in front of a dependent load.
+//  * Compaction is stable and wave-local: each wave owns a contiguous,
+//    64-aligned segment of LRU positions (and of top-k indices), ranks come
+//    from ballot + mbcnt plus a running count, and only the 16 per-wave
+//    totals cross waves, so there is no block-wide scan and no wave64 scan
+//    window to get wrong (the pages' per-warp chunk scan needs one).
 //  * swap_copy_kernel: the misses, published as a compact (pool row, hot row)
-//    list in a caller-provided workspace, are copied by many 256-lane
-//    workgroups per request as a flat stream of 16-byte chunks.
+//    list in the caller's workspace, are copied by many 256-lane workgroups
+//    per request as a flat stream of 16-byte chunks. The kernel boundary is
+//    the only hand-off between the two, so no workgroup ever waits on another.
 #include <hip/hip_runtime.h>
+
+#include <climits>
 
 #include "hs_common.hpp"
 
 namespace hs {
 namespace {
 
-constexpr int kResolveThreads = 1024;
-constexpr int kResolveWaves = kResolveThreads / kWave;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
-constexpr uint64_t kEmpty = ~0ull;  // (token -1, index 0xFFFFFFFF): never a live entry
+constexpr int kCopyUnroll = 8;             // chunks in flight per copy lane
+constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
+constexpr uint64_t kEmpty = ~0ull;         // (token -1, index 0xFFFFFFFF): never live
 
 // Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by
 // floor(2^32 / golden ratio) = 2654435761 and keep the TOP log2(T) bits of the
@@ -40,7 +46,7 @@ __device__ __forceinline__ uint32_t hash_home(int32_t key, uint32_t shift) {
   return (static_cast<uint32_t>(key) * 2654435761u) >> shift;
 }
 
-struct ResolveArgs {
+struct SwapArgs {
   const int32_t* topk;
   int64_t topk_stride;
   const int64_t* req_rows;
@@ -51,291 +57,355 @@ struct ResolveArgs {
   const int32_t* slot_rows;
   const int64_t* pool_rows;
   int64_t ctx_stride;
+  const char* pool;
   int64_t pool_nrows;
+  char* hot;
+  int64_t hot_nrows;
+  int64_t row_bytes;
   int32_t* out_rows;
   int32_t* miss_counts;
-  int32_t* ws_count;  // [B]
-  int64_t* ws_src;    // [B, K] pool row of miss m
-  int32_t* ws_dst;    // [B, K] hot row of miss m (-1 = skip)
+  int32_t* count;     // [B] misses of request b
+  int64_t* src;       // [B, K] pool row of miss m
+  int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
   int32_t B, K, H;
   int64_t S_r, R;
-  uint32_t T;        // hash table entries (power of two, >= 2K)
-  uint32_t shift;    // 32 - log2(T)
+  uint32_t T;         // hash entries, power of two >= 2K
+  uint32_t shift;     // 32 - log2(T)
+  int32_t stage_tokens;
+  FastDiv cdiv;       // chunks per row
 };
 
 struct LdsLayout {
-  // byte offsets
-  uint32_t hash, pend, hit, hitpos, topk, scan, wtot, lru, victim, total;
+  uint32_t hash, out, topk, lru, tok, victim, hitpos, missw, wtot, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T) {
-  const uint32_t kw = (static_cast<uint32_t>(K) + 63) / 64;
-  const uint32_t hw = (static_cast<uint32_t>(H) + 63) / 64;
-  const uint32_t mw = kw > hw ? kw : hw;
+// Wave w owns positions [w*seg, (w+1)*seg) of an n-long array; seg is a
+// multiple of 64 so every 64-position chunk is one ballot word.
+__host__ __device__ inline uint32_t wave_segment(int32_t n) {
+  return align_up((static_cast<uint32_t>(n) + kWaves - 1) / kWaves, 64);
+}
+
+__host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T, bool stage_tokens) {
+  const uint32_t hwords = kWaves * wave_segment(H) / 64;
+  const uint32_t kwords = kWaves * wave_segment(K) / 64;
   LdsLayout l;
+  // every region starts on a 16-byte boundary
   uint32_t o = 0;
-  l.hash = o;   o += 8 * T;
-  l.pend = o;   o += 8 * kw;
-  l.hit = o;    o += 8 * kw;
-  l.hitpos = o; o += 8 * hw;
-  l.topk = o;   o += 4 * static_cast<uint32_t>(K);
-  l.scan = o;   o += 4 * mw;
-  l.wtot = o;   o += 4 * 32;
-  l.lru = o;    o += 2 * static_cast<uint32_t>(H);
-  l.victim = o; o += 2 * static_cast<uint32_t>(K);
-  l.total = align_up(o, 16);
+  l.hash = o;   o = align_up(o + 8 * T, 16);                  // later: miss list
+  l.out = o;    o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
+  l.topk = o;   o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
+  l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
+  l.hitpos = o; o = align_up(o + 8 * hwords, 16);
+  l.missw = o;  o = align_up(o + 8 * kwords, 16);
+  l.wtot = o;   o = align_up(o + 4 * 3 * kWaves + 16, 16);
+  l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
+  l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
+  l.total = o;
   return l;
 }
 
-// Exclusive block-wide scan of popcount(word(w)) over w < nw (nw <= 1024).
-// Writes the prefix of word w to scan[w] and returns the grand total to every
-// thread. Two barriers; safe to call back to back.
-template <class WordFn>
-__device__ __forceinline__ int block_popc_scan(WordFn word, int nw, int32_t* scan, int32_t* wtot) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int own = tid < nw ? __popcll(word(tid)) : 0;
-  int v = own;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int n = __shfl_up(v, off, kWave);
-    if (lane >= off) v += n;
-  }
-  if (lane == kWave - 1) wtot[wave] = v;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kResolveWaves; ++w) {
-    const int t = wtot[w];
-    before += (w < wave) ? t : 0;
-    total += t;
-  }
-  if (tid < nw) scan[tid] = before + v - own;
-  __syncthreads();
-  return total;
+// popcount of the bits of a 64-bit wave mask held by lanes below this one.
+__device__ __forceinline__ int rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
-__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a) {
-  extern __shared__ __align__(16) unsigned char lds[];
+// Resolve request b (one workgroup). Leaves the miss list in LDS (msrc/mdst,
+// reusing the hash area) and returns the miss count; all state and outputs
+// are written to global memory.
+__device__ int resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay,
+                       int64_t*& msrc, int32_t*& mdst) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int b = blockIdx.x;
   const int32_t K = a.K, H = a.H;
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
+  uint64_t* hash = reinterpret_cast<uint64_t*>(lds + lay.hash);
+  int32_t* s_out = reinterpret_cast<int32_t*>(lds + lay.out);
+  int32_t* s_topk = reinterpret_cast<int32_t*>(lds + lay.topk);
+  int32_t* s_tok = reinterpret_cast<int32_t*>(lds + lay.tok);
+  uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
+  uint64_t* missw = reinterpret_cast<uint64_t*>(lds + lay.missw);
+  int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
+  int16_t* s_lru = reinterpret_cast<int16_t*>(lds + lay.lru);
+  int16_t* victim = reinterpret_cast<int16_t*>(lds + lay.victim);
+  msrc = reinterpret_cast<int64_t*>(lds + lay.hash);
+  mdst = reinterpret_cast<int32_t*>(lds + lay.hash + 8 * static_cast<uint32_t>(K));
+  const uint32_t tmask = a.T - 1;
+  const int32_t* ids = a.topk + static_cast<int64_t>(b) * a.topk_stride;
+
+  // ---- stage: ids, the LRU row and the slot-token row, into LDS ------------
+  // All global loads of a round are issued before any is consumed, so the
+  // whole stage costs one memory round trip per 4096 entries.
   const int64_t r = a.req_rows[b];
   const int32_t nreal = a.num_real ? *a.num_real : a.B;
+  const int64_t L = a.seq_lens[b];
   if (b >= nreal || r < 0 || r >= a.R) {
     // Padding row (vLLM page's V2 convention): -1 everywhere, no misses.
-    for (int i = tid; i < K; i += kResolveThreads) out[i] = -1;
-    if (tid == 0) {
-      a.ws_count[b] = 0;
-      if (a.miss_counts) a.miss_counts[b] = 0;
-    }
-    return;
+    for (int i = tid; i < K; i += kThreads) out[i] = -1;
+    if (tid == 0 && a.miss_counts) a.miss_counts[b] = 0;
+    __syncthreads();
+    return 0;
   }
-  const int64_t L = a.seq_lens[b];
-  const int32_t* ids = a.topk + static_cast<int64_t>(b) * a.topk_stride;
   int32_t* tokens = a.slot_tokens + r * a.S_r;
   int16_t* lru = a.lru + r * H;
   const int32_t* srows = a.slot_rows ? a.slot_rows + r * a.S_r : nullptr;
   const int64_t* prow = a.pool_rows ? a.pool_rows + r * a.ctx_stride : nullptr;
   const int64_t hot_base = r * a.S_r;
-
-  const LdsLayout lay = lds_layout(K, H, a.T);
-  uint64_t* hash = reinterpret_cast<uint64_t*>(lds + lay.hash);
-  uint64_t* pend = reinterpret_cast<uint64_t*>(lds + lay.pend);
-  uint64_t* hitb = reinterpret_cast<uint64_t*>(lds + lay.hit);
-  uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
-  int32_t* s_topk = reinterpret_cast<int32_t*>(lds + lay.topk);
-  int32_t* scan = reinterpret_cast<int32_t*>(lds + lay.scan);
-  int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
-  int16_t* s_lru = reinterpret_cast<int16_t*>(lds + lay.lru);
-  int16_t* victim = reinterpret_cast<int16_t*>(lds + lay.victim);
-  const uint32_t tmask = a.T - 1;
-  const int kw = (K + 63) / 64, hw = (H + 63) / 64;
-
   auto row_of = [&](int32_t s) -> int32_t {
     return srows ? srows[s] : static_cast<int32_t>(hot_base + s);
   };
   auto pool_of = [&](int64_t t) -> int64_t { return prow ? prow[t] : r * a.ctx_stride + t; };
 
-  // ---- init ---------------------------------------------------------------
-  for (uint32_t i = tid; i < a.T; i += kResolveThreads) hash[i] = kEmpty;
-  for (int i = tid; i < kw; i += kResolveThreads) hitb[i] = 0;
-  if (tid == 0) wtot[kResolveWaves] = 0;  // pending-id counter
+  const int span = K > H ? K : H;
+  for (int base = 0; base < span; base += 4 * kThreads) {
+    int32_t vi[4], vt[4];
+    int16_t vl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      vi[u] = x < K ? ids[x] : 0;
+      vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
+      vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < K) s_topk[x] = vi[u];
+      if (x < H) {
+        s_lru[x] = vl[u];
+        if (a.stage_tokens) s_tok[x] = vt[u];
+      }
+    }
+  }
+  for (uint32_t i = tid; i < a.T; i += kThreads) hash[i] = kEmpty;
+  if (tid == 0) wtot[2 * kWaves] = 0;  // pending-id counter
   __syncthreads();
 
   // ---- 1. classify ids; bind the newest token; insert pending ids ----------
-  // SGLang page: newest token -> newest_slot (= H), everything else hashed.
-  // vLLM page: ids outside the pool resolve to -1 and are not misses.
-  for (int base = 0; base < K; base += kResolveThreads) {
+  // SGLang page: the newest token goes to newest_slot (= H), every other id is
+  // hashed. vLLM page: ids outside the pool resolve to -1 and are not misses.
+  for (int base = 0; base < K; base += kThreads) {
     const int i = base + tid;
-    bool pending = false;
-    if (i < K) {
-      const int32_t t = ids[i];
-      s_topk[i] = t;
-      bool valid = t >= 0 && static_cast<int64_t>(t) < L && static_cast<int64_t>(t) < a.ctx_stride;
-      if (valid) {
-        const int64_t pr = pool_of(t);
-        valid = pr >= 0 && pr < a.pool_nrows;
-      }
-      if (!valid) {
-        out[i] = -1;
-      } else if (static_cast<int64_t>(t) == L - 1) {
-        out[i] = row_of(H);
-      } else {
-        pending = true;
-        const uint64_t entry = (static_cast<uint64_t>(static_cast<uint32_t>(i)) << 32) |
-                               static_cast<uint32_t>(t);
-        uint32_t h = hash_home(t, a.shift);
-        // At most K <= T/2 entries, so an empty cell is always found.
-        while (atomicCAS(reinterpret_cast<unsigned long long*>(&hash[h]),
-                         static_cast<unsigned long long>(kEmpty),
-                         static_cast<unsigned long long>(entry)) != kEmpty) {
-          h = (h + 1) & tmask;
-        }
+    if (i >= K) {
+      (void)__ballot(false);
+      continue;
+    }
+    const int32_t t = s_topk[i];
+    bool valid = t >= 0 && static_cast<int64_t>(t) < L && static_cast<int64_t>(t) < a.ctx_stride;
+    if (valid && prow) {
+      const int64_t pr = prow[t];
+      valid = pr >= 0 && pr < a.pool_nrows;
+    } else if (valid) {
+      valid = r * a.ctx_stride + t < a.pool_nrows;
+    }
+    int32_t o;
+    if (!valid) {
+      o = -1;
+    } else if (static_cast<int64_t>(t) == L - 1) {
+      o = row_of(H);
+    } else {
+      o = kPending;
+      const uint64_t entry = (static_cast<uint64_t>(static_cast<uint32_t>(i)) << 32) |
+                             static_cast<uint32_t>(t);
+      uint32_t h = hash_home(t, a.shift);
+      // At most K <= T/2 entries, so an empty cell is always found.
+      bool ins = true;
+      while (ins) {
+        const unsigned long long prev =
+            atomicCAS(reinterpret_cast<unsigned long long*>(&hash[h]),
+                      static_cast<unsigned long long>(kEmpty), static_cast<unsigned long long>(entry));
+        ins = prev != kEmpty;
+        h = (h + 1) & tmask;
       }
     }
-    const uint64_t m = __ballot(pending);
-    if (lane == 0 && i < K) {
-      pend[i >> 6] = m;
-      if (m) atomicAdd(&wtot[kResolveWaves], static_cast<int>(__popcll(m)));
-    }
+    s_out[i] = o;
+    const uint64_t pm = __ballot(o == kPending);
+    if (lane == 0 && pm) atomicAdd(&wtot[2 * kWaves], static_cast<int>(__popcll(pm)));
   }
   __syncthreads();
-  const int pending_n = wtot[kResolveWaves];
+  const int pending_n = wtot[2 * kWaves];
 
-  // ---- 2a. LRU scan: stage the order, probe each slot's token --------------
-  // A slot whose token is pending is a hit and serves that top-k entry.
-  for (int base = 0; base < H; base += kResolveThreads * 4) {
-    int32_t s[4];
-    int32_t tok[4];
+  // ---- 2a. LRU scan: probe each slot's token -------------------------------
+  // Wave w walks its own segment of LRU positions. A slot whose token is
+  // pending is a hit and serves that top-k entry; the first claimant wins (a
+  // second slot with the same token -- corrupt state -- stays evictable).
+  // Four positions per lane are probed together so four LDS reads are in
+  // flight per lane and the loop runs once per probe step, not per position.
+  const int wave = tid / kWave;
+  const int segH = static_cast<int>(wave_segment(H));
+  const int segK = static_cast<int>(wave_segment(K));
+  const int h0 = wave * segH;
+  int run = 0;
+  for (int c0 = 0; c0 < segH; c0 += 4 * kWave) {
+    int32_t sl[4], key[4], idx[4];
+    uint32_t hh[4];
+    bool act[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = base + u * kResolveThreads + tid;
-      s[u] = p < H ? static_cast<int32_t>(lru[p]) : -1;
+      const int p = h0 + c0 + u * kWave + lane;
+      const bool in = c0 + u * kWave < segH && p < H;
+      sl[u] = in ? s_lru[p] : -1;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = base + u * kResolveThreads + tid;
-      if (p < H) s_lru[p] = static_cast<int16_t>(s[u]);
-      tok[u] = (s[u] >= 0 && s[u] < H) ? tokens[s[u]] : -1;
+      const bool ok = sl[u] >= 0 && sl[u] < H;
+      key[u] = ok ? (a.stage_tokens ? s_tok[sl[u]] : tokens[sl[u]]) : -1;
+      act[u] = key[u] >= 0;
+      hh[u] = hash_home(key[u], a.shift);
+      idx[u] = -1;
     }
+    // Branch-free probe step: every lane reads its four current cells, then
+    // selects; the loop exits when no lane of the wave is still searching.
+    while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
+      uint64_t e[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = base + u * kResolveThreads + tid;
-      bool hit = false;
-      if (tok[u] >= 0) {
-        uint32_t h = hash_home(tok[u], a.shift);
-        int idx = -1;
-        while (true) {
-          const uint64_t e = hash[h];
-          if (e == kEmpty) break;
-          if (static_cast<int32_t>(static_cast<uint32_t>(e)) == tok[u]) {
-            idx = static_cast<int>(e >> 32);
-            break;
-          }
-          h = (h + 1) & tmask;
-        }
-        if (idx >= 0) {
-          // First claimant wins; a second slot with the same token (corrupt
-          // state) is treated as evictable instead of double-serving the entry.
-          const unsigned long long bit = 1ull << (idx & 63);
-          const unsigned long long old =
-              atomicOr(reinterpret_cast<unsigned long long*>(&hitb[idx >> 6]), bit);
-          if (!(old & bit)) {
-            hit = true;
-            out[idx] = row_of(s[u]);
-          }
-        }
+      for (int u = 0; u < 4; ++u) e[u] = hash[hh[u]];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool empty = e[u] == kEmpty;
+        const bool match = static_cast<int32_t>(static_cast<uint32_t>(e[u])) == key[u] && !empty;
+        idx[u] = (act[u] && match) ? static_cast<int>(e[u] >> 32) : idx[u];
+        act[u] = act[u] && !empty && !match;
+        hh[u] = act[u] ? ((hh[u] + 1) & tmask) : hh[u];
       }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool hit = idx[u] >= 0 && atomicCAS(&s_out[idx[u]], kPending, row_of(sl[u])) == kPending;
       const uint64_t m = __ballot(hit);
-      if (lane == 0 && p < H) hitpos[p >> 6] = m;
+      const int p0 = h0 + c0 + u * kWave;
+      if (c0 + u * kWave < segH && p0 < H) {
+        if (lane == 0) hitpos[p0 >> 6] = m;
+        run += __popcll(m);
+      }
     }
   }
+  int32_t* wt_hit = wtot;
+  int32_t* wt_miss = wtot + kWaves;
+  if (lane == 0) wt_hit[wave] = run;
   __syncthreads();
 
-  // ---- 2b. ranks of hits among LRU positions -------------------------------
-  const int hits = block_popc_scan([&](int w) { return hitpos[w]; }, hw, scan, wtot);
+  // ---- 2b. victims and the new LRU order -----------------------------------
+  // New order: stale evictables, then the M victims (they receive the misses,
+  // in miss order), then the hits -- every group in its old order. A
+  // position's rank among hits is the hits of earlier waves, plus this wave's
+  // earlier chunks, plus the hit lanes below it.
+  int hits = 0, hits_before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = wt_hit[w];
+    hits += t;
+    hits_before += w < wave ? t : 0;
+  }
   const int E = H - hits;            // evictable slots
   const int M = pending_n - hits;    // misses (<= E because K <= H)
-
-  // ---- 2c. victims and the new LRU order -----------------------------------
-  // New order: stale evictables, then the M victims (they receive the misses,
-  // in miss order), then the hits -- every group in its old order.
-  for (int base = 0; base < H; base += kResolveThreads) {
-    const int p = base + tid;
+  run = hits_before;
+  for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += kWave) {
+    const int p = h0 + c0 + lane;
+    const uint64_t wd = hitpos[(h0 + c0) >> 6];
     if (p < H) {
-      const uint64_t wd = hitpos[p >> 6];
-      const int bp = p & 63;
-      const int hr = scan[p >> 6] + __popcll(wd & ((1ull << bp) - 1ull));
-      const int16_t s = s_lru[p];
+      const int hr = run + rank_below(wd);
+      const int16_t sp = s_lru[p];
       int np;
-      if ((wd >> bp) & 1ull) {
+      if ((wd >> lane) & 1ull) {
         np = E + hr;
       } else {
         const int e = p - hr;
         if (e < M) {
-          victim[e] = s;
+          victim[e] = sp;
           np = E - M + e;
         } else {
           np = e - M;
         }
       }
-      lru[np] = s;
+      lru[np] = sp;
     }
+    run += __popcll(wd);
+  }
+  // miss words over this wave's segment of top-k indices: ids still pending
+  const int k0 = wave * segK;
+  run = 0;
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kWave) {
+    const int i = k0 + c0 + lane;
+    const uint64_t m = __ballot(i < K && s_out[i] == kPending);
+    if (lane == 0) missw[(k0 + c0) >> 6] = m;
+    run += __popcll(m);
+  }
+  if (lane == 0) wt_miss[wave] = run;
+  __syncthreads();
+
+  // ---- 3. misses in top-k order take victims --------------------------------
+  int m_total = 0, miss_before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = wt_miss[w];
+    m_total += t;
+    miss_before += w < wave ? t : 0;
+  }
+  run = miss_before;
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kWave) {
+    const int i = k0 + c0 + lane;
+    const uint64_t wd = missw[(k0 + c0) >> 6];
+    if ((wd >> lane) & 1ull) {
+      const int m = run + rank_below(wd);
+      const int32_t t = s_topk[i];
+      const int32_t v = m < M ? victim[m] : -1;
+      if (v >= 0 && v < H) {
+        const int32_t row = row_of(v);
+        s_out[i] = row;
+        tokens[v] = t;
+        msrc[m] = pool_of(t);
+        mdst[m] = row;
+      } else {
+        s_out[i] = -1;
+        msrc[m] = 0;
+        mdst[m] = -1;
+      }
+    }
+    run += __popcll(wd);
   }
   __syncthreads();
 
-  // ---- 3. misses in top-k order take victims; publish the copy list --------
-  auto miss_word = [&](int w) { return pend[w] & ~hitb[w]; };
-  const int m_total = block_popc_scan(miss_word, kw, scan, wtot);
-  int64_t* ws_src = a.ws_src + static_cast<int64_t>(b) * K;
-  int32_t* ws_dst = a.ws_dst + static_cast<int64_t>(b) * K;
-  for (int base = 0; base < K; base += kResolveThreads) {
-    const int i = base + tid;
-    if (i < K) {
-      const uint64_t wd = miss_word(i >> 6);
-      const int bp = i & 63;
-      if ((wd >> bp) & 1ull) {
-        const int m = scan[i >> 6] + __popcll(wd & ((1ull << bp) - 1ull));
-        const int32_t t = s_topk[i];
-        const int32_t v = m < M ? victim[m] : -1;
-        if (v >= 0 && v < H) {
-          const int32_t row = row_of(v);
-          out[i] = row;
-          tokens[v] = t;
-          ws_src[m] = pool_of(t);
-          ws_dst[m] = row;
-        } else {
-          out[i] = -1;
-          ws_src[m] = 0;
-          ws_dst[m] = -1;
-        }
-      }
-    }
-  }
-  if (tid == 0) {
-    a.ws_count[b] = m_total;
-    if (a.miss_counts) a.miss_counts[b] = m_total;
-  }
+  // ---- 4. outputs ------------------------------------------------------------
+  for (int i = tid; i < K; i += kThreads) out[i] = s_out[i];
+  if (tid == 0 && a.miss_counts) a.miss_counts[b] = m_total;
+  return m_total;
 }
 
-// Copy the published misses: workgroup g serves request g % B, part g / B.
+// Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
+// (pool row, hot row) and its length to the workspace for the copy kernel.
+__global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0);
+  const int b = blockIdx.x;
+  int64_t* msrc;
+  int32_t* mdst;
+  const int M = resolve(a, b, lds, lay, msrc, mdst);
+  int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
+  int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
+  for (int m = threadIdx.x; m < M; m += kThreads) {
+    src[m] = msrc[m];
+    dst[m] = mdst[m];
+  }
+  if (threadIdx.x == 0) a.count[b] = M;
+}
+
+// Copy the published misses as a flat stream of W-byte chunks: workgroup g
+// serves request g % B, part g / B of `parts`. Consecutive lanes take
+// consecutive chunks of a row, so each wave's accesses coalesce, and every
+// lane keeps kCopyUnroll independent loads in flight.
 template <int W>
-__global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(
-    const char* __restrict__ pool, char* __restrict__ hot, int64_t row_bytes, int64_t hot_nrows,
-    const int32_t* __restrict__ ws_count, const int64_t* __restrict__ ws_src,
-    const int32_t* __restrict__ ws_dst, int32_t B, int32_t K, int32_t parts, FastDiv cdiv) {
+__global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(SwapArgs a, int32_t parts) {
   typedef Chunk<W> C;
-  const int b = blockIdx.x % B;
-  const int part = blockIdx.x / B;
-  const int M = ws_count[b];
-  const uint32_t total = static_cast<uint32_t>(M) * cdiv.d;
-  const int64_t* src = ws_src + static_cast<int64_t>(b) * K;
-  const int32_t* dst = ws_dst + static_cast<int64_t>(b) * K;
+  const int b = blockIdx.x % a.B;
+  const int part = blockIdx.x / a.B;
+  const int M = a.count[b];
+  const uint32_t total = static_cast<uint32_t>(M) * a.cdiv.d;
+  const int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
+  const int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
   const uint32_t stride = static_cast<uint32_t>(parts) * kCopyThreads;
   for (uint32_t j0 = static_cast<uint32_t>(part) * kCopyThreads + threadIdx.x; j0 < total;
        j0 += stride * kCopyUnroll) {
@@ -346,12 +416,13 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(
       const uint32_t j = j0 + u * stride;
       d[u] = nullptr;
       if (j < total) {
-        const uint32_t m = fdiv(j, cdiv);
-        const uint32_t c = j - m * cdiv.d;
+        const uint32_t m = fdiv(j, a.cdiv);
+        const uint32_t c = j - m * a.cdiv.d;
         const int32_t hr = dst[m];
-        if (hr >= 0 && hr < hot_nrows) {
-          v[u] = C::load(pool + src[m] * row_bytes + static_cast<int64_t>(c) * W);
-          d[u] = hot + static_cast<int64_t>(hr) * row_bytes + static_cast<int64_t>(c) * W;
+        if (hr >= 0 && hr < a.hot_nrows) {
+          const int64_t off = static_cast<int64_t>(c) * W;
+          v[u] = C::load(a.pool + src[m] * a.row_bytes + off);
+          d[u] = a.hot + static_cast<int64_t>(hr) * a.row_bytes + off;
         }
       }
     }
@@ -370,7 +441,7 @@ struct WsLayout {
 inline WsLayout ws_layout(int64_t B, int64_t K) {
   WsLayout w;
   w.count = 0;
-  w.src = align256(4 * static_cast<size_t>(B));
+  w.src = w.count + align256(4 * static_cast<size_t>(B));
   w.dst = w.src + align256(8 * static_cast<size_t>(B) * static_cast<size_t>(K));
   w.total = w.dst + align256(4 * static_cast<size_t>(B) * static_cast<size_t>(K));
   return w;
@@ -430,14 +501,27 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   DeviceInfo di;
   int rc = device_info(&di);
   if (rc != HS_OK) return rc;
-  const uint32_t T = pow2_at_least(static_cast<uint32_t>(2 * a->K) < 64 ? 64u : static_cast<uint32_t>(2 * a->K));
-  uint32_t log2T = 0;
-  while ((1u << log2T) < T) ++log2T;
-  const LdsLayout lay = lds_layout(a->K, a->H, T);
-  if (static_cast<int>(lay.total) > di.max_lds)
+  // LDS plan, best first: a quarter-full hash table with the slot-token row
+  // staged; a half-full table with the row staged; then the same without
+  // staging (tokens gathered from HBM). Shorter probe chains matter most: a
+  // wave's probe loop runs as long as its longest chain.
+  const uint32_t k2 = 2u * static_cast<uint32_t>(a->K) < 64u ? 64u : 2u * static_cast<uint32_t>(a->K);
+  const uint32_t plans_T[4] = {pow2_at_least(2 * k2), pow2_at_least(k2), pow2_at_least(2 * k2),
+                               pow2_at_least(k2)};
+  const bool plans_stage[4] = {true, true, false, false};
+  int plan = -1;
+  LdsLayout lay{};
+  for (int i = 0; i < 4 && plan < 0; ++i) {
+    lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i]);
+    if (static_cast<int>(lay.total) <= di.max_lds) plan = i;
+  }
+  if (plan < 0)
     return set_error(HS_ERANGE, "K=%d, H=%d need %u bytes of LDS; the device allows %d", a->K,
                      a->H, lay.total, di.max_lds);
-
+  const uint32_t T = plans_T[plan];
+  const bool stage = plans_stage[plan];
+  uint32_t log2T = 0;
+  while ((1u << log2T) < T) ++log2T;
   if (lay.total > 65536) {
     // Opt in to more than 64 KB of dynamic LDS (gfx950 has 160 KB per CU).
     const hipError_t fe = hipFuncSetAttribute(reinterpret_cast<const void*>(&resolve_kernel),
@@ -467,53 +551,55 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   }
 
   char* ws = static_cast<char*>(workspace);
-  ResolveArgs ra;
-  ra.topk = a->topk_ids;
-  ra.topk_stride = a->topk_stride;
-  ra.req_rows = a->req_rows;
-  ra.seq_lens = a->seq_lens;
-  ra.num_real = a->num_real;
-  ra.slot_tokens = a->slot_tokens;
-  ra.lru = a->lru;
-  ra.slot_rows = a->slot_rows;
-  ra.pool_rows = a->pool_rows;
-  ra.ctx_stride = a->ctx_stride;
-  ra.pool_nrows = a->pool_nrows;
-  ra.out_rows = a->out_rows;
-  ra.miss_counts = a->miss_counts;
-  ra.ws_count = reinterpret_cast<int32_t*>(ws + wl.count);
-  ra.ws_src = reinterpret_cast<int64_t*>(ws + wl.src);
-  ra.ws_dst = reinterpret_cast<int32_t*>(ws + wl.dst);
-  ra.B = a->B;
-  ra.K = a->K;
-  ra.H = a->H;
-  ra.S_r = a->S_r;
-  ra.R = a->R;
-  ra.T = T;
-  ra.shift = 32 - log2T;
+  SwapArgs s;
+  s.topk = a->topk_ids;
+  s.topk_stride = a->topk_stride;
+  s.req_rows = a->req_rows;
+  s.seq_lens = a->seq_lens;
+  s.num_real = a->num_real;
+  s.slot_tokens = a->slot_tokens;
+  s.lru = a->lru;
+  s.slot_rows = a->slot_rows;
+  s.pool_rows = a->pool_rows;
+  s.ctx_stride = a->ctx_stride;
+  s.pool = pool_dev;
+  s.pool_nrows = a->pool_nrows;
+  s.hot = static_cast<char*>(a->hot);
+  s.hot_nrows = a->hot_nrows;
+  s.row_bytes = a->row_bytes;
+  s.out_rows = a->out_rows;
+  s.miss_counts = a->miss_counts;
+  s.count = reinterpret_cast<int32_t*>(ws + wl.count);
+  s.src = reinterpret_cast<int64_t*>(ws + wl.src);
+  s.dst = reinterpret_cast<int32_t*>(ws + wl.dst);
+  s.B = a->B;
+  s.K = a->K;
+  s.H = a->H;
+  s.S_r = a->S_r;
+  s.R = a->R;
+  s.T = T;
+  s.shift = 32 - log2T;
+  s.stage_tokens = stage ? 1 : 0;
+  s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
 
-  hipLaunchKernelGGL(resolve_kernel, dim3(a->B), dim3(kResolveThreads), lay.total, stream, ra);
+  hipLaunchKernelGGL(resolve_kernel, dim3(a->B), dim3(kThreads), lay.total, stream, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "resolve launch: %s", hipGetErrorString(e));
 
   // Copy grid: enough workgroups per request to cover its worst case (all K
-  // missing) at kCopyUnroll chunks per lane, capped so the whole launch is a
-  // few thousand workgroups.
+  // ids missing) at kCopyUnroll chunks per lane, capped at 8 per CU overall.
   const int64_t max_items = static_cast<int64_t>(a->K) * C;
   int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
   const int64_t cap = (8LL * di.num_cus + a->B - 1) / a->B;
   if (parts > cap) parts = cap;
   if (parts < 1) parts = 1;
-  const FastDiv cdiv = make_fastdiv(static_cast<uint32_t>(C));
   const dim3 grid(static_cast<unsigned>(a->B * parts));
   if (W == 16)
-    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, pool_dev,
-                       static_cast<char*>(a->hot), a->row_bytes, a->hot_nrows, ra.ws_count,
-                       ra.ws_src, ra.ws_dst, a->B, a->K, static_cast<int32_t>(parts), cdiv);
+    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, s,
+                       static_cast<int32_t>(parts));
   else
-    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, pool_dev,
-                       static_cast<char*>(a->hot), a->row_bytes, a->hot_nrows, ra.ws_count,
-                       ra.ws_src, ra.ws_dst, a->B, a->K, static_cast<int32_t>(parts), cdiv);
+    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, s,
+                       static_cast<int32_t>(parts));
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "copy launch: %s", hipGetErrorString(e));
   return HS_OK;

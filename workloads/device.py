@@ -50,7 +50,7 @@ class DeviceSwapState:
                                device=device)
         self.out = torch.empty((cfg.B, cfg.K), dtype=torch.int32, device=device)
         self.counts = torch.empty(cfg.B, dtype=torch.int32, device=device)
-        self.ws = torch.empty(hs.swap_in_workspace_bytes(cfg.B, cfg.K), dtype=torch.uint8,
+        self.ws = torch.zeros(hs.swap_in_workspace_bytes(cfg.B, cfg.K), dtype=torch.uint8,
                               device=device)
 
 
