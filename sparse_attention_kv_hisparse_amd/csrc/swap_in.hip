@@ -38,12 +38,13 @@ constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresol
 constexpr uint64_t kEmpty = ~0ull;         // (token -1, index 0xFFFFFFFF): never live
 
 // Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by
-// floor(2^32 / golden ratio) = 2654435761 and keep the TOP log2(T) bits of the
-// 32-bit product. Both pages use this multiplier but keep the low bits
-// (product mod size), which for power-of-two sizes only permutes id mod size;
-// the high bits spread ids that share low bits. Only speed depends on this.
-__device__ __forceinline__ uint32_t hash_home(int32_t key, uint32_t shift) {
-  return (static_cast<uint32_t>(key) * 2654435761u) >> shift;
+// floor(2^32 / golden ratio) = 2654435761 and keep the TOP bits of the 32-bit
+// product -- here the top log2(buckets) bits pick the home bucket. Both pages
+// use this multiplier but keep the low bits (product mod size), which for
+// power-of-two sizes only permutes id mod size; the high bits spread ids that
+// share low bits. Only speed depends on this choice, never a result.
+__device__ __forceinline__ uint32_t bucket_of(int32_t key, uint32_t bshift) {
+  return (static_cast<uint32_t>(key) * 2654435761u) >> bshift;
 }
 
 struct SwapArgs {
@@ -76,7 +77,7 @@ struct SwapArgs {
 };
 
 struct LdsLayout {
-  uint32_t hash, out, topk, lru, tok, victim, hitpos, missw, wtot, total;
+  uint32_t hash, out, topk, lru, tok, victim, hitpos, missw, wtot, dummy, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
@@ -100,6 +101,7 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.hitpos = o; o = align_up(o + 8 * hwords, 16);
   l.missw = o;  o = align_up(o + 8 * kwords, 16);
   l.wtot = o;   o = align_up(o + 4 * 3 * kWaves + 16, 16);
+  l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
   l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
   l.total = o;
@@ -115,10 +117,19 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // Resolve request b (one workgroup). Leaves the miss list in LDS (msrc/mdst,
 // reusing the hash area) and returns the miss count; all state and outputs
 // are written to global memory.
-__device__ int resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay,
-                       int64_t*& msrc, int32_t*& mdst) {
+// kSlotRows / kPoolRows: whether the slot-row and pool-row tables are given.
+// Without them no global load follows the first global store, so no wait on
+// outstanding stores (vmcnt counts both) ever stalls a phase.
+//
+// LDS latency is ~230 cycles on gfx950, so every phase issues all of its
+// independent LDS reads first and then works from registers; the hash is
+// bucketed (four 8-byte entries per 32-byte bucket, at most a quarter full)
+// so a lookup almost always ends after one bucket read.
+template <bool kSlotRows, bool kPoolRows>
+__device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int32_t K = a.K, H = a.H;
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
@@ -129,50 +140,65 @@ __device__ int resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLa
   uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
   uint64_t* missw = reinterpret_cast<uint64_t*>(lds + lay.missw);
   int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
+  int32_t* wt_hit = wtot;
+  int32_t* wt_miss = wtot + kWaves;
+  int32_t* s_pending = wtot + 2 * kWaves;
   int16_t* s_lru = reinterpret_cast<int16_t*>(lds + lay.lru);
   int16_t* victim = reinterpret_cast<int16_t*>(lds + lay.victim);
-  msrc = reinterpret_cast<int64_t*>(lds + lay.hash);
-  mdst = reinterpret_cast<int32_t*>(lds + lay.hash + 8 * static_cast<uint32_t>(K));
-  const uint32_t tmask = a.T - 1;
+  // Inactive lanes aim their CAS at a private word, so the CAS of every
+  // query can be issued unconditionally and all are in flight together.
+  unsigned long long* sink64 = reinterpret_cast<unsigned long long*>(lds + lay.dummy) + tid;
+  int32_t* sink32 = reinterpret_cast<int32_t*>(sink64);
+  const uint32_t bmask = a.T / 4 - 1;       // buckets - 1
+  const uint32_t bshift = a.shift + 2;      // top log2(buckets) bits
   const int32_t* ids = a.topk + static_cast<int64_t>(b) * a.topk_stride;
 
-  // ---- stage: ids, the LRU row and the slot-token row, into LDS ------------
-  // All global loads of a round are issued before any is consumed, so the
-  // whole stage costs one memory round trip per 4096 entries.
   const int64_t r = a.req_rows[b];
   const int32_t nreal = a.num_real ? *a.num_real : a.B;
   const int64_t L = a.seq_lens[b];
   if (b >= nreal || r < 0 || r >= a.R) {
     // Padding row (vLLM page's V2 convention): -1 everywhere, no misses.
     for (int i = tid; i < K; i += kThreads) out[i] = -1;
-    if (tid == 0 && a.miss_counts) a.miss_counts[b] = 0;
-    __syncthreads();
-    return 0;
+    if (tid == 0) {
+      a.count[b] = 0;
+      if (a.miss_counts) a.miss_counts[b] = 0;
+    }
+    return;
   }
   int32_t* tokens = a.slot_tokens + r * a.S_r;
   int16_t* lru = a.lru + r * H;
-  const int32_t* srows = a.slot_rows ? a.slot_rows + r * a.S_r : nullptr;
-  const int64_t* prow = a.pool_rows ? a.pool_rows + r * a.ctx_stride : nullptr;
+  const int32_t* srows = kSlotRows ? a.slot_rows + r * a.S_r : nullptr;
+  const int64_t* prow = kPoolRows ? a.pool_rows + r * a.ctx_stride : nullptr;
   const int64_t hot_base = r * a.S_r;
   auto row_of = [&](int32_t s) -> int32_t {
-    return srows ? srows[s] : static_cast<int32_t>(hot_base + s);
+    if constexpr (kSlotRows) return srows[s];
+    return static_cast<int32_t>(hot_base + s);
   };
-  auto pool_of = [&](int64_t t) -> int64_t { return prow ? prow[t] : r * a.ctx_stride + t; };
+  auto pool_of = [&](int64_t t) -> int64_t {
+    if constexpr (kPoolRows) return prow[t];
+    return r * a.ctx_stride + t;
+  };
 
-  const int span = K > H ? K : H;
-  for (int base = 0; base < span; base += 4 * kThreads) {
-    int32_t vi[4], vt[4];
+  // ---- stage: ids, the LRU row and the slot-token row -----------------------
+  // The first 4096 entries of each land in registers with all loads in flight
+  // at once; the hash table is cleared while they are outstanding.
+  int32_t vi[4];
+  {
+    int32_t vt[4];
     int16_t vl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
+      const int x = u * kThreads + tid;
       vi[u] = x < K ? ids[x] : 0;
       vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
+    u64x2* h2 = reinterpret_cast<u64x2*>(hash);
+    for (uint32_t i = tid; i < a.T / 2; i += kThreads) h2[i] = u64x2{kEmpty, kEmpty};
+    if (tid == 0) *s_pending = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
+      const int x = u * kThreads + tid;
       if (x < K) s_topk[x] = vi[u];
       if (x < H) {
         s_lru[x] = vl[u];
@@ -180,101 +206,152 @@ __device__ int resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLa
       }
     }
   }
-  for (uint32_t i = tid; i < a.T; i += kThreads) hash[i] = kEmpty;
-  if (tid == 0) wtot[2 * kWaves] = 0;  // pending-id counter
+  const int span = K > H ? K : H;
+  for (int base = 4 * kThreads; base < span; base += 4 * kThreads) {
+    int32_t wi[4], wt[4];
+    int16_t wl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      wi[u] = x < K ? ids[x] : 0;
+      wl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
+      wt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < K) s_topk[x] = wi[u];
+      if (x < H) {
+        s_lru[x] = wl[u];
+        if (a.stage_tokens) s_tok[x] = wt[u];
+      }
+    }
+  }
   __syncthreads();
 
   // ---- 1. classify ids; bind the newest token; insert pending ids ----------
   // SGLang page: the newest token goes to newest_slot (= H), every other id is
   // hashed. vLLM page: ids outside the pool resolve to -1 and are not misses.
-  for (int base = 0; base < K; base += kThreads) {
-    const int i = base + tid;
-    if (i >= K) {
-      (void)__ballot(false);
-      continue;
+  for (int base = 0; base < K; base += 4 * kThreads) {
+    int32_t t[4], o[4];
+    uint32_t bk[4];
+    uint64_t ent[4];
+    bool ins[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kThreads + tid;
+      t[u] = base == 0 ? vi[u] : (i < K ? s_topk[i] : 0);
     }
-    const int32_t t = s_topk[i];
-    bool valid = t >= 0 && static_cast<int64_t>(t) < L && static_cast<int64_t>(t) < a.ctx_stride;
-    if (valid && prow) {
-      const int64_t pr = prow[t];
-      valid = pr >= 0 && pr < a.pool_nrows;
-    } else if (valid) {
-      valid = r * a.ctx_stride + t < a.pool_nrows;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kThreads + tid;
+      bool valid = i < K && t[u] >= 0 && static_cast<int64_t>(t[u]) < L &&
+                   static_cast<int64_t>(t[u]) < a.ctx_stride;
+      if (valid) {
+        const int64_t pr = pool_of(t[u]);
+        valid = pr >= 0 && pr < a.pool_nrows;
+      }
+      const bool newest = valid && static_cast<int64_t>(t[u]) == L - 1;
+      ins[u] = valid && !newest;
+      o[u] = !valid ? -1 : (newest ? row_of(H) : kPending);
+      ent[u] = (static_cast<uint64_t>(static_cast<uint32_t>(i)) << 32) | static_cast<uint32_t>(t[u]);
+      bk[u] = bucket_of(t[u], bshift);
     }
-    int32_t o;
-    if (!valid) {
-      o = -1;
-    } else if (static_cast<int64_t>(t) == L - 1) {
-      o = row_of(H);
-    } else {
-      o = kPending;
-      const uint64_t entry = (static_cast<uint64_t>(static_cast<uint32_t>(i)) << 32) |
-                             static_cast<uint32_t>(t);
-      uint32_t h = hash_home(t, a.shift);
-      // At most K <= T/2 entries, so an empty cell is always found.
-      bool ins = true;
-      while (ins) {
-        const unsigned long long prev =
-            atomicCAS(reinterpret_cast<unsigned long long*>(&hash[h]),
-                      static_cast<unsigned long long>(kEmpty), static_cast<unsigned long long>(entry));
-        ins = prev != kEmpty;
-        h = (h + 1) & tmask;
+    int npend = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) npend += __popcll(__ballot(ins[u]));
+    // Linear probing in entry order from the first entry of the home bucket
+    // (a lookup reads whole buckets and stops at one with a free entry, which
+    // this order guarantees to be past the key). K < T, so it terminates.
+    uint32_t e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = 4 * bk[u];
+    const uint32_t emask = a.T - 1;
+    while (__ballot(ins[0] | ins[1] | ins[2] | ins[3]) != 0) {
+      unsigned long long prev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        prev[u] = atomicCAS(ins[u] ? reinterpret_cast<unsigned long long*>(hash + e[u]) : sink64,
+                            static_cast<unsigned long long>(kEmpty),
+                            static_cast<unsigned long long>(ent[u]));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool taken = prev[u] != kEmpty;
+        e[u] = (ins[u] && taken) ? ((e[u] + 1) & emask) : e[u];
+        ins[u] = ins[u] && taken;
       }
     }
-    s_out[i] = o;
-    const uint64_t pm = __ballot(o == kPending);
-    if (lane == 0 && pm) atomicAdd(&wtot[2 * kWaves], static_cast<int>(__popcll(pm)));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kThreads + tid;
+      if (i < K) s_out[i] = o[u];
+    }
+    if (lane == 0 && npend) atomicAdd(s_pending, npend);
   }
   __syncthreads();
-  const int pending_n = wtot[2 * kWaves];
 
-  // ---- 2a. LRU scan: probe each slot's token -------------------------------
-  // Wave w walks its own segment of LRU positions. A slot whose token is
-  // pending is a hit and serves that top-k entry; the first claimant wins (a
-  // second slot with the same token -- corrupt state -- stays evictable).
-  // Four positions per lane are probed together so four LDS reads are in
-  // flight per lane and the loop runs once per probe step, not per position.
-  const int wave = tid / kWave;
+  // ---- 2. LRU scan: probe each slot's token -------------------------------
+  // Wave w walks its own 64-aligned segment of LRU positions. A slot whose
+  // token is pending is a hit and serves that top-k entry; the first claimant
+  // wins (a second slot with the same token -- corrupt state -- stays
+  // evictable instead of serving the entry twice).
+  const int pending_n = *s_pending;
   const int segH = static_cast<int>(wave_segment(H));
   const int segK = static_cast<int>(wave_segment(K));
   const int h0 = wave * segH;
+  const int k0 = wave * segK;
   int run = 0;
   for (int c0 = 0; c0 < segH; c0 += 4 * kWave) {
     int32_t sl[4], key[4], idx[4];
-    uint32_t hh[4];
+    uint32_t bk[4];
     bool act[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      const bool in = c0 + u * kWave < segH && p < H;
-      sl[u] = in ? s_lru[p] : -1;
+      sl[u] = (c0 + u * kWave < segH && p < H) ? s_lru[p] : -1;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool ok = sl[u] >= 0 && sl[u] < H;
       key[u] = ok ? (a.stage_tokens ? s_tok[sl[u]] : tokens[sl[u]]) : -1;
       act[u] = key[u] >= 0;
-      hh[u] = hash_home(key[u], a.shift);
+      bk[u] = bucket_of(key[u], bshift);
       idx[u] = -1;
     }
-    // Branch-free probe step: every lane reads its four current cells, then
-    // selects; the loop exits when no lane of the wave is still searching.
+    // Branch-free lookup step over one bucket per query; ends when no lane of
+    // the wave is still searching (a bucket with an empty entry ends a miss).
     while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
-      uint64_t e[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = hash[hh[u]];
+      u64x2 lo[4], hi[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool empty = e[u] == kEmpty;
-        const bool match = static_cast<int32_t>(static_cast<uint32_t>(e[u])) == key[u] && !empty;
-        idx[u] = (act[u] && match) ? static_cast<int>(e[u] >> 32) : idx[u];
-        act[u] = act[u] && !empty && !match;
-        hh[u] = act[u] ? ((hh[u] + 1) & tmask) : hh[u];
+        const u64x2* bp = reinterpret_cast<const u64x2*>(hash + 4 * bk[u]);
+        lo[u] = bp[0];
+        hi[u] = bp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t kk = key[u];
+        const bool m0 = static_cast<int32_t>(static_cast<uint32_t>(lo[u].x)) == kk;
+        const bool m1 = static_cast<int32_t>(static_cast<uint32_t>(lo[u].y)) == kk;
+        const bool m2 = static_cast<int32_t>(static_cast<uint32_t>(hi[u].x)) == kk;
+        const bool m3 = static_cast<int32_t>(static_cast<uint32_t>(hi[u].y)) == kk;
+        const uint64_t e = m0 ? lo[u].x : m1 ? lo[u].y : m2 ? hi[u].x : hi[u].y;
+        const bool found = m0 | m1 | m2 | m3;
+        const bool open = lo[u].x == kEmpty || lo[u].y == kEmpty || hi[u].x == kEmpty ||
+                          hi[u].y == kEmpty;
+        idx[u] = (act[u] && found) ? static_cast<int>(e >> 32) : idx[u];
+        act[u] = act[u] && !found && !open;
+        bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
       }
     }
+    int32_t prev[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending,
+                          idx[u] >= 0 ? row_of(sl[u]) : 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool hit = idx[u] >= 0 && atomicCAS(&s_out[idx[u]], kPending, row_of(sl[u])) == kPending;
+      const bool hit = idx[u] >= 0 && prev[u] == kPending;
       const uint64_t m = __ballot(hit);
       const int p0 = h0 + c0 + u * kWave;
       if (c0 + u * kWave < segH && p0 < H) {
@@ -283,114 +360,155 @@ __device__ int resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLa
       }
     }
   }
-  int32_t* wt_hit = wtot;
-  int32_t* wt_miss = wtot + kWaves;
   if (lane == 0) wt_hit[wave] = run;
   __syncthreads();
 
-  // ---- 2b. victims and the new LRU order -----------------------------------
+  // ---- 3. victims, the new LRU order, miss words ----------------------------
   // New order: stale evictables, then the M victims (they receive the misses,
   // in miss order), then the hits -- every group in its old order. A
   // position's rank among hits is the hits of earlier waves, plus this wave's
   // earlier chunks, plus the hit lanes below it.
   int hits = 0, hits_before = 0;
+  {
+    const int4* w4 = reinterpret_cast<const int4*>(wt_hit);
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = wt_hit[w];
-    hits += t;
-    hits_before += w < wave ? t : 0;
+    for (int q = 0; q < kWaves / 4; ++q) {
+      const int4 v = w4[q];
+      const int t4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hits += t4[k];
+        hits_before += (4 * q + k) < wave ? t4[k] : 0;
+      }
+    }
   }
   const int E = H - hits;            // evictable slots
   const int M = pending_n - hits;    // misses (<= E because K <= H)
   run = hits_before;
-  for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += kWave) {
-    const int p = h0 + c0 + lane;
-    const uint64_t wd = hitpos[(h0 + c0) >> 6];
-    if (p < H) {
-      const int hr = run + rank_below(wd);
-      const int16_t sp = s_lru[p];
-      int np;
-      if ((wd >> lane) & 1ull) {
-        np = E + hr;
-      } else {
-        const int e = p - hr;
-        if (e < M) {
-          victim[e] = sp;
-          np = E - M + e;
-        } else {
-          np = e - M;
-        }
-      }
-      lru[np] = sp;
+  for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += 4 * kWave) {
+    uint64_t wd[4];
+    int16_t sp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = h0 + c0 + u * kWave;     // chunk start
+      const bool in = c0 + u * kWave < segH && q < H;
+      wd[u] = in ? hitpos[q >> 6] : 0;
+      sp[u] = (in && q + lane < H) ? s_lru[q + lane] : static_cast<int16_t>(0);
     }
-    run += __popcll(wd);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + c0 + u * kWave + lane;
+      if (c0 + u * kWave < segH && p < H) {
+        const int hr = run + rank_below(wd[u]);
+        int np;
+        if ((wd[u] >> lane) & 1ull) {
+          np = E + hr;
+        } else {
+          const int e = p - hr;
+          if (e < M) {
+            victim[e] = sp[u];
+            np = E - M + e;
+          } else {
+            np = e - M;
+          }
+        }
+        lru[np] = sp[u];
+      }
+      run += __popcll(wd[u]);
+    }
   }
-  // miss words over this wave's segment of top-k indices: ids still pending
-  const int k0 = wave * segK;
   run = 0;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kWave) {
-    const int i = k0 + c0 + lane;
-    const uint64_t m = __ballot(i < K && s_out[i] == kPending);
-    if (lane == 0) missw[(k0 + c0) >> 6] = m;
-    run += __popcll(m);
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
+    int32_t so[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = k0 + c0 + u * kWave + lane;
+      so[u] = (c0 + u * kWave < segK && i < K) ? s_out[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = k0 + c0 + u * kWave;
+      const uint64_t mm = __ballot(so[u] == kPending);
+      if (c0 + u * kWave < segK && q < K) {
+        if (lane == 0) missw[q >> 6] = mm;
+        run += __popcll(mm);
+      }
+    }
   }
   if (lane == 0) wt_miss[wave] = run;
   __syncthreads();
 
-  // ---- 3. misses in top-k order take victims --------------------------------
+  // ---- 4. misses in top-k order take victims; outputs; copy list -----------
+  // Each wave finishes its own segment of top-k entries: the entries it does
+  // not fill were final before the last barrier.
   int m_total = 0, miss_before = 0;
+  {
+    const int4* w4 = reinterpret_cast<const int4*>(wt_miss);
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = wt_miss[w];
-    m_total += t;
-    miss_before += w < wave ? t : 0;
-  }
-  run = miss_before;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kWave) {
-    const int i = k0 + c0 + lane;
-    const uint64_t wd = missw[(k0 + c0) >> 6];
-    if ((wd >> lane) & 1ull) {
-      const int m = run + rank_below(wd);
-      const int32_t t = s_topk[i];
-      const int32_t v = m < M ? victim[m] : -1;
-      if (v >= 0 && v < H) {
-        const int32_t row = row_of(v);
-        s_out[i] = row;
-        tokens[v] = t;
-        msrc[m] = pool_of(t);
-        mdst[m] = row;
-      } else {
-        s_out[i] = -1;
-        msrc[m] = 0;
-        mdst[m] = -1;
+    for (int q = 0; q < kWaves / 4; ++q) {
+      const int4 v = w4[q];
+      const int t4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m_total += t4[k];
+        miss_before += (4 * q + k) < wave ? t4[k] : 0;
       }
     }
-    run += __popcll(wd);
   }
-  __syncthreads();
-
-  // ---- 4. outputs ------------------------------------------------------------
-  for (int i = tid; i < K; i += kThreads) out[i] = s_out[i];
-  if (tid == 0 && a.miss_counts) a.miss_counts[b] = m_total;
-  return m_total;
+  int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
+  int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
+  run = miss_before;
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
+    uint64_t wd[4];
+    int32_t so[4], t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = k0 + c0 + u * kWave;
+      const int i = q + lane;
+      const bool in = c0 + u * kWave < segK && q < K;
+      wd[u] = in ? missw[q >> 6] : 0;
+      so[u] = (in && i < K) ? s_out[i] : 0;
+      t[u] = (in && i < K) ? s_topk[i] : 0;
+    }
+    int m[4], v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m[u] = run + rank_below(wd[u]);
+      run += __popcll(wd[u]);
+      v[u] = (((wd[u] >> lane) & 1ull) && m[u] < M) ? victim[m[u]] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = k0 + c0 + u * kWave + lane;
+      if (c0 + u * kWave >= segK || i >= K) continue;
+      int32_t o = so[u];
+      if ((wd[u] >> lane) & 1ull) {
+        if (v[u] >= 0 && v[u] < H) {
+          o = row_of(v[u]);
+          tokens[v[u]] = t[u];
+          ws_src[m[u]] = pool_of(t[u]);
+        } else {
+          o = -1;
+          ws_src[m[u]] = 0;
+        }
+        ws_dst[m[u]] = o;
+      }
+      out[i] = o;
+    }
+  }
+  if (tid == 0) {
+    a.count[b] = m_total;
+    if (a.miss_counts) a.miss_counts[b] = m_total;
+  }
 }
 
 // Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
 // (pool row, hot row) and its length to the workspace for the copy kernel.
+template <bool kSlotRows, bool kPoolRows>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0);
-  const int b = blockIdx.x;
-  int64_t* msrc;
-  int32_t* mdst;
-  const int M = resolve(a, b, lds, lay, msrc, mdst);
-  int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
-  int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
-  for (int m = threadIdx.x; m < M; m += kThreads) {
-    src[m] = msrc[m];
-    dst[m] = mdst[m];
-  }
-  if (threadIdx.x == 0) a.count[b] = M;
+  resolve<kSlotRows, kPoolRows>(a, blockIdx.x, lds, lay);
 }
 
 // Copy the published misses as a flat stream of W-byte chunks: workgroup g
@@ -522,10 +640,14 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   const bool stage = plans_stage[plan];
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
+  const void* resolve_fn =
+      a->slot_rows ? (a->pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true>)
+                                   : reinterpret_cast<const void*>(&resolve_kernel<true, false>))
+                   : (a->pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true>)
+                                   : reinterpret_cast<const void*>(&resolve_kernel<false, false>));
   if (lay.total > 65536) {
     // Opt in to more than 64 KB of dynamic LDS (gfx950 has 160 KB per CU).
-    const hipError_t fe = hipFuncSetAttribute(reinterpret_cast<const void*>(&resolve_kernel),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+    const hipError_t fe = hipFuncSetAttribute(resolve_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                               static_cast<int>(lay.total));
     if (fe != hipSuccess) {
       (void)hipGetLastError();
@@ -582,8 +704,9 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   s.stage_tokens = stage ? 1 : 0;
   s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
 
-  hipLaunchKernelGGL(resolve_kernel, dim3(a->B), dim3(kThreads), lay.total, stream, s);
-  hipError_t e = hipGetLastError();
+  void* params[] = {&s};
+  hipError_t e = hipLaunchKernel(resolve_fn, dim3(a->B), dim3(kThreads), params, lay.total, stream);
+  if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "resolve launch: %s", hipGetErrorString(e));
 
   // Copy grid: enough workgroups per request to cover its worst case (all K
