@@ -44,6 +44,10 @@ def parse():
     p.add_argument("--no-device-pool", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-host-link", action="store_true")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only run a plain device-to-device stream copy of known size "
+                        "(256 MiB read + 256 MiB written per launch, 3 launches) so HBM byte "
+                        "counters can be scaled, then exit")
     return p.parse_args()
 
 
@@ -62,8 +66,16 @@ class Trace:
 
 
 def run_gpu(cfg, warmup, steps, torch, hs, wdev):
-    """Returns event-timed µs over the K timed calls, miss counts per timed step, wall seconds."""
-    from workloads import gen  # noqa: F401
+    """Time K swap-in calls after W warm-up calls.
+
+    Pass 1 (the timed region of the contract): W untimed calls, then K plain
+    hisparse_swap_in calls bracketed by two events and the wall clock.
+    Pass 2: the state is reset and the same trace replayed with resolve-only
+    calls (hisparse_resolve); the state after each call is identical because
+    row copies never touch it, so the K timed resolves give the resolve kernel's
+    time and the difference gives the copy kernel's.
+    Returns dict(us_total, us_resolve, counts, wall).
+    """
     log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})")
     pool = wdev.make_pool(cfg)
     st = wdev.DeviceSwapState(cfg)
@@ -71,30 +83,57 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     counts = torch.empty((warmup + steps, cfg.B), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def call(t):
-        hs.hisparse_swap_in(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t],
-                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
-                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
-                            miss_counts=counts[t], stream=stream)
+    def call(t, fn):
+        fn(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t], slot_tokens=st.slot_tokens,
+           lru=st.lru, pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+           miss_counts=counts[t], stream=stream)
 
-    for t in range(warmup):
-        call(t)
-    torch.cuda.synchronize()
-    log(f"[bench] {cfg.name}: {warmup} warm-up steps done, timing {steps}")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(steps):
-        call(warmup + k)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    us_total = e0.elapsed_time(e1) * 1000.0
-    c = counts.cpu().numpy()[warmup:]
+    def timed(fn):
+        for t in range(warmup):
+            call(t, fn)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(steps):
+            call(warmup + k, fn)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0, time.perf_counter() - w0
+
+    us_total, wall = timed(hs.hisparse_swap_in)
+    log(f"[bench] {cfg.name}: {steps} timed calls after {warmup} warm-up, {us_total / steps:.1f} us/call")
+    c = counts.cpu().numpy()[warmup:].copy()
+    hs.hisparse_state_reset(slot_tokens=st.slot_tokens, lru=st.lru,
+                            rows=torch.arange(st.R, dtype=torch.int64, device="cuda"))
+    us_resolve, _ = timed(hs.hisparse_resolve)
+    c2 = counts.cpu().numpy()[warmup:]
+    assert (c == c2).all(), "resolve-only replay diverged from the timed pass"
     del pool, st, tr
     torch.cuda.empty_cache()
-    return us_total, c, wall
+    return dict(us_total=us_total, us_resolve=us_resolve, counts=c, wall=wall)
+
+
+def kernel_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("swap_in.hip", "hs_common.hpp"):
+        h.update(open(os.path.join(ROOT, "sparse_attention_kv_hisparse_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM/fabric bytes per copy-kernel launch from the committed rocprofv3
+    counter summary, if it was taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", "swap_copy_traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sources_sha256_16") != kernel_sources_hash():
+        return None
+    w = d.get("workloads", {}).get(workload)
+    return None if w is None else w.get("bytes_per_launch")
 
 
 def host_link_ceiling(torch, hs):
@@ -139,6 +178,24 @@ def host_link_ceiling(torch, hs):
     return res
 
 
+def calibrate(torch, hs):
+    """Three launches of the library's row transfer over contiguous 1 MiB rows:
+    exactly 256 MiB read and 256 MiB written per launch, device to device."""
+    n = 256 << 20
+    rb = 1 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    idx = torch.arange(n // rb, dtype=torch.int64, device="cuda")
+    sp = torch.tensor([src.data_ptr()], dtype=torch.int64, device="cuda")
+    dp = torch.tensor([dst.data_ptr()], dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=idx, dst_idx=idx,
+                                   row_bytes=rb, src_nrows=n // rb, dst_nrows=n // rb)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "transfer_kernel<16>", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 3}), flush=True)
+
+
 def cpu_baseline(cfg, warmup, steps):
     """The oracle, single-threaded, on the headline trace: steps before the timed
     window are replayed untimed to reach the same state, then the timed steps."""
@@ -173,27 +230,32 @@ def main():
     from workloads import gen
     hs.load()
     torch.cuda.set_device(0)
+    if args.calibrate:
+        calibrate(torch, hs)
+        return
     cfg = gen.DSV32
 
     link = None if args.no_host_link else host_link_ceiling(torch, hs)
     if link:
         log(f"[bench] host link: {json.dumps({k: round(v, 2) for k, v in link.items()})}")
 
-    us_total, counts, wall = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev)
-    rows = int(counts.sum())
+    r = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev)
+    K = args.steps
+    rows = int(r["counts"].sum())
     bytes_link = rows * cfg.row_bytes
-    total_s = us_total * 1e-6
-    value = rows / wall
-    achieved = bytes_link / total_s / 1e9
+    us_copy = max(r["us_total"] - r["us_resolve"], 1e-9)
+    value = rows / r["wall"]
+    achieved = bytes_link / (us_copy * 1e-6) / 1e9          # copy kernel alone
+    call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
     peak = link["h2d_ceiling_gbs"] if link else None
     out = {
         "metric": "swapped-in rows/s + effective GB/s (% of HBM/host-link peak); µs per decode-step call",
         "value": round(value, 1),
         "unit": "rows/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(r["wall"] / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -203,33 +265,45 @@ def main():
                    "context": cfg.ctx, "hot_size": cfg.H, "top_k": cfg.K,
                    "row_bytes": cfg.row_bytes, "pool": "pinned_host", "retention": cfg.rho,
                    "new_ids": "zipf1.1_recency"},
-        "us_per_call": round(us_total / args.steps, 2),
-        "rows_per_call": round(rows / args.steps, 1),
-        "effective_GBps": round(achieved, 2),
-        "roofline": {"bound": "host_link", "kernel": "hisparse_swap_in call (resolve_kernel + swap_copy_kernel)",
+        "us_per_call": round(r["us_total"] / K, 2),
+        "us_resolve_kernel": round(r["us_resolve"] / K, 2),
+        "us_copy_kernel": round(us_copy / K, 2),
+        "rows_per_call": round(rows / K, 1),
+        "effective_GBps_call": round(call_gbs, 2),
+        "frac_host_link_call": round(call_gbs / peak, 4) if peak else None,
+        "roofline": {"bound": "host_link", "kernel": "swap_copy_kernel<16>",
                      "achieved": round(achieved, 2), "peak": round(peak, 2) if peak else None,
                      "unit": "GB/s", "frac": round(achieved / peak, 4) if peak else None,
-                     "peak_published": PCIE5_X16_GBS, "traffic": None},
+                     "peak_published": PCIE5_X16_GBS,
+                     "traffic": measured_traffic("dsv32_decode")},
         "host_link": {k: round(v, 2) for k, v in link.items()} if link else None,
     }
 
     if not args.no_device_pool:
         dcfg = gen.DEVPOOL
-        dus_total, dcounts, dwall = run_gpu(dcfg, 1, args.device_pool_steps, torch, hs, wdev)
-        drows = int(dcounts.sum())
-        # algorithmic HBM bytes: each row read once and written once, plus the
-        # per-request metadata (top-k ids, LRU read+write, slot tokens gathered,
-        # outputs written, new owners written)
-        meta = dcfg.B * (4 * dcfg.K * 2 + 2 * dcfg.H * 2 + 4 * dcfg.H) + 4 * drows / args.device_pool_steps
-        dbytes = 2 * drows * dcfg.row_bytes + meta * args.device_pool_steps
-        dach = dbytes / (dus_total * 1e-6) / 1e9
+        n = args.device_pool_steps
+        d = run_gpu(dcfg, 1, n, torch, hs, wdev)
+        drows = int(d["counts"].sum())
+        d_copy = max(d["us_total"] - d["us_resolve"], 1e-9)
+        # algorithmic HBM bytes of the copy kernel: each missed row read once and
+        # written once, plus its (pool row, hot row) list entry (12 B)
+        dbytes = drows * (2 * dcfg.row_bytes + 12)
+        dach = dbytes / (d_copy * 1e-6) / 1e9
+        # whole call: rows plus the resolve's own traffic (ids, LRU read and
+        # write, slot tokens read, outputs, list) per request
+        meta = dcfg.B * (4 * dcfg.K + 2 * dcfg.H * 2 + 4 * dcfg.H + 4 * dcfg.K) * n
+        dcall = (drows * 2 * dcfg.row_bytes + meta) / (d["us_total"] * 1e-6) / 1e9
         out["device_pool"] = {
             "workload": "device_pool_swap_in_hbm", "batch": dcfg.B, "context": dcfg.ctx,
-            "hot_size": dcfg.H, "top_k": dcfg.K, "row_bytes": dcfg.row_bytes, "steps": args.device_pool_steps,
-            "rows_per_s": round(drows / dwall, 1), "rows_per_call": round(drows / args.device_pool_steps, 1),
-            "us_per_call": round(dus_total / args.device_pool_steps, 2),
-            "roofline": {"bound": "hbm", "achieved": round(dach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(dach / HBM_PEAK_GBS, 4), "traffic": None},
+            "hot_size": dcfg.H, "top_k": dcfg.K, "row_bytes": dcfg.row_bytes, "steps": n,
+            "rows_per_s": round(drows / d["wall"], 1), "rows_per_call": round(drows / n, 1),
+            "us_per_call": round(d["us_total"] / n, 2),
+            "us_resolve_kernel": round(d["us_resolve"] / n, 2),
+            "us_copy_kernel": round(d_copy / n, 2),
+            "effective_GBps_call": round(dcall, 1), "frac_hbm_call": round(dcall / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16>", "achieved": round(dach, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("device_pool")},
         }
 
     if not args.no_cpu_baseline:

@@ -143,6 +143,41 @@ int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t worksp
                      hipStream_t stream);
 
 /*
+ * hisparse_resolve / hisparse_gather_compact -- the two halves of
+ * hisparse_swap_in, for callers that want to run the row copy later, on
+ * another stream, or once per layer group.
+ * vLLM hisparse_kernels.cu, hisparse_resolve_residency_kernel (resolution
+ * half, compact swap lists) and hisparse_gather_compact_kernel (copy half).
+ *
+ * hisparse_resolve performs steps 1-5 of hisparse_swap_in except the byte
+ * copy: outputs, state and miss counts are final, and the workspace holds
+ * each row's miss list (see hs_swap_in_workspace_layout).
+ * hisparse_gather_compact copies the rows that list names, from pool to hot.
+ * Both take the same argument struct; gather reads only B, K, pool,
+ * pool_nrows, hot, hot_nrows and row_bytes from it, plus the workspace, which
+ * must hold the list of a resolve call with the same B and K enqueued before
+ * it (on the same stream, or ordered by an event). Resolve then gather is
+ * exactly hisparse_swap_in. Errors as for hisparse_swap_in.
+ */
+int hisparse_resolve(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+int hisparse_gather_compact(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Workspace layout of the miss list, for callers that read it (vLLM
+ * hisparse_kernels.cu: swap_counts, swap_host_physical_rows,
+ * swap_device_physical_rows). Byte offsets from the workspace start:
+ *   count: int32 [B]      misses of batch row b
+ *   src:   int64 [B, K]   pool row of miss m of row b (m < count[b]), miss order
+ *   dst:   int32 [B, K]   hot row of that miss, or -1 when it was not copied
+ * Returns the total size (== hs_swap_in_workspace_bytes), 0 for B or K <= 0.
+ * Any offset pointer may be NULL.
+ */
+size_t hs_swap_in_workspace_layout(int32_t B, int32_t K, size_t* count_offset, size_t* src_offset,
+                                   size_t* dst_offset);
+
+/*
  * transfer_rows_all_layer -- fused multi-layer indexed row copy.
  * tokenspeed kvcache/triton.py, _kv_transfer_all_layer_mla_kernel; SGLang
  * hisparse.cuh, transfer_cache_dsv4_mla_kernel (generic row layout).

@@ -15,7 +15,8 @@ import torch
 
 from ._lib import EXPORTS, HisparseError, SwapInArgs, check, load
 
-__all__ = ["hisparse_swap_in", "transfer_rows_all_layer", "store_kv_scatter",
+__all__ = ["hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
+           "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
            "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
 
 
@@ -40,13 +41,22 @@ def swap_in_workspace_bytes(B: int, K: int) -> int:
     return int(load().hs_swap_in_workspace_bytes(B, K))
 
 
+def swap_in_workspace_layout(B: int, K: int) -> dict:
+    """Byte offsets of the miss list in the workspace: count int32[B], src int64[B,K],
+    dst int32[B,K] (``hs_swap_in_workspace_layout``)."""
+    c, s_, d = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    total = load().hs_swap_in_workspace_layout(B, K, ctypes.byref(c), ctypes.byref(s_), ctypes.byref(d))
+    return {"count": c.value, "src": s_.value, "dst": d.value, "total": int(total)}
+
+
 def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: torch.Tensor,
                      slot_tokens: torch.Tensor, lru: torch.Tensor, pool: torch.Tensor,
                      hot: torch.Tensor, out_rows: torch.Tensor, ctx_stride: int,
                      workspace: torch.Tensor, miss_counts: Optional[torch.Tensor] = None,
                      num_real: Optional[torch.Tensor] = None,
                      slot_rows: Optional[torch.Tensor] = None,
-                     pool_rows: Optional[torch.Tensor] = None, stream=None) -> None:
+                     pool_rows: Optional[torch.Tensor] = None, stream=None,
+                     _entry: str = "hisparse_swap_in") -> None:
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
@@ -83,8 +93,19 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         out_rows=_dev(out_rows, torch.int32, "out_rows"),
         miss_counts=_opt(miss_counts, torch.int32, "miss_counts"))
     ws = _dev(workspace, torch.uint8, "workspace")
-    check("hisparse_swap_in", load().hisparse_swap_in(ctypes.byref(a), ws, workspace.numel(),
-                                                      _stream(stream)))
+    check(_entry, getattr(load(), _entry)(ctypes.byref(a), ws, workspace.numel(), _stream(stream)))
+
+
+def hisparse_resolve(**kw) -> None:
+    """Resolution half of the swap-in (``hisparse_resolve``): same arguments as
+    ``hisparse_swap_in``; leaves the miss list in the workspace, copies nothing."""
+    hisparse_swap_in(_entry="hisparse_resolve", **kw)
+
+
+def hisparse_gather_compact(**kw) -> None:
+    """Copy half (``hisparse_gather_compact``): copies the rows a preceding
+    ``hisparse_resolve`` with the same workspace listed."""
+    hisparse_swap_in(_entry="hisparse_gather_compact", **kw)
 
 
 def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: torch.Tensor,

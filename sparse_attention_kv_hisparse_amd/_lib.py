@@ -17,7 +17,8 @@ STATUS = {0: "HS_OK", -1: "HS_EINVAL", -2: "HS_ERANGE", -3: "HS_EMEMKIND", -4: "
           -5: "HS_EWORKSPACE"}
 
 # Every function include/hisparse.h declares.
-EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "transfer_rows_all_layer",
+EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_resolve",
+           "hisparse_gather_compact", "hs_swap_in_workspace_layout", "transfer_rows_all_layer",
            "store_kv_scatter", "hisparse_state_reset", "hisparse_last_error")
 
 
@@ -60,8 +61,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.hs_swap_in_workspace_bytes.argtypes = [i32, i32]
     lib.hs_swap_in_workspace_bytes.restype = sz
-    lib.hisparse_swap_in.argtypes = [ctypes.POINTER(SwapInArgs), vp, sz, vp]
-    lib.hisparse_swap_in.restype = ctypes.c_int
+    for name in ("hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(SwapInArgs), vp, sz, vp]
+        getattr(lib, name).restype = ctypes.c_int
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    lib.hs_swap_in_workspace_layout.argtypes = [i32, i32, szp, szp, szp]
+    lib.hs_swap_in_workspace_layout.restype = sz
     lib.transfer_rows_all_layer.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
     lib.transfer_rows_all_layer.restype = ctypes.c_int
     lib.store_kv_scatter.argtypes = [vp, i64, vp, i64, i64, vp, i64, i64, vp]

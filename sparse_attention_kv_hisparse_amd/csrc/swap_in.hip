@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 
 #include "hs_common.hpp"
 
@@ -576,16 +577,45 @@ inline uint32_t pow2_at_least(uint32_t x) {
 
 using namespace hs;
 
-extern "C" size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K) {
-  if (B <= 0 || K <= 0) return 0;
-  return ws_layout(B, K).total;
+namespace {
+
+constexpr int kEmptyCall = 1;  // internal: nothing to launch
+
+// Opt a resolve kernel in to more than 64 KB of dynamic LDS (gfx950 has
+// 160 KB per CU), once per device, kernel and size.
+int allow_lds(int device, const void* fn, uint32_t bytes) {
+  static std::mutex mu;
+  struct Entry { int device; const void* fn; uint32_t bytes; };
+  static Entry done[64];
+  static int n = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (done[i].device == device && done[i].fn == fn && done[i].bytes >= bytes) return HS_OK;
+  const hipError_t fe = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            static_cast<int>(bytes));
+  if (fe != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(HS_ERANGE, "cannot raise dynamic LDS to %u bytes: %s", bytes,
+                     hipGetErrorString(fe));
+  }
+  if (n < 64) done[n++] = Entry{device, fn, bytes};
+  return HS_OK;
 }
 
-extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+// Everything a launch needs, validated once per call.
+struct Plan {
+  SwapArgs s;
+  const void* resolve_fn;
+  LdsLayout lay;
+  int W;
+  int64_t C;
+  int num_cus;
+};
+
+int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, Plan* pl) {
   if (!a) return set_error(HS_EINVAL, "args is NULL");
   if (a->B < 0 || a->K < 0) return set_error(HS_EINVAL, "B and K must be >= 0");
-  if (a->B == 0 || a->K == 0) return HS_OK;
+  if (a->B == 0 || a->K == 0) return kEmptyCall;
   if (!a->topk_ids || !a->req_rows || !a->seq_lens || !a->slot_tokens || !a->lru || !a->pool ||
       !a->hot || !a->out_rows)
     return set_error(HS_EINVAL, "a required pointer is NULL");
@@ -646,14 +676,8 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
                    : (a->pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true>)
                                    : reinterpret_cast<const void*>(&resolve_kernel<false, false>));
   if (lay.total > 65536) {
-    // Opt in to more than 64 KB of dynamic LDS (gfx950 has 160 KB per CU).
-    const hipError_t fe = hipFuncSetAttribute(resolve_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                              static_cast<int>(lay.total));
-    if (fe != hipSuccess) {
-      (void)hipGetLastError();
-      return set_error(HS_ERANGE, "cannot raise dynamic LDS to %u bytes: %s", lay.total,
-                       hipGetErrorString(fe));
-    }
+    rc = allow_lds(di.device, resolve_fn, lay.total);
+    if (rc != HS_OK) return rc;
   }
 
   // Pool: device memory, or pinned host memory read directly by the kernels
@@ -673,7 +697,7 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   }
 
   char* ws = static_cast<char*>(workspace);
-  SwapArgs s;
+  SwapArgs& s = pl->s;
   s.topk = a->topk_ids;
   s.topk_stride = a->topk_stride;
   s.req_rows = a->req_rows;
@@ -704,26 +728,81 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   s.stage_tokens = stage ? 1 : 0;
   s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
 
-  void* params[] = {&s};
-  hipError_t e = hipLaunchKernel(resolve_fn, dim3(a->B), dim3(kThreads), params, lay.total, stream);
+  pl->resolve_fn = resolve_fn;
+  pl->lay = lay;
+  pl->W = W;
+  pl->C = C;
+  pl->num_cus = di.num_cus;
+  return HS_OK;
+}
+
+int launch_resolve(Plan& pl, hipStream_t stream) {
+  void* params[] = {&pl.s};
+  hipError_t e = hipLaunchKernel(pl.resolve_fn, dim3(pl.s.B), dim3(kThreads), params, pl.lay.total, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "resolve launch: %s", hipGetErrorString(e));
+  return HS_OK;
+}
 
+int launch_copy(Plan& pl, hipStream_t stream) {
   // Copy grid: enough workgroups per request to cover its worst case (all K
   // ids missing) at kCopyUnroll chunks per lane, capped at 8 per CU overall.
-  const int64_t max_items = static_cast<int64_t>(a->K) * C;
+  const int64_t max_items = static_cast<int64_t>(pl.s.K) * pl.C;
   int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
-  const int64_t cap = (8LL * di.num_cus + a->B - 1) / a->B;
+  const int64_t cap = (8LL * pl.num_cus + pl.s.B - 1) / pl.s.B;
   if (parts > cap) parts = cap;
   if (parts < 1) parts = 1;
-  const dim3 grid(static_cast<unsigned>(a->B * parts));
-  if (W == 16)
-    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, s,
+  const dim3 grid(static_cast<unsigned>(pl.s.B * parts));
+  if (pl.W == 16)
+    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, pl.s,
                        static_cast<int32_t>(parts));
   else
-    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, s,
+    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, pl.s,
                        static_cast<int32_t>(parts));
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "copy launch: %s", hipGetErrorString(e));
   return HS_OK;
+}
+
+}  // namespace
+
+extern "C" size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K) {
+  if (B <= 0 || K <= 0) return 0;
+  return ws_layout(B, K).total;
+}
+
+extern "C" size_t hs_swap_in_workspace_layout(int32_t B, int32_t K, size_t* count_offset,
+                                              size_t* src_offset, size_t* dst_offset) {
+  if (B <= 0 || K <= 0) return 0;
+  const WsLayout w = ws_layout(B, K);
+  if (count_offset) *count_offset = w.count;
+  if (src_offset) *src_offset = w.src;
+  if (dst_offset) *dst_offset = w.dst;
+  return w.total;
+}
+
+extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  Plan pl;
+  const int rc = prepare(a, workspace, workspace_bytes, &pl);
+  if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
+  const int r1 = launch_resolve(pl, stream);
+  if (r1 != HS_OK) return r1;
+  return launch_copy(pl, stream);
+}
+
+extern "C" int hisparse_resolve(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  Plan pl;
+  const int rc = prepare(a, workspace, workspace_bytes, &pl);
+  if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
+  return launch_resolve(pl, stream);
+}
+
+extern "C" int hisparse_gather_compact(const hs_swap_in_args* a, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  Plan pl;
+  const int rc = prepare(a, workspace, workspace_bytes, &pl);
+  if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
+  return launch_copy(pl, stream);
 }

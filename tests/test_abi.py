@@ -91,6 +91,26 @@ def test_workspace_size(lib):
     assert size >= b * 4 + b * k * 12 and size % 256 == 0
 
 
+def test_workspace_layout(lib):
+    c, s, d = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    b, k = 7, 300
+    total = lib.hs_swap_in_workspace_layout(b, k, ctypes.byref(c), ctypes.byref(s), ctypes.byref(d))
+    assert total == lib.hs_swap_in_workspace_bytes(b, k)
+    # three disjoint, 256-byte aligned regions, in order, inside the total
+    assert c.value == 0 and s.value >= 4 * b and d.value >= s.value + 8 * b * k
+    assert d.value + 4 * b * k <= total
+    assert s.value % 256 == 0 and d.value % 256 == 0
+    assert lib.hs_swap_in_workspace_layout(0, 3, None, None, None) == 0
+
+
+@pytest.mark.parametrize("name", ["hisparse_resolve", "hisparse_gather_compact"])
+def test_split_calls_validate_like_swap_in(lib, name):
+    fn = getattr(lib, name)
+    assert fn(ctypes.byref(_args(H=3)), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+    assert fn(ctypes.byref(_args(B=0)), None, 0, None) == 0
+    assert fn(None, None, 0, None) == -1
+
+
 def test_transfer_rejects(lib):
     f = 0x100000
     assert lib.transfer_rows_all_layer(f, f, f, f, -1, 3, 16, 10, 10, None) == -1
