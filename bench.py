@@ -8,9 +8,15 @@ W warm-up steps (the first is the cold step) run untimed, then K steps are
 timed; inputs for every step are resident in HBM before timing starts.
 
 Also reported in the same JSON line:
+  * cold_step: the first (all-miss) call of the headline trace, timed alone;
   * device_pool: the same call on the device-pool workload (B=128, 16,384-token
     contexts, pool of 2,097,152 rows in HBM, 60% retention) against 8 TB/s;
-  * host_link: the measured host-link ceiling the host-pool roofline uses;
+  * adversarial: B=64, hot_size 8192, 65,536-token contexts, ids that collide
+    in the low-bit multiplicative hash, 1152-byte and 132-byte rows: the cold
+    step and the steps after it;
+  * all_layer: the fused all-layer transfer (61 layers x 262,144 rows x 656 B,
+    8192 pairs) in both directions against the host-link ceiling;
+  * host_link: the measured host-link ceiling the host-pool rooflines use;
   * cpu_baseline: the CPU oracle (single thread) on the headline steps.
 """
 
@@ -44,6 +50,14 @@ def parse():
     p.add_argument("--no-device-pool", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-host-link", action="store_true")
+    p.add_argument("--no-all-layer", action="store_true")
+    p.add_argument("--no-adversarial", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU seconds of oracle work for cpu_baseline (whole replays "
+                        "of the headline's timed steps)")
+    p.add_argument("--copy-ceilings", action="store_true",
+                   help="only measure the library's row transfer on scattered rows of several "
+                        "sizes (pinned host -> HBM and HBM -> HBM), one JSON line each, then exit")
     p.add_argument("--calibrate", action="store_true",
                    help="only run a plain device-to-device stream copy of known size "
                         "(256 MiB read + 256 MiB written per launch, 3 launches) so HBM byte "
@@ -70,11 +84,14 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
 
     Pass 1 (the timed region of the contract): W untimed calls, then K plain
     hisparse_swap_in calls bracketed by two events and the wall clock.
-    Pass 2: the state is reset and the same trace replayed with resolve-only
-    calls (hisparse_resolve); the state after each call is identical because
-    row copies never touch it, so the K timed resolves give the resolve kernel's
-    time and the difference gives the copy kernel's.
-    Returns dict(us_total, us_resolve, counts, wall).
+    Pass 2 (per-kernel times): the state is reset and the same trace replayed;
+    the K timed steps run as K hisparse_resolve calls, each into its own
+    workspace, back to back, then the K hisparse_gather_compact calls back to
+    back -- the same work in the same order for the hot buffer, with each
+    kernel's total bracketed by two events and no gaps between launches.
+    The first warm-up call is the cold step (every id a miss) and is timed on
+    its own with two events.
+    Returns dict(us_total, us_resolve, us_copy, us_cold, cold_rows, counts, wall).
     """
     log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})")
     pool = wdev.make_pool(cfg)
@@ -83,41 +100,79 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     counts = torch.empty((warmup + steps, cfg.B), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def call(t, fn):
+    def call(t, fn, ws):
         fn(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t], slot_tokens=st.slot_tokens,
-           lru=st.lru, pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+           lru=st.lru, pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx, workspace=ws,
            miss_counts=counts[t], stream=stream)
 
-    def timed(fn):
-        for t in range(warmup):
-            call(t, fn)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        e0.record(stream)
-        for k in range(steps):
-            call(warmup + k, fn)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1000.0, time.perf_counter() - w0
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    us_total, wall = timed(hs.hisparse_swap_in)
+    # One call with every row padding (num_real = 0) takes the library's
+    # one-time costs (LDS opt-in, first launches) and changes no state. Before
+    # the cold step the GPU is kept busy by a short spin kernel, so the
+    # host-side time of the call is hidden and the two events bracket the
+    # call's kernels only.
+    pad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hs.hisparse_swap_in(topk=tr.topk[0], req_rows=tr.rows, seq_lens=tr.seq[0],
+                        slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                        out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws, num_real=pad,
+                        stream=stream)
+    torch.cuda.synchronize()
+    c0, c1 = events()
+    for t in range(warmup):
+        if t == 0:
+            torch.cuda._sleep(2_000_000)
+            c0.record(stream)
+        call(t, hs.hisparse_swap_in, st.ws)
+        if t == 0:
+            c1.record(stream)
+    torch.cuda.synchronize()
+    us_cold = c0.elapsed_time(c1) * 1000.0 if warmup else None
+    cold_rows = int(counts[0].sum().item()) if warmup else 0
+    e0, e1 = events()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(steps):
+        call(warmup + k, hs.hisparse_swap_in, st.ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    us_total = e0.elapsed_time(e1) * 1000.0
     log(f"[bench] {cfg.name}: {steps} timed calls after {warmup} warm-up, {us_total / steps:.1f} us/call")
     c = counts.cpu().numpy()[warmup:].copy()
+
+    # pass 2
     hs.hisparse_state_reset(slot_tokens=st.slot_tokens, lru=st.lru,
                             rows=torch.arange(st.R, dtype=torch.int64, device="cuda"))
-    us_resolve, _ = timed(hs.hisparse_resolve)
-    c2 = counts.cpu().numpy()[warmup:]
-    assert (c == c2).all(), "resolve-only replay diverged from the timed pass"
-    del pool, st, tr
+    for t in range(warmup):
+        call(t, hs.hisparse_swap_in, st.ws)
+    wss = [torch.zeros_like(st.ws) for _ in range(steps)]
+    torch.cuda.synchronize()
+    r0, r1 = events()
+    g0, g1 = events()
+    r0.record(stream)
+    for k in range(steps):
+        call(warmup + k, hs.hisparse_resolve, wss[k])
+    r1.record(stream)
+    g0.record(stream)
+    for k in range(steps):
+        call(warmup + k, hs.hisparse_gather_compact, wss[k])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    us_resolve = r0.elapsed_time(r1) * 1000.0
+    us_copy = g0.elapsed_time(g1) * 1000.0
+    assert (counts.cpu().numpy()[warmup:] == c).all(), "replay diverged from the timed pass"
+    del pool, st, tr, wss
     torch.cuda.empty_cache()
-    return dict(us_total=us_total, us_resolve=us_resolve, counts=c, wall=wall)
+    return dict(us_total=us_total, us_resolve=us_resolve, us_copy=us_copy, us_cold=us_cold,
+                cold_rows=cold_rows, counts=c, wall=wall)
 
 
 def kernel_sources_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("swap_in.hip", "hs_common.hpp"):
+    for f in ("swap_copy.hpp", "hs_common.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_attention_kv_hisparse_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -196,26 +251,136 @@ def calibrate(torch, hs):
                       "bytes_written_per_launch": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(cfg, warmup, steps):
-    """The oracle, single-threaded, on the headline trace: steps before the timed
-    window are replayed untimed to reach the same state, then the timed steps."""
+def copy_ceilings(torch, hs):
+    """What the copy engine reaches on scattered rows, by row size and bytes per
+    launch: transfer_rows_all_layer with one layer, rows drawn without
+    replacement from a 688 MB pool (pinned host, or HBM), written to a random
+    permutation of a hot buffer in HBM. Fresh rows every repetition and a
+    512 MiB write between repetitions, so no row is served from L2 or MALL.
+    Prints one JSON line per case with the median and best of 7 launches."""
+    s = torch.cuda.current_stream()
+    pool_bytes = 688 << 20
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    cases = []
+    for kind in ("host", "device"):
+        for rb in (132, 512, 640, 656, 1024, 1152, 2048, 4096):
+            for total in (4 << 20, 64 << 20):
+                cases.append((kind, rb, total))
+    for kind, rb in (("device", 656),):
+        cases.append((kind, rb, 85848 * 656))   # one device-pool swap-in launch
+    pools = {}
+    for kind, rb, total in cases:
+        key = (kind, rb)
+        if key not in pools:
+            pools.clear()
+            torch.cuda.empty_cache()
+            nrows = pool_bytes // rb
+            if kind == "host":
+                pools[key] = torch.empty((nrows, rb), dtype=torch.uint8, pin_memory=True)
+                pools[key].numpy()[:] = 3
+            else:
+                pools[key] = torch.full((nrows, rb), 3, dtype=torch.uint8, device="cuda")
+        pool = pools[key]
+        n = max(1, total // rb)
+        hot = torch.zeros((max(n, 4096), rb), dtype=torch.uint8, device="cuda")
+        sp = torch.tensor([pool.data_ptr()], dtype=torch.int64, device="cuda")
+        dp = torch.tensor([hot.data_ptr()], dtype=torch.int64, device="cuda")
+        us = []
+        for rep in range(8):
+            src = torch.randperm(pool.shape[0], generator=g)[:n].cuda()
+            dst = torch.randperm(hot.shape[0], generator=g)[:n].cuda()
+            flush.fill_(rep)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=src, dst_idx=dst,
+                                       row_bytes=rb, src_nrows=pool.shape[0], dst_nrows=hot.shape[0])
+            e1.record(s)
+            torch.cuda.synchronize()
+            if rep:
+                us.append(e0.elapsed_time(e1) * 1000.0)
+        us.sort()
+        moved = n * rb * (1 if kind == "host" else 2)   # host: link bytes; device: HBM read + write
+        print(json.dumps({"copy_ceiling": f"{kind}_to_hbm", "row_bytes": rb, "rows": n,
+                          "bytes_per_launch": moved, "us_median": round(us[len(us) // 2], 2),
+                          "GBps_median": round(moved / us[len(us) // 2] / 1e3, 1),
+                          "GBps_best": round(moved / us[0] / 1e3, 1)}), flush=True)
+        del hot
+    pools.clear()
+    del flush
+    torch.cuda.empty_cache()
+
+
+def run_all_layer(torch, hs, reps=5):
+    """The fused all-layer transfer at full size: 61 layers x 262,144 rows x
+    656 B, 8192 index pairs, one call per repetition, per direction (offload =
+    HBM -> pinned host, load = pinned host -> HBM). A 512 MiB write between
+    repetitions evicts L2 and MALL. Returns per-direction µs (median, best)."""
+    from workloads import gen
+    cfg = gen.ALL_LAYER
+    L, rows, rb = cfg.layers, cfg.rows_per_layer, cfg.row_bytes
+    log(f"[bench] all_layer: allocating 2 x {L * rows * rb / 1e9:.2f} GB")
+    dev = torch.empty((L * rows, rb), dtype=torch.uint8, device="cuda")
+    dev.fill_(5)
+    host = torch.empty((L * rows, rb), dtype=torch.uint8, pin_memory=True)
+    dptr = torch.tensor([dev[l * rows:].data_ptr() for l in range(L)], dtype=torch.int64, device="cuda")
+    hptr = torch.tensor([host[l * rows:].data_ptr() for l in range(L)], dtype=torch.int64, device="cuda")
+    si, di = gen.transfer_indices(cfg)
+    si, di = torch.as_tensor(si).cuda(), torch.as_tensor(di).cuda()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    res = {}
+    for name, sp, dp in (("offload", dptr, hptr), ("load", hptr, dptr)):
+        us = []
+        for rep in range(reps + 1):
+            flush.fill_(rep)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=si, dst_idx=di,
+                                       row_bytes=rb, src_nrows=rows, dst_nrows=rows)
+            e1.record(s)
+            torch.cuda.synchronize()
+            if rep:
+                us.append(e0.elapsed_time(e1) * 1000.0)
+        us.sort()
+        res[name] = (us[len(us) // 2], us[0])
+        log(f"[bench] all_layer {name}: median {us[len(us) // 2]:.1f} us")
+    del dev, host, flush
+    torch.cuda.empty_cache()
+    return cfg, L * cfg.n_pairs * rb, res
+
+
+def cpu_baseline(cfg, warmup, steps, min_seconds):
+    """The oracle, single-threaded, on the headline trace: the warm-up steps run
+    untimed to reach the timed window's starting state, then the timed steps
+    run from that state, as whole passes, until at least `min_seconds` of
+    oracle time has accumulated (each pass restores the slot tables; replaying
+    a step from the same state repeats exactly the same work)."""
     import oracle
     from workloads import gen
     pool = gen.fill_pool(cfg.seed, np.empty((cfg.pool_nrows, cfg.row_bytes), np.uint8))
     tok, lru = gen.initial_state(cfg)
     hot = np.zeros((cfg.R * cfg.S_r, cfg.row_bytes), np.uint8)
     rows = np.arange(cfg.B, dtype=np.int64)
-    secs, rows_copied = 0.0, 0
-    for t, topk in enumerate(gen.topk_trace(cfg, warmup + steps)):
-        seq = gen.seq_lens(cfg, t)
-        t0 = time.perf_counter()
-        _, cnt = oracle.swap_in(topk=topk, req_rows=rows, seq_lens=seq, slot_tokens=tok, lru=lru,
-                                pool=pool, hot=hot, ctx_stride=cfg.ctx)
-        dt = time.perf_counter() - t0
-        if t >= warmup:
-            secs += dt
+    trace = list(gen.topk_trace(cfg, warmup + steps))
+    for t in range(warmup):
+        oracle.swap_in(topk=trace[t], req_rows=rows, seq_lens=gen.seq_lens(cfg, t), slot_tokens=tok,
+                       lru=lru, pool=pool, hot=hot, ctx_stride=cfg.ctx)
+    tok0, lru0 = tok.copy(), lru.copy()
+    seqs = [gen.seq_lens(cfg, t) for t in range(warmup + steps)]
+    secs, rows_copied, passes = 0.0, 0, 0
+    while passes == 0 or secs < min_seconds:
+        tok[...] = tok0
+        lru[...] = lru0
+        for t in range(warmup, warmup + steps):
+            t0 = time.perf_counter()
+            _, cnt = oracle.swap_in(topk=trace[t], req_rows=rows, seq_lens=seqs[t], slot_tokens=tok,
+                                    lru=lru, pool=pool, hot=hot, ctx_stride=cfg.ctx)
+            secs += time.perf_counter() - t0
             rows_copied += int(cnt.sum())
-    return rows_copied, secs
+        passes += 1
+    return rows_copied, secs, passes
 
 
 def main():
@@ -233,6 +398,9 @@ def main():
     if args.calibrate:
         calibrate(torch, hs)
         return
+    if args.copy_ceilings:
+        copy_ceilings(torch, hs)
+        return
     cfg = gen.DSV32
 
     link = None if args.no_host_link else host_link_ceiling(torch, hs)
@@ -243,7 +411,7 @@ def main():
     K = args.steps
     rows = int(r["counts"].sum())
     bytes_link = rows * cfg.row_bytes
-    us_copy = max(r["us_total"] - r["us_resolve"], 1e-9)
+    us_copy = r["us_copy"]
     value = rows / r["wall"]
     achieved = bytes_link / (us_copy * 1e-6) / 1e9          # copy kernel alone
     call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
@@ -269,6 +437,8 @@ def main():
         "us_resolve_kernel": round(r["us_resolve"] / K, 2),
         "us_copy_kernel": round(us_copy / K, 2),
         "rows_per_call": round(rows / K, 1),
+        "cold_step": {"us": round(r["us_cold"], 2), "rows": r["cold_rows"],
+                      "GBps": round(r["cold_rows"] * cfg.row_bytes / r["us_cold"] / 1e3, 2)},
         "effective_GBps_call": round(call_gbs, 2),
         "frac_host_link_call": round(call_gbs / peak, 4) if peak else None,
         "roofline": {"bound": "host_link", "kernel": "swap_copy_kernel<16>",
@@ -284,7 +454,7 @@ def main():
         n = args.device_pool_steps
         d = run_gpu(dcfg, 1, n, torch, hs, wdev)
         drows = int(d["counts"].sum())
-        d_copy = max(d["us_total"] - d["us_resolve"], 1e-9)
+        d_copy = d["us_copy"]
         # algorithmic HBM bytes of the copy kernel: each missed row read once and
         # written once, plus its (pool row, hot row) list entry (12 B)
         dbytes = drows * (2 * dcfg.row_bytes + 12)
@@ -300,20 +470,61 @@ def main():
             "us_per_call": round(d["us_total"] / n, 2),
             "us_resolve_kernel": round(d["us_resolve"] / n, 2),
             "us_copy_kernel": round(d_copy / n, 2),
+            "cold_step": {"us": round(d["us_cold"], 2), "rows": d["cold_rows"],
+                          "GBps_rows_read_written": round(
+                              d["cold_rows"] * 2 * dcfg.row_bytes / d["us_cold"] / 1e3, 1)},
             "effective_GBps_call": round(dcall, 1), "frac_hbm_call": round(dcall / HBM_PEAK_GBS, 4),
             "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16>", "achieved": round(dach, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("device_pool")},
         }
 
+    if not args.no_adversarial:
+        # cold step (all misses, ids that collide in the pages' low-bit hash),
+        # then the remaining steps of the 4-step trace
+        adv = {}
+        for acfg in (gen.ADVERSARIAL, gen.ADVERSARIAL_132):
+            a = run_gpu(acfg, 1, acfg.steps - 1, torch, hs, wdev)
+            n = acfg.steps - 1
+            arows = int(a["counts"].sum())
+            cold_gbs = a["cold_rows"] * acfg.row_bytes / a["us_cold"] / 1e3
+            adv[acfg.name] = {
+                "batch": acfg.B, "hot_size": acfg.H, "top_k": acfg.K, "context": acfg.ctx,
+                "row_bytes": acfg.row_bytes,
+                "cold_step": {"us": round(a["us_cold"], 2), "rows": a["cold_rows"],
+                              "GBps": round(cold_gbs, 2),
+                              "frac_host_link": round(cold_gbs / peak, 4) if peak else None},
+                "steps_after_cold": n, "us_per_call": round(a["us_total"] / n, 2),
+                "us_resolve_kernel": round(a["us_resolve"] / n, 2),
+                "us_copy_kernel": round(a["us_copy"] / n, 2),
+                "rows_per_call": round(arows / n, 1),
+                "GBps_call": round(arows * acfg.row_bytes / a["us_total"] / 1e3, 2),
+            }
+        out["adversarial"] = adv
+
+    if not args.no_all_layer:
+        tcfg, tbytes, tres = run_all_layer(torch, hs)
+        ceil = {"offload": link["d2h_ceiling_gbs"] if link else None,
+                "load": link["h2d_ceiling_gbs"] if link else None}
+        out["all_layer"] = {
+            "workload": "all_layer_transfer", "layers": tcfg.layers,
+            "rows_per_layer": tcfg.rows_per_layer, "row_bytes": tcfg.row_bytes,
+            "pairs": tcfg.n_pairs, "bytes_per_call": tbytes,
+            **{name: {"us_median": round(med, 1), "us_best": round(best, 1),
+                      "GBps": round(tbytes / med / 1e3, 2),
+                      "frac_host_link": round(tbytes / med / 1e3 / ceil[name], 4) if ceil[name] else None}
+               for name, (med, best) in tres.items()},
+        }
+
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on the headline steps")
-        crow, csec = cpu_baseline(cfg, args.warmup, args.steps)
+        crow, csec, passes = cpu_baseline(cfg, args.warmup, args.steps, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(crow / csec, 1), "unit": "rows/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"the headline trace's {args.steps} timed steps "
-                                         f"(B={cfg.B}, K={cfg.K}, H={cfg.H}), single thread, "
-                                         f"host pool image in RAM; {csec:.2f} s"}
+                                         f"(B={cfg.B}, K={cfg.K}, H={cfg.H}) run {passes} times "
+                                         f"from the same starting state, single thread, host "
+                                         f"pool image in RAM; {crow} rows in {csec:.2f} s"}
     print(json.dumps(out), flush=True)
 
 

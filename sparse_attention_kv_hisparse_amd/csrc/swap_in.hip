@@ -27,14 +27,13 @@
 #include <mutex>
 
 #include "hs_common.hpp"
+#include "swap_copy.hpp"
 
 namespace hs {
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 8;             // chunks in flight per copy lane
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
 constexpr uint64_t kEmpty = ~0ull;         // (token -1, index 0xFFFFFFFF): never live
 
@@ -512,45 +511,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   resolve<kSlotRows, kPoolRows>(a, blockIdx.x, lds, lay);
 }
 
-// Copy the published misses as a flat stream of W-byte chunks: workgroup g
-// serves request g % B, part g / B of `parts`. Consecutive lanes take
-// consecutive chunks of a row, so each wave's accesses coalesce, and every
-// lane keeps kCopyUnroll independent loads in flight.
-template <int W>
-__global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(SwapArgs a, int32_t parts) {
-  typedef Chunk<W> C;
-  const int b = blockIdx.x % a.B;
-  const int part = blockIdx.x / a.B;
-  const int M = a.count[b];
-  const uint32_t total = static_cast<uint32_t>(M) * a.cdiv.d;
-  const int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
-  const int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
-  const uint32_t stride = static_cast<uint32_t>(parts) * kCopyThreads;
-  for (uint32_t j0 = static_cast<uint32_t>(part) * kCopyThreads + threadIdx.x; j0 < total;
-       j0 += stride * kCopyUnroll) {
-    typename C::T v[kCopyUnroll];
-    char* d[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const uint32_t j = j0 + u * stride;
-      d[u] = nullptr;
-      if (j < total) {
-        const uint32_t m = fdiv(j, a.cdiv);
-        const uint32_t c = j - m * a.cdiv.d;
-        const int32_t hr = dst[m];
-        if (hr >= 0 && hr < a.hot_nrows) {
-          const int64_t off = static_cast<int64_t>(c) * W;
-          v[u] = C::load(a.pool + src[m] * a.row_bytes + off);
-          d[u] = a.hot + static_cast<int64_t>(hr) * a.row_bytes + off;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u)
-      if (d[u]) C::store(d[u], v[u]);
-  }
-}
-
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
@@ -745,23 +705,18 @@ int launch_resolve(Plan& pl, hipStream_t stream) {
 }
 
 int launch_copy(Plan& pl, hipStream_t stream) {
-  // Copy grid: enough workgroups per request to cover its worst case (all K
-  // ids missing) at kCopyUnroll chunks per lane, capped at 8 per CU overall.
-  const int64_t max_items = static_cast<int64_t>(pl.s.K) * pl.C;
-  int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
-  const int64_t cap = (8LL * pl.num_cus + pl.s.B - 1) / pl.s.B;
-  if (parts > cap) parts = cap;
-  if (parts < 1) parts = 1;
-  const dim3 grid(static_cast<unsigned>(pl.s.B * parts));
-  if (pl.W == 16)
-    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, pl.s,
-                       static_cast<int32_t>(parts));
-  else
-    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, pl.s,
-                       static_cast<int32_t>(parts));
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return set_error(HS_ELAUNCH, "copy launch: %s", hipGetErrorString(e));
-  return HS_OK;
+  MissList l;
+  l.count = pl.s.count;
+  l.src = pl.s.src;
+  l.dst = pl.s.dst;
+  l.pool = pl.s.pool;
+  l.hot = pl.s.hot;
+  l.hot_nrows = pl.s.hot_nrows;
+  l.row_bytes = pl.s.row_bytes;
+  l.B = pl.s.B;
+  l.K = pl.s.K;
+  l.cdiv = pl.s.cdiv;
+  return launch_swap_copy(l, pl.W, pl.num_cus, stream);
 }
 
 }  // namespace
