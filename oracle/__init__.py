@@ -13,7 +13,11 @@ Parity pins (the tests under ``tests/test_oracle_*.py``):
   * closed forms for a cold start, a repeated step and a disjoint step;
   * invariants after every step of every workload trace;
   * hand-derived worked examples under ``tests/golden/``;
-  * numpy fancy indexing for both row copies.
+  * numpy fancy indexing for both row copies;
+  * the plan: replaying a call's compact miss list on the hot buffer as it was
+    before the call reproduces the call's hot buffer, the list agrees with the
+    dense form (out_rows, miss_mask, each entry's pool row), and miss_mask
+    marks exactly the ids the LRU model did not hold.
 """
 
 from __future__ import annotations
@@ -67,6 +71,8 @@ class _SwapArgs(ctypes.Structure):
         ("hot", ctypes.c_void_p), ("hot_nrows", ctypes.c_int64),
         ("row_bytes", ctypes.c_int64),
         ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
+        ("miss_mask", ctypes.c_void_p), ("list_count", ctypes.c_void_p),
+        ("list_src", ctypes.c_void_p), ("list_dst", ctypes.c_void_p),
     ]
 
 
@@ -91,6 +97,11 @@ def _load(path: Optional[str] = None):
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_int64, ctypes.c_int64]
         lib.oracle_state_reset.restype = ctypes.c_int
+        lib.oracle_gather_compact_layers.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int64]
+        lib.oracle_gather_compact_layers.restype = ctypes.c_int64
         _lib = lib
     return _lib
 
@@ -130,8 +141,11 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
             slot_tokens: np.ndarray, lru: np.ndarray, pool: np.ndarray, hot: np.ndarray,
             ctx_stride: int, num_real: int = -1, slot_rows: Optional[np.ndarray] = None,
             pool_rows: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None,
-            miss_counts: Optional[np.ndarray] = None):
-    """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``.
+            miss_counts: Optional[np.ndarray] = None, plan: bool = False):
+    """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``,
+    and with ``plan=True`` a third item: the plan index-sharing layers replay,
+    ``{"miss_mask": int32[B,K], "count": int32[B], "src": int64[B,K], "dst": int32[B,K]}``
+    (the compact miss list in miss order; entries past ``count[b]`` are unspecified).
 
     ``pool`` and ``hot`` are ``uint8[nrows, row_bytes]``. State arrays are updated in place.
     """
@@ -143,6 +157,10 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
         out_rows = np.empty((B, K), dtype=np.int32)
     if miss_counts is None:
         miss_counts = np.empty(B, dtype=np.int32)
+    p = None
+    if plan:
+        p = {"miss_mask": np.empty((B, K), np.int32), "count": np.empty(B, np.int32),
+             "src": np.zeros((B, K), np.int64), "dst": np.zeros((B, K), np.int32)}
     a = _SwapArgs(
         B=B, K=K, H=H, S_r=S_r, R=R,
         topk=_rows_ptr(topk, np.int32), topk_stride=_row_stride(topk),
@@ -154,11 +172,36 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
         pool=_ptr(pool, np.uint8), pool_nrows=pool.shape[0],
         hot=_ptr(hot, np.uint8, True), hot_nrows=hot.shape[0],
         row_bytes=pool.shape[1],
-        out_rows=_ptr(out_rows, np.int32, True), miss_counts=_ptr(miss_counts, np.int32, True))
+        out_rows=_ptr(out_rows, np.int32, True), miss_counts=_ptr(miss_counts, np.int32, True),
+        miss_mask=p and _ptr(p["miss_mask"], np.int32, True),
+        list_count=p and _ptr(p["count"], np.int32, True),
+        list_src=p and _ptr(p["src"], np.int64, True), list_dst=p and _ptr(p["dst"], np.int32, True))
     rc = _load().oracle_swap_in(ctypes.byref(a))
     if rc != ORACLE_OK:
         raise OracleError(rc)
-    return out_rows, miss_counts
+    return (out_rows, miss_counts, p) if plan else (out_rows, miss_counts)
+
+
+def gather_compact_layers(count: np.ndarray, src: np.ndarray, dst: np.ndarray,
+                          pool_layers: Sequence[np.ndarray], hot_layers: Sequence[np.ndarray]) -> int:
+    """Replay a compact miss plan (``count[B]``, ``src[B,K]``, ``dst[B,K]``) on every
+    (pool, hot) layer pair; returns the number of hot rows zeroed for want of a
+    source row."""
+    B, K = src.shape
+    L = len(pool_layers)
+    assert len(hot_layers) == L and count.shape == (B,) and dst.shape == (B, K)
+    rb = hot_layers[0].shape[1] if L else 1
+    for pl, hl in zip(pool_layers, hot_layers):
+        assert pl.shape[1] == rb and hl.shape[1] == rb
+        assert pl.shape[0] == pool_layers[0].shape[0] and hl.shape[0] == hot_layers[0].shape[0]
+    pp = (ctypes.c_void_p * max(L, 1))(*[_ptr(x, np.uint8) for x in pool_layers])
+    hp = (ctypes.c_void_p * max(L, 1))(*[_ptr(x, np.uint8, True) for x in hot_layers])
+    r = _load().oracle_gather_compact_layers(
+        _ptr(count, np.int32), _ptr(src, np.int64), _ptr(dst, np.int32), B, K, pp,
+        pool_layers[0].shape[0] if L else 0, hp, hot_layers[0].shape[0] if L else 0, L, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
 
 
 def transfer_rows_all_layer(src_layers: Sequence[np.ndarray], dst_layers: Sequence[np.ndarray],

@@ -63,6 +63,7 @@ static int check_args(const oracle_swap_in_args *a) {
   if (a->H < a->K || a->S_r < (int64_t)a->H + 1 || a->topk_stride < a->K || a->row_bytes <= 0 ||
       a->ctx_stride <= 0)
     return ORACLE_EARG;
+  if (a->list_count && (!a->list_src || !a->list_dst)) return ORACLE_EARG;
   return ORACLE_OK;
 }
 
@@ -115,6 +116,11 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
     int32_t *out = a->out_rows + (int64_t)b * K;
     const int32_t *ids = a->topk + (int64_t)b * a->topk_stride;
     const int64_t r = a->req_rows[b];
+
+    int32_t *mask = a->miss_mask ? a->miss_mask + (int64_t)b * K : NULL;
+    if (mask)
+      for (int32_t i = 0; i < K; ++i) mask[i] = 0;
+    if (a->list_count) a->list_count[b] = 0;
 
     /* Padding rows: -1 outputs and a zero count (vLLM page, V2 padding). */
     if (b >= nreal || r < 0 || r >= a->R) {
@@ -179,8 +185,16 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
       out[pending[j].index] = (int32_t)dst;
       tokens[v] = pending[j].token;
       memcpy(a->hot + dst * a->row_bytes, a->pool + src * a->row_bytes, (size_t)a->row_bytes);
+      /* The plan (vLLM page: miss_mask, and the compact swap lists in miss
+       * order) that index-sharing layers replay. */
+      if (mask) mask[pending[j].index] = 1;
+      if (a->list_count) {
+        a->list_src[(int64_t)b * K + M] = src;
+        a->list_dst[(int64_t)b * K + M] = (int32_t)dst;
+      }
       ++M;
     }
+    if (a->list_count) a->list_count[b] = M;
 
     /* Step 4 (LRU write-back): stale evictables first, then the slots just
      * filled in miss order, then the hits, each group in its old order. */
@@ -196,6 +210,38 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
 done:
   free(pending); free(hits); free(evict); free(new_lru);
   return rc;
+}
+
+int64_t oracle_gather_compact_layers(const int32_t *count, const int64_t *src, const int32_t *dst,
+                                     int32_t B, int32_t K, const uint8_t *const *pool_layers,
+                                     int64_t pool_nrows, uint8_t *const *hot_layers,
+                                     int64_t hot_nrows, int32_t num_layers, int64_t row_bytes) {
+  if (B < 0 || K < 0 || num_layers < 0 || row_bytes <= 0) return ORACLE_EARG;
+  if (B > 0 && K > 0 && num_layers > 0 && (!count || !src || !dst || !pool_layers || !hot_layers))
+    return ORACLE_EARG;
+  int64_t zeroed = 0;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    for (int32_t b = 0; b < B && K > 0; ++b) {
+      int32_t n = count[b];
+      if (n < 0) n = 0;
+      if (n > K) n = K;
+      for (int32_t m = 0; m < n; ++m) {
+        const int64_t s = src[(int64_t)b * K + m];
+        const int64_t d = dst[(int64_t)b * K + m];
+        if (d < 0 || d >= hot_nrows) continue;
+        uint8_t *to = hot_layers[l] + d * row_bytes;
+        if (s >= 0 && s < pool_nrows) {
+          memcpy(to, pool_layers[l] + s * row_bytes, (size_t)row_bytes);
+        } else {
+          /* No source row: the vLLM page zeroes the planned slot rather than
+           * leave stale bytes behind. */
+          memset(to, 0, (size_t)row_bytes);
+          ++zeroed;
+        }
+      }
+    }
+  }
+  return zeroed;
 }
 
 int64_t oracle_transfer_rows_all_layer(const uint8_t *const *src_layers, uint8_t *const *dst_layers,

@@ -11,7 +11,7 @@
  *   [SGL]  SGLang hisparse.cuh, load_cache_to_device_buffer_kernel and
  *          transfer_cache_dsv4_mla_kernel.
  *   [VLLM] vLLM hisparse_kernels.cu, hisparse_resolve_residency_kernel,
- *          hisparse_gather_compact_kernel.
+ *          hisparse_gather_compact_kernel, hisparse_gather_plan_kernel.
  *   [TS]   tokenspeed kvcache/triton.py, _store_kv_cache_kernel and
  *          _kv_transfer_all_layer_mla_kernel.
  *
@@ -57,11 +57,29 @@ typedef struct {
   int64_t row_bytes;
   int32_t *out_rows;        /* [B, K] */
   int32_t *miss_counts;     /* [B] or NULL */
+  /* Optional plan outputs (all NULL, or each as documented): */
+  int32_t *miss_mask;       /* [B, K] or NULL: 1 where the entry missed and got a slot */
+  int32_t *list_count;      /* [B] or NULL: misses of row b (the compact plan's length) */
+  int64_t *list_src;        /* [B, K]: pool row of miss m of row b, m < list_count[b] */
+  int32_t *list_dst;        /* [B, K]: hot row of miss m of row b */
 } oracle_swap_in_args;
 
 /* One decode-step swap-in call. Returns ORACLE_OK or a negative code when a
  * precondition of the pages is broken; outputs are then unspecified. */
 int oracle_swap_in(const oracle_swap_in_args *a);
+
+/* Replay of a compact miss plan on num_layers (pool, hot) pairs that share
+ * the plan's indices ([VLLM] hisparse_gather_compact_kernel, and the
+ * index-sharing layers of hisparse_gather_plan_kernel): for every layer l,
+ * row b and miss m < count[b] (count clamped to [0, K]), with s = src[b][m]
+ * and d = dst[b][m]: skip when d is outside [0, hot_nrows); copy pool row s
+ * of layer l to hot row d of layer l when s is inside [0, pool_nrows);
+ * otherwise write zeros to that hot row. Returns the number of rows zeroed
+ * (summed over layers), or ORACLE_EARG. */
+int64_t oracle_gather_compact_layers(const int32_t *count, const int64_t *src, const int32_t *dst,
+                                     int32_t B, int32_t K, const uint8_t *const *pool_layers,
+                                     int64_t pool_nrows, uint8_t *const *hot_layers,
+                                     int64_t hot_nrows, int32_t num_layers, int64_t row_bytes);
 
 /* dst_layers[l][dst_idx[i]] <- src_layers[l][src_idx[i]] for every pair i and
  * layer l (row_bytes bytes each). Pairs with an index outside [0, nrows) are

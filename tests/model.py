@@ -24,8 +24,11 @@ from typing import Dict, List, Optional
 
 
 def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, ctx_stride,
-                      num_real=-1, slot_rows=None, pool_rows=None):
-    """Same contract as ``oracle.swap_in`` (numpy arrays updated in place)."""
+                      num_real=-1, slot_rows=None, pool_rows=None, plan=False):
+    """Same contract as ``oracle.swap_in`` (numpy arrays updated in place). With
+    ``plan=True`` also returns the plan: ``miss_mask`` [B,K] (1 for each entry
+    whose token no slot held) and, per row, the list of (pool row, hot row)
+    copies in the order they were made."""
     import numpy as np
 
     B, K = topk.shape
@@ -33,6 +36,8 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
     H = lru.shape[1]
     out = np.full((B, K), -1, dtype=np.int32)
     counts = np.zeros(B, dtype=np.int32)
+    mask = np.zeros((B, K), dtype=np.int32)
+    copies = [[] for _ in range(B)]
 
     def row_of(r, s):
         return int(slot_rows[r, s]) if slot_rows is not None else r * S_r + s
@@ -74,8 +79,12 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
             slot_tokens[r, v] = t
             hot[row_of(r, v)] = pool[pool_of(r, t)]
             out[b, i] = row_of(r, v)
+            mask[b, i] = 1
+            copies[b].append((pool_of(r, t), row_of(r, v)))
         lru[r] = np.asarray(list(cache) + [s for s in order if s in hit_slots], dtype=np.int16)
         counts[b] = len(misses)
+    if plan:
+        return out, counts, {"miss_mask": mask, "copies": copies}
     return out, counts
 
 

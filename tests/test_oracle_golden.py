@@ -32,15 +32,21 @@ def test_swap_in_worked_examples(name):
     slot_rows = np.asarray(fx["slot_rows"], dtype=np.int32) if "slot_rows" in fx else None
     pool_rows = np.asarray(fx["pool_rows"], dtype=np.int64) if "pool_rows" in fx else None
     for call in fx["calls"]:
-        out, counts = oracle.swap_in(
+        out, counts, plan = oracle.swap_in(
             topk=np.asarray(call["topk"], dtype=np.int32),
             req_rows=np.asarray(call["req_rows"], dtype=np.int64),
             seq_lens=np.asarray(call["seq_lens"], dtype=np.int64),
             slot_tokens=tokens, lru=lru, pool=pool, hot=hot, ctx_stride=fx["ctx_stride"],
-            num_real=call["num_real"], slot_rows=slot_rows, pool_rows=pool_rows)
+            num_real=call["num_real"], slot_rows=slot_rows, pool_rows=pool_rows, plan=True)
         e = call["expect"]
         assert out.tolist() == e["out"]
         assert counts.tolist() == e["miss_counts"]
+        assert plan["miss_mask"].tolist() == e["miss_mask"]
+        assert plan["count"].tolist() == e["miss_counts"]
+        for b, lst in enumerate(e["miss_list"]):
+            n = len(lst)
+            got = list(zip(plan["src"][b, :n].tolist(), plan["dst"][b, :n].tolist()))
+            assert got == [tuple(x) for x in lst], (b, got, lst)
         assert tokens.tolist() == e["slot_tokens"]
         assert lru.tolist() == e["lru"]
         want = np.zeros_like(hot)

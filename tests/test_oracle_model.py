@@ -8,6 +8,9 @@
   ``TextbookLRU``.
 * The two pages' LRU write-back formulas (different index algebra on the
   same compacted array) give the oracle's order.
+* Every comparison with the model also covers the plan the oracle publishes
+  for index-sharing layers: the miss mask and the compact copy list in miss
+  order.
 """
 
 import itertools
@@ -37,8 +40,15 @@ def _run_both(calls, *, R, H, S_r, ctx_stride, rb=8, slot_rows=None, pool_rows=N
         kw = dict(topk=c["topk"], req_rows=c["req_rows"], seq_lens=c["seq_lens"],
                   ctx_stride=ctx_stride, num_real=c.get("num_real", -1), slot_rows=slot_rows,
                   pool_rows=pool_rows, pool=pool)
-        out_o, cnt_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, **kw)
-        out_m, cnt_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, **kw)
+        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True, **kw)
+        out_m, cnt_m, plan_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, plan=True,
+                                                 **kw)
+        # the plan: which entries missed, and the copies in the order made
+        assert plan_o["miss_mask"].tolist() == plan_m["miss_mask"].tolist()
+        assert plan_o["count"].tolist() == cnt_m.tolist()
+        for b, cp in enumerate(plan_m["copies"]):
+            n = len(cp)
+            assert list(zip(plan_o["src"][b, :n].tolist(), plan_o["dst"][b, :n].tolist())) == cp
         assert out_o.tolist() == out_m.tolist()
         assert cnt_o.tolist() == cnt_m.tolist()
         assert st_o.tolist() == st_m.tolist()

@@ -38,6 +38,14 @@ MUTANTS = {
                               "out[f->index] = (int32_t)hot_row(a, r, p);"),
     "lru_transposed_index": ("const int16_t s = lru[p];", "const int16_t s = (int16_t)p;"),
     "no_padding": ("if (b >= nreal || r < 0 || r >= a->R) {", "if (r < 0 || r >= a->R) {"),
+    "plan_list_at_entry_index": ("a->list_src[(int64_t)b * K + M] = src;\n"
+                                 "        a->list_dst[(int64_t)b * K + M] = (int32_t)dst;",
+                                 "a->list_src[(int64_t)b * K + pending[j].index] = src;\n"
+                                 "        a->list_dst[(int64_t)b * K + pending[j].index] = (int32_t)dst;"),
+    "plan_mask_not_set": ("if (mask) mask[pending[j].index] = 1;", ""),
+    "replay_count_clamp_off_by_one": ("if (n > K) n = K;", "if (n > K) n = K - 1;"),
+    "replay_no_zero_fill": ("memset(to, 0, (size_t)row_bytes);", ""),
+    "replay_row_zero_has_no_source": ("if (s >= 0 && s < pool_nrows) {", "if (s > 0 && s < pool_nrows) {"),
 }
 
 
@@ -46,6 +54,7 @@ def _pins():
     import test_oracle_closed_forms as cf
     import test_oracle_golden as g
     import test_oracle_model as m
+    import test_oracle_plan as pl
     failed = []
     checks = [
         ("golden1", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_1.json")),
@@ -54,6 +63,8 @@ def _pins():
         ("textbook_lru", lambda: m.test_topk1_is_textbook_lru(4, 9, 1)),
         ("cold", lambda: cf.test_cold_start(64, 16)),
         ("disjoint", lambda: cf.test_disjoint_step_evicts_oldest(0)),
+        ("replay_golden", pl.test_replay_worked_example),
+        ("replay_numpy", lambda: pl.test_replay_layers_matches_numpy(1)),
     ]
     for name, fn in checks:
         try:
