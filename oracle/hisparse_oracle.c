@@ -228,9 +228,9 @@ int64_t oracle_gather_compact_layers(const int32_t *count, const int64_t *src, c
       for (int32_t m = 0; m < n; ++m) {
         const int64_t s = src[(int64_t)b * K + m];
         const int64_t d = dst[(int64_t)b * K + m];
-        if (d < 0 || d >= hot_nrows) continue;
+        if (s < 0 || d < 0 || d >= hot_nrows) continue;
         uint8_t *to = hot_layers[l] + d * row_bytes;
-        if (s >= 0 && s < pool_nrows) {
+        if (s < pool_nrows) {
           memcpy(to, pool_layers[l] + s * row_bytes, (size_t)row_bytes);
         } else {
           /* No source row: the vLLM page zeroes the planned slot rather than

@@ -72,10 +72,10 @@ int oracle_swap_in(const oracle_swap_in_args *a);
  * the plan's indices ([VLLM] hisparse_gather_compact_kernel, and the
  * index-sharing layers of hisparse_gather_plan_kernel): for every layer l,
  * row b and miss m < count[b] (count clamped to [0, K]), with s = src[b][m]
- * and d = dst[b][m]: skip when d is outside [0, hot_nrows); copy pool row s
- * of layer l to hot row d of layer l when s is inside [0, pool_nrows);
- * otherwise write zeros to that hot row. Returns the number of rows zeroed
- * (summed over layers), or ORACLE_EARG. */
+ * and d = dst[b][m]: skip when s < 0 or d is outside [0, hot_nrows); copy
+ * pool row s of layer l to hot row d of layer l when s < pool_nrows;
+ * otherwise (no such source row) write zeros to that hot row. Returns the
+ * number of rows zeroed (summed over layers), or ORACLE_EARG. */
 int64_t oracle_gather_compact_layers(const int32_t *count, const int64_t *src, const int32_t *dst,
                                      int32_t B, int32_t K, const uint8_t *const *pool_layers,
                                      int64_t pool_nrows, uint8_t *const *hot_layers,

@@ -45,7 +45,9 @@ MUTANTS = {
     "plan_mask_not_set": ("if (mask) mask[pending[j].index] = 1;", ""),
     "replay_count_clamp_off_by_one": ("if (n > K) n = K;", "if (n > K) n = K - 1;"),
     "replay_no_zero_fill": ("memset(to, 0, (size_t)row_bytes);", ""),
-    "replay_row_zero_has_no_source": ("if (s >= 0 && s < pool_nrows) {", "if (s > 0 && s < pool_nrows) {"),
+    "replay_row_zero_has_no_source": ("if (s < pool_nrows) {", "if (s > 0 && s < pool_nrows) {"),
+    "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
+                                      "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }
 
 

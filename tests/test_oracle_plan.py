@@ -6,7 +6,8 @@ entries that missed and the compact list of (pool row, hot row) copies in miss
 order. Pins, none of which retypes the oracle:
 
 * the hand-derived replay in ``tests/golden/plan_replay_worked_example.json``
-  (count clamping, skipped destinations, zero-filled rows without a source);
+  (count clamping, skipped entries, a zero-filled row whose source is past
+  the end of the pool);
 * replaying a call's list on the hot buffer as it was before the call gives
   the hot buffer the call produced, on every step of the small workload traces;
 * the list is the dense plan read in top-k order: for each masked entry, the
@@ -90,8 +91,8 @@ def test_replay_layers_matches_numpy(seed):
         for b in range(B):
             n = min(max(int(count[b]), 0), K)
             d, s = dst[b, :n].astype(np.int64), src[b, :n]
-            ok = (d >= 0) & (d < Hn)
-            has = ok & (s >= 0) & (s < P)
+            ok = (s >= 0) & (d >= 0) & (d < Hn)
+            has = ok & (s < P)
             want[l][d[has]] = pools[l][s[has]]
             want[l][d[ok & ~has]] = 0
             zeroed += int((ok & ~has).sum())
