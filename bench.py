@@ -14,6 +14,9 @@ Also reported in the same JSON line:
   * adversarial: B=64, hot_size 8192, 65,536-token contexts, ids that collide
     in the low-bit multiplicative hash, 1152-byte and 132-byte rows: the cold
     step and the steps after it;
+  * plan_replay: the headline trace with index-sharing layers (1 resolving
+    layer + 3 replaying its plan): one fused replay launch for all layers
+    against one copy launch per layer;
   * all_layer: the fused all-layer transfer (61 layers x 262,144 rows x 656 B,
     8192 pairs) in both directions against the host-link ceiling;
   * host_link: the measured host-link ceiling the host-pool rooflines use;
@@ -52,6 +55,10 @@ def parse():
     p.add_argument("--no-host-link", action="store_true")
     p.add_argument("--no-all-layer", action="store_true")
     p.add_argument("--no-adversarial", action="store_true")
+    p.add_argument("--no-plan-replay", action="store_true")
+    p.add_argument("--replay-layers", type=int, default=4,
+                   help="layers per index-sharing group in the plan-replay leg (1 resolving "
+                        "layer + the rest replaying its plan)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU seconds of oracle work for cpu_baseline (whole replays "
                         "of the headline's timed steps)")
@@ -167,6 +174,84 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     torch.cuda.empty_cache()
     return dict(us_total=us_total, us_resolve=us_resolve, us_copy=us_copy, us_cold=us_cold,
                 cold_rows=cold_rows, counts=c, wall=wall)
+
+
+def run_plan_replay(cfg, layers, warmup, steps, torch, hs, wdev):
+    """Index-sharing layers on the headline workload: per step one resolve on
+    layer 0, then the plan is copied for all `layers` layers, either as ONE
+    hisparse_gather_compact_layers launch (fused) or as one
+    hisparse_gather_compact launch per layer (separate). Layer 0's pool holds
+    the workload's bytes; the other layers' pools are pinned buffers of the
+    same shape. Each variant runs the trace from a reset state (W warm-up
+    steps, then K timed steps between two events). A third pass times the K
+    fused replays alone, back to back after K resolves into K workspaces."""
+    log(f"[bench] plan replay: {layers} layers on {cfg.name}")
+    pools = [wdev.make_pool(cfg)] + [wdev.pinned_uint8(cfg.pool_nrows, cfg.row_bytes)
+                                     for _ in range(layers - 1)]
+    st = wdev.DeviceSwapState(cfg)
+    hots = [st.hot] + [torch.zeros_like(st.hot) for _ in range(layers - 1)]
+    pptr = torch.tensor([p.data_ptr() for p in pools], dtype=torch.int64, device="cuda")
+    hptr = torch.tensor([h.data_ptr() for h in hots], dtype=torch.int64, device="cuda")
+    tr = Trace(cfg, warmup + steps, torch)
+    counts = torch.empty((warmup + steps, cfg.B), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    allrows = torch.arange(cfg.R, dtype=torch.int64, device="cuda")
+
+    def resolve(t, ws):
+        hs.hisparse_resolve(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t],
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pools[0], hot=hots[0],
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=ws,
+                            miss_counts=counts[t], stream=stream)
+
+    def fused(ws):
+        hs.hisparse_gather_compact_layers(workspace=ws, B=cfg.B, K=cfg.K, pool_layer_ptrs=pptr,
+                                          pool_nrows=cfg.pool_nrows, hot_layer_ptrs=hptr,
+                                          hot_nrows=hots[0].shape[0], row_bytes=cfg.row_bytes,
+                                          stream=stream)
+
+    def separate(t, ws):
+        for l in range(layers):
+            hs.hisparse_gather_compact(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t],
+                                       slot_tokens=st.slot_tokens, lru=st.lru, pool=pools[l],
+                                       hot=hots[l], out_rows=st.out, ctx_stride=cfg.ctx,
+                                       workspace=ws, stream=stream)
+
+    def timed(step_fn):
+        hs.hisparse_state_reset(slot_tokens=st.slot_tokens, lru=st.lru, rows=allrows)
+        for t in range(warmup):
+            step_fn(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(steps):
+            step_fn(warmup + k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0
+
+    us_fused = timed(lambda t: (resolve(t, st.ws), fused(st.ws)))
+    c = counts.cpu().numpy()[warmup:].copy()
+    us_sep = timed(lambda t: (resolve(t, st.ws), separate(t, st.ws)))
+    assert (counts.cpu().numpy()[warmup:] == c).all(), "plan replay passes diverged"
+    # replay kernel alone
+    hs.hisparse_state_reset(slot_tokens=st.slot_tokens, lru=st.lru, rows=allrows)
+    for t in range(warmup):
+        resolve(t, st.ws)
+        fused(st.ws)
+    wss = [torch.zeros_like(st.ws) for _ in range(steps)]
+    for k in range(steps):
+        resolve(warmup + k, wss[k])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(steps):
+        fused(wss[k])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_replay = e0.elapsed_time(e1) * 1000.0
+    del pools, hots, st, tr, wss
+    torch.cuda.empty_cache()
+    return dict(rows=int(c.sum()), us_fused=us_fused, us_separate=us_sep, us_replay=us_replay)
 
 
 def kernel_sources_hash():
@@ -477,6 +562,23 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16>", "achieved": round(dach, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("device_pool")},
+        }
+
+    if not args.no_plan_replay:
+        L = args.replay_layers
+        pr = run_plan_replay(cfg, L, args.warmup, K, torch, hs, wdev)
+        link_bytes = pr["rows"] * cfg.row_bytes * L
+        out["plan_replay"] = {
+            "workload": "dsv32_decode_index_sharing_layers", "layers": L,
+            "rows_per_step_per_layer": round(pr["rows"] / K, 1),
+            "us_per_step_fused": round(pr["us_fused"] / K, 2),
+            "us_per_step_separate": round(pr["us_separate"] / K, 2),
+            "us_replay_kernel": round(pr["us_replay"] / K, 2),
+            "GBps_replay_kernel": round(link_bytes / pr["us_replay"] / 1e3, 2),
+            "frac_host_link_replay_kernel": round(link_bytes / pr["us_replay"] / 1e3 / peak, 4)
+            if peak else None,
+            "GBps_step_fused": round(link_bytes / pr["us_fused"] / 1e3, 2),
+            "GBps_step_separate": round(link_bytes / pr["us_separate"] / 1e3, 2),
         }
 
     if not args.no_adversarial:

@@ -12,7 +12,9 @@
  *                                 transfer_cache_dsv4_mla_kernel (all-layer copy).
  *   vLLM hisparse_kernels.cu   -- hisparse_resolve_residency_kernel (the swap-in's
  *                                 resolution half), hisparse_gather_compact_kernel
- *                                 (its copy half), host argument checks.
+ *                                 (its copy half), hisparse_gather_plan_kernel
+ *                                 (plan replay on index-sharing layers), host
+ *                                 argument checks.
  *   tokenspeed kvcache/triton.py -- _kv_transfer_all_layer_mla_kernel,
  *                                 _store_kv_cache_kernel.
  *
@@ -97,6 +99,9 @@ typedef struct hs_swap_in_args {
 
   int32_t* out_rows;         /* device [B, K] out: hot row per entry, or -1      */
   int32_t* miss_counts;      /* device [B] out, or NULL: rows copied per row     */
+  int32_t* miss_mask;        /* device [B, K] out, or NULL: 1 where the entry    */
+                             /* missed and was given a slot (step 3), else 0     */
+                             /* (vLLM hisparse_kernels.cu, miss_mask)            */
 } hs_swap_in_args;
 
 /* Bytes of device workspace hisparse_swap_in needs for B rows of K ids
@@ -158,11 +163,42 @@ int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t worksp
  * must hold the list of a resolve call with the same B and K enqueued before
  * it (on the same stream, or ordered by an event). Resolve then gather is
  * exactly hisparse_swap_in. Errors as for hisparse_swap_in.
+ * Per list entry (as vLLM's hisparse_gather_compact_kernel): the count is
+ * clamped to [0, K]; an entry whose pool row is negative or whose hot row is
+ * outside [0, hot_nrows) is skipped; a pool row >= pool_nrows writes zeros to
+ * the hot row. A list written by a resolve on the same pool never hits the
+ * last two cases.
  */
 int hisparse_resolve(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 int hisparse_gather_compact(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * hisparse_gather_compact_layers -- replay one resolved plan on several layers.
+ * vLLM hisparse_kernels.cu, hisparse_gather_plan_kernel: layers that share the
+ * index-producing layer's top-k ids get the same slots, so they reuse its
+ * plan and copy only their own bytes; no LRU work is redone.
+ *
+ * workspace / workspace_bytes / B / K: a workspace holding the miss list of a
+ * hisparse_resolve call with the same B and K, enqueued before this call.
+ * pool_layer_ptrs, hot_layer_ptrs: device uint64 [num_layers] arrays of layer
+ * base addresses, as the device sees them (a pinned host pool's address, or
+ * HBM); every layer holds pool_nrows (hot_nrows) rows of row_bytes, with the
+ * row numbering of the layer the plan was resolved on. Bases must be 4-byte
+ * aligned; 16-byte aligned bases with row_bytes % 16 == 0 take the 16-byte
+ * path. For every layer l and list entry (pool row s, hot row d), with the
+ * entry rules of hisparse_gather_compact:
+ *   hot_layer_ptrs[l] + d*row_bytes  <-  pool_layer_ptrs[l] + s*row_bytes.
+ * All layers move in one launch. Hot rows of different layers must not
+ * overlap. B, K or num_layers == 0 returns HS_OK with nothing enqueued; other
+ * errors as for hisparse_swap_in, and HS_ERANGE when K * num_layers *
+ * (row_bytes / 16, or / 4) reaches 2^31.
+ */
+int hisparse_gather_compact_layers(const void* workspace, size_t workspace_bytes, int32_t B,
+                                   int32_t K, const uint64_t* pool_layer_ptrs, int64_t pool_nrows,
+                                   const uint64_t* hot_layer_ptrs, int64_t hot_nrows,
+                                   int32_t num_layers, int64_t row_bytes, hipStream_t stream);
 
 /*
  * Workspace layout of the miss list, for callers that read it (vLLM

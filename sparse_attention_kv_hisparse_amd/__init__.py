@@ -16,6 +16,7 @@ import torch
 from ._lib import EXPORTS, HisparseError, SwapInArgs, check, load
 
 __all__ = ["hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
+           "hisparse_gather_compact_layers",
            "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
            "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
 
@@ -55,14 +56,16 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                      workspace: torch.Tensor, miss_counts: Optional[torch.Tensor] = None,
                      num_real: Optional[torch.Tensor] = None,
                      slot_rows: Optional[torch.Tensor] = None,
-                     pool_rows: Optional[torch.Tensor] = None, stream=None,
+                     pool_rows: Optional[torch.Tensor] = None,
+                     miss_mask: Optional[torch.Tensor] = None, stream=None,
                      _entry: str = "hisparse_swap_in") -> None:
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
     slot_tokens int32 [R, S_r], lru int16 [R, H], pool uint8 [rows, row_bytes]
     (pinned host or device), hot uint8 [rows, row_bytes] (device), out_rows int32 [B, K],
-    workspace uint8 device tensor of at least ``swap_in_workspace_bytes(B, K)`` bytes.
+    workspace uint8 device tensor of at least ``swap_in_workspace_bytes(B, K)`` bytes,
+    miss_mask int32 [B, K] (optional output: 1 where the entry missed and got a slot).
     """
     B, K = out_rows.shape
     if topk.dim() != 2 or topk.shape[0] != B or topk.shape[1] < K or topk.stride(1) != 1:
@@ -91,7 +94,10 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         ctx_stride=ctx_stride, pool=pool.data_ptr(), pool_nrows=pool.shape[0],
         hot=hot.data_ptr(), hot_nrows=hot.shape[0], row_bytes=hot.shape[1],
         out_rows=_dev(out_rows, torch.int32, "out_rows"),
-        miss_counts=_opt(miss_counts, torch.int32, "miss_counts"))
+        miss_counts=_opt(miss_counts, torch.int32, "miss_counts"),
+        miss_mask=_opt(miss_mask, torch.int32, "miss_mask"))
+    if miss_mask is not None and (tuple(miss_mask.shape) != (B, K) or not miss_mask.is_contiguous()):
+        raise ValueError("miss_mask must be a contiguous [B, K] int32 tensor")
     ws = _dev(workspace, torch.uint8, "workspace")
     check(_entry, getattr(load(), _entry)(ctypes.byref(a), ws, workspace.numel(), _stream(stream)))
 
@@ -106,6 +112,22 @@ def hisparse_gather_compact(**kw) -> None:
     """Copy half (``hisparse_gather_compact``): copies the rows a preceding
     ``hisparse_resolve`` with the same workspace listed."""
     hisparse_swap_in(_entry="hisparse_gather_compact", **kw)
+
+
+def hisparse_gather_compact_layers(*, workspace: torch.Tensor, B: int, K: int,
+                                   pool_layer_ptrs: torch.Tensor, pool_nrows: int,
+                                   hot_layer_ptrs: torch.Tensor, hot_nrows: int, row_bytes: int,
+                                   stream=None) -> None:
+    """Replay the plan a preceding ``hisparse_resolve`` left in ``workspace`` on every
+    layer pair; layer pointer arrays are device uint64 (torch int64) [L]."""
+    L = pool_layer_ptrs.numel()
+    if hot_layer_ptrs.numel() != L:
+        raise ValueError("pool and hot layer pointer arrays must have equal lengths")
+    check("hisparse_gather_compact_layers", load().hisparse_gather_compact_layers(
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), B, K,
+        _dev(pool_layer_ptrs, torch.int64, "pool_layer_ptrs"), pool_nrows,
+        _dev(hot_layer_ptrs, torch.int64, "hot_layer_ptrs"), hot_nrows, L, row_bytes,
+        _stream(stream)))
 
 
 def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: torch.Tensor,

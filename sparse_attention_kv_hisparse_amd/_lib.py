@@ -18,8 +18,9 @@ STATUS = {0: "HS_OK", -1: "HS_EINVAL", -2: "HS_ERANGE", -3: "HS_EMEMKIND", -4: "
 
 # Every function include/hisparse.h declares.
 EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_resolve",
-           "hisparse_gather_compact", "hs_swap_in_workspace_layout", "transfer_rows_all_layer",
-           "store_kv_scatter", "hisparse_state_reset", "hisparse_last_error")
+           "hisparse_gather_compact", "hisparse_gather_compact_layers",
+           "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
+           "hisparse_state_reset", "hisparse_last_error")
 
 
 class SwapInArgs(ctypes.Structure):
@@ -38,6 +39,7 @@ class SwapInArgs(ctypes.Structure):
         ("hot", ctypes.c_void_p), ("hot_nrows", ctypes.c_int64),
         ("row_bytes", ctypes.c_int64),
         ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
+        ("miss_mask", ctypes.c_void_p),
     ]
 
 
@@ -64,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact"):
         getattr(lib, name).argtypes = [ctypes.POINTER(SwapInArgs), vp, sz, vp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.hisparse_gather_compact_layers.argtypes = [vp, sz, i32, i32, vp, i64, vp, i64, i32, i64, vp]
+    lib.hisparse_gather_compact_layers.restype = ctypes.c_int
     szp = ctypes.POINTER(ctypes.c_size_t)
     lib.hs_swap_in_workspace_layout.argtypes = [i32, i32, szp, szp, szp]
     lib.hs_swap_in_workspace_layout.restype = sz

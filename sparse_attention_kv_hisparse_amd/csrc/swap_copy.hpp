@@ -1,9 +1,16 @@
 // Copy half of the swap-in: moves the rows a resolve published as a compact
 // miss list (count[b], then (pool row, hot row) pairs in miss order) from the
-// pool to the hot buffer. SGLang hisparse.cuh copies inside the resolving
-// block and vLLM hisparse_kernels.cu runs hisparse_gather_compact_kernel over
-// the same kind of list; here the list is copied by many 256-lane workgroups
-// per request as one flat stream of W-byte chunks.
+// pool to the hot buffer, on one (pool, hot) pair or replayed on several
+// layers that share the plan. SGLang hisparse.cuh copies inside the resolving
+// block; vLLM hisparse_kernels.cu runs hisparse_gather_compact_kernel over the
+// same kind of list and hisparse_gather_plan_kernel for index-sharing layers.
+// Here the list is copied by many 256-lane workgroups per request as one flat
+// stream of W-byte chunks.
+//
+// Per entry (vLLM hisparse_gather_compact_kernel): the count is clamped to
+// [0, K]; an entry with a negative pool row or a hot row outside the hot
+// buffer is skipped; a pool row at or past the end of the pool zeroes the hot
+// row instead of leaving stale bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,31 +21,50 @@ namespace hs {
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 8;  // chunks in flight per copy lane
+constexpr int kCopyUnroll = 8;        // chunks in flight per copy lane
+constexpr int kMaxStagedPairs = 256;  // layer pointer pairs staged in LDS
 
-// One miss list and the two row spaces it indexes.
+// One miss list and the row spaces it indexes.
 struct MissList {
   const int32_t* count;  // [B] misses of request b
   const int64_t* src;    // [B, K] pool row of miss m
-  const int32_t* dst;    // [B, K] hot row of miss m (outside [0, hot_nrows) = skip)
-  const char* pool;      // device-visible address of the pool
-  char* hot;
+  const int32_t* dst;    // [B, K] hot row of miss m
+  const char* pool;      // device-visible address of the pool (single pair)
+  char* hot;             // (single pair)
+  const uint64_t* pool_layers;  // [layers] pool bases (layered replay)
+  const uint64_t* hot_layers;   // [layers] hot bases (layered replay)
+  int64_t pool_nrows;
   int64_t hot_nrows;
   int64_t row_bytes;
   int32_t B, K;
+  int32_t layers;        // 1 for a single pair
   FastDiv cdiv;          // chunks per row
+  FastDiv ldiv;          // layers
 };
 
-// Workgroup g serves request g % B, part g / B of `parts`. Consecutive lanes
-// take consecutive chunks of a row, so each wave's accesses coalesce, and
-// every lane keeps kCopyUnroll independent loads in flight.
-template <int W>
+// Workgroup g serves request g % B, part g / B of `parts`. Items are
+// (miss, layer, chunk) with the chunk fastest: consecutive lanes take
+// consecutive chunks of one row, so each wave's accesses coalesce, and every
+// lane keeps kCopyUnroll independent loads in flight.
+template <int W, bool kLayers>
 __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int32_t parts) {
   typedef Chunk<W> C;
+  __shared__ uint64_t s_pool[kLayers ? kMaxStagedPairs : 1];
+  __shared__ uint64_t s_hot[kLayers ? kMaxStagedPairs : 1];
+  const bool staged = kLayers && a.layers <= kMaxStagedPairs;
+  if (staged) {
+    for (int l = threadIdx.x; l < a.layers; l += kCopyThreads) {
+      s_pool[l] = a.pool_layers[l];
+      s_hot[l] = a.hot_layers[l];
+    }
+    __syncthreads();
+  }
   const int b = blockIdx.x % a.B;
   const int part = blockIdx.x / a.B;
-  const int M = a.count[b];
-  const uint32_t total = static_cast<uint32_t>(M) * a.cdiv.d;
+  int M = a.count[b];
+  M = M < 0 ? 0 : (M > a.K ? a.K : M);
+  const uint32_t per_miss = (kLayers ? static_cast<uint32_t>(a.layers) : 1u) * a.cdiv.d;
+  const uint32_t total = static_cast<uint32_t>(M) * per_miss;
   const int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
   const int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
   const uint32_t stride = static_cast<uint32_t>(parts) * kCopyThreads;
@@ -51,13 +77,35 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
       const uint32_t j = j0 + u * stride;
       d[u] = nullptr;
       if (j < total) {
-        const uint32_t m = fdiv(j, a.cdiv);
-        const uint32_t c = j - m * a.cdiv.d;
+        const uint32_t q = fdiv(j, a.cdiv);          // (miss, layer) row
+        const uint32_t c = j - q * a.cdiv.d;        // chunk in the row
+        uint32_t m = q, l = 0;
+        if (kLayers) {
+          m = fdiv(q, a.ldiv);
+          l = q - m * a.ldiv.d;
+        }
+        const int64_t s = src[m];
         const int32_t hr = dst[m];
-        if (hr >= 0 && hr < a.hot_nrows) {
+        if (s >= 0 && hr >= 0 && hr < a.hot_nrows) {
+          const char* pbase = a.pool;
+          char* hbase = a.hot;
+          if (kLayers) {
+            pbase = reinterpret_cast<const char*>(staged ? s_pool[l] : a.pool_layers[l]);
+            hbase = reinterpret_cast<char*>(staged ? s_hot[l] : a.hot_layers[l]);
+          }
           const int64_t off = static_cast<int64_t>(c) * W;
-          v[u] = C::load(a.pool + src[m] * a.row_bytes + off);
-          d[u] = a.hot + static_cast<int64_t>(hr) * a.row_bytes + off;
+          char* to = hbase + static_cast<int64_t>(hr) * a.row_bytes + off;
+          const char* from = pbase + s * a.row_bytes + off;
+          const bool has = s < a.pool_nrows;
+          if (W == 16 && kLayers &&
+              ((reinterpret_cast<uintptr_t>(pbase) | reinterpret_cast<uintptr_t>(hbase)) & 15)) {
+            // A layer base that is only 4-byte aligned: move this chunk as dwords.
+#pragma unroll
+            for (int k = 0; k < W; k += 4) Chunk<4>::store(to + k, has ? Chunk<4>::load(from + k) : 0u);
+          } else {
+            v[u] = has ? C::load(from) : typename C::T{};
+            d[u] = to;
+          }
         }
       }
     }
@@ -68,21 +116,28 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
 }
 
 // Grid: enough workgroups per request to cover its worst case (all K ids
-// missing) at kCopyUnroll chunks per lane, capped at 8 per CU overall.
-// W is 16 when pool, hot and row_bytes are 16-byte aligned, else 4.
+// missing, every layer) at kCopyUnroll chunks per lane, capped at 8 per CU
+// overall. W is 16 when the bases and row_bytes are 16-byte aligned, else 4.
 inline int launch_swap_copy(const MissList& a, int W, int num_cus, hipStream_t stream) {
-  const int64_t max_items = static_cast<int64_t>(a.K) * a.cdiv.d;
+  const bool layered = a.pool_layers != nullptr;
+  const int64_t max_items = static_cast<int64_t>(a.K) * a.layers * a.cdiv.d;
   int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
   const int64_t cap = (8LL * num_cus + a.B - 1) / a.B;
   if (parts > cap) parts = cap;
   if (parts < 1) parts = 1;
   const dim3 grid(static_cast<unsigned>(a.B * parts));
-  if (W == 16)
-    hipLaunchKernelGGL(swap_copy_kernel<16>, grid, dim3(kCopyThreads), 0, stream, a,
-                       static_cast<int32_t>(parts));
-  else
-    hipLaunchKernelGGL(swap_copy_kernel<4>, grid, dim3(kCopyThreads), 0, stream, a,
-                       static_cast<int32_t>(parts));
+  const int32_t p = static_cast<int32_t>(parts);
+  if (W == 16) {
+    if (layered)
+      hipLaunchKernelGGL((swap_copy_kernel<16, true>), grid, dim3(kCopyThreads), 0, stream, a, p);
+    else
+      hipLaunchKernelGGL((swap_copy_kernel<16, false>), grid, dim3(kCopyThreads), 0, stream, a, p);
+  } else {
+    if (layered)
+      hipLaunchKernelGGL((swap_copy_kernel<4, true>), grid, dim3(kCopyThreads), 0, stream, a, p);
+    else
+      hipLaunchKernelGGL((swap_copy_kernel<4, false>), grid, dim3(kCopyThreads), 0, stream, a, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "copy launch: %s", hipGetErrorString(e));
   return HS_OK;

@@ -65,6 +65,7 @@ struct SwapArgs {
   int64_t row_bytes;
   int32_t* out_rows;
   int32_t* miss_counts;
+  int32_t* miss_mask; // [B, K] or null: 1 where the entry missed and got a slot
   int32_t* count;     // [B] misses of request b
   int64_t* src;       // [B, K] pool row of miss m
   int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
@@ -159,6 +160,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   if (b >= nreal || r < 0 || r >= a.R) {
     // Padding row (vLLM page's V2 convention): -1 everywhere, no misses.
     for (int i = tid; i < K; i += kThreads) out[i] = -1;
+    if (a.miss_mask)
+      for (int i = tid; i < K; i += kThreads) a.miss_mask[static_cast<int64_t>(b) * K + i] = 0;
     if (tid == 0) {
       a.count[b] = 0;
       if (a.miss_counts) a.miss_counts[b] = 0;
@@ -457,6 +460,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   }
   int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
+  int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
   run = miss_before;
   for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
     uint64_t wd[4];
@@ -482,6 +486,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int i = k0 + c0 + u * kWave + lane;
       if (c0 + u * kWave >= segK || i >= K) continue;
       int32_t o = so[u];
+      const bool missed = ((wd[u] >> lane) & 1ull) && v[u] >= 0 && v[u] < H;
+      if (mask) mask[i] = missed ? 1 : 0;
       if ((wd[u] >> lane) & 1ull) {
         if (v[u] >= 0 && v[u] < H) {
           o = row_of(v[u]);
@@ -675,6 +681,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.row_bytes = a->row_bytes;
   s.out_rows = a->out_rows;
   s.miss_counts = a->miss_counts;
+  s.miss_mask = a->miss_mask;
   s.count = reinterpret_cast<int32_t*>(ws + wl.count);
   s.src = reinterpret_cast<int64_t*>(ws + wl.src);
   s.dst = reinterpret_cast<int32_t*>(ws + wl.dst);
@@ -705,17 +712,22 @@ int launch_resolve(Plan& pl, hipStream_t stream) {
 }
 
 int launch_copy(Plan& pl, hipStream_t stream) {
-  MissList l;
+  MissList l{};
   l.count = pl.s.count;
   l.src = pl.s.src;
   l.dst = pl.s.dst;
   l.pool = pl.s.pool;
   l.hot = pl.s.hot;
+  l.pool_layers = nullptr;
+  l.hot_layers = nullptr;
+  l.pool_nrows = pl.s.pool_nrows;
   l.hot_nrows = pl.s.hot_nrows;
   l.row_bytes = pl.s.row_bytes;
   l.B = pl.s.B;
   l.K = pl.s.K;
+  l.layers = 1;
   l.cdiv = pl.s.cdiv;
+  l.ldiv = make_fastdiv(1);
   return launch_swap_copy(l, pl.W, pl.num_cus, stream);
 }
 
@@ -760,4 +772,47 @@ extern "C" int hisparse_gather_compact(const hs_swap_in_args* a, void* workspace
   const int rc = prepare(a, workspace, workspace_bytes, &pl);
   if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
   return launch_copy(pl, stream);
+}
+
+extern "C" int hisparse_gather_compact_layers(const void* workspace, size_t workspace_bytes,
+                                              int32_t B, int32_t K, const uint64_t* pool_layer_ptrs,
+                                              int64_t pool_nrows, const uint64_t* hot_layer_ptrs,
+                                              int64_t hot_nrows, int32_t num_layers,
+                                              int64_t row_bytes, hipStream_t stream) {
+  if (B < 0 || K < 0 || num_layers < 0) return set_error(HS_EINVAL, "B, K and num_layers must be >= 0");
+  if (B == 0 || K == 0 || num_layers == 0) return HS_OK;
+  if (!pool_layer_ptrs || !hot_layer_ptrs) return set_error(HS_EINVAL, "a required pointer is NULL");
+  if (row_bytes <= 0 || (row_bytes & 3) != 0)
+    return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
+  if (row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
+  if (pool_nrows < 0 || hot_nrows < 0) return set_error(HS_EINVAL, "row counts must be >= 0");
+  if (hot_nrows > 0x7fffffffll) return set_error(HS_ERANGE, "hot_nrows exceeds int32 hot-row indices");
+  const int W = (row_bytes & 15) == 0 ? 16 : 4;
+  const int64_t C = row_bytes / W;
+  if (static_cast<int64_t>(K) * num_layers * C >= (1ll << 31))
+    return set_error(HS_ERANGE, "top_k * num_layers * chunks per row exceeds 2^31");
+  const WsLayout wl = ws_layout(B, K);
+  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256))
+    return set_error(HS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned", wl.total);
+  DeviceInfo di;
+  const int rc = device_info(&di);
+  if (rc != HS_OK) return rc;
+  const char* ws = static_cast<const char*>(workspace);
+  MissList l{};
+  l.count = reinterpret_cast<const int32_t*>(ws + wl.count);
+  l.src = reinterpret_cast<const int64_t*>(ws + wl.src);
+  l.dst = reinterpret_cast<const int32_t*>(ws + wl.dst);
+  l.pool = nullptr;
+  l.hot = nullptr;
+  l.pool_layers = pool_layer_ptrs;
+  l.hot_layers = hot_layer_ptrs;
+  l.pool_nrows = pool_nrows;
+  l.hot_nrows = hot_nrows;
+  l.row_bytes = row_bytes;
+  l.B = B;
+  l.K = K;
+  l.layers = num_layers;
+  l.cdiv = make_fastdiv(static_cast<uint32_t>(C));
+  l.ldiv = make_fastdiv(static_cast<uint32_t>(num_layers));
+  return launch_swap_copy(l, W, di.num_cus, stream);
 }

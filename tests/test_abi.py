@@ -154,3 +154,23 @@ def test_fastdiv_is_exact():
         for n in ns:
             if 0 <= n < (1 << 31):
                 assert ((n * m) & ((1 << 64) - 1)) >> s == n // d, (n, d)
+
+
+def test_gather_layers_rejects(lib):
+    f = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.hs_swap_in_workspace_bytes(2, 4)
+    g = lib.hisparse_gather_compact_layers
+    assert g(ws, need, 0, 4, f, 10, f, 10, 3, 16, None) == 0           # empty
+    assert g(ws, need, 2, 4, f, 10, f, 10, 0, 16, None) == 0           # no layers
+    assert g(ws, need, -1, 4, f, 10, f, 10, 3, 16, None) == -1
+    assert g(ws, need, 2, 4, None, 10, f, 10, 3, 16, None) == -1
+    assert g(ws, need, 2, 4, f, 10, f, 10, 3, 18, None) == -1          # row_bytes % 4
+    assert g(ws, need, 2, 4, f, -1, f, 10, 3, 16, None) == -1
+    assert g(ws, need, 2, 4, f, 10, f, 1 << 40, 3, 16, None) == -2     # hot rows beyond int32
+    assert g(ws, need, 2, 4, f, 10, f, 10, 3, 1 << 21, None) == -2
+    assert g(ws, need - 1, 2, 4, f, 10, f, 10, 3, 16, None) == -5
+    assert g(None, need, 2, 4, f, 10, f, 10, 3, 16, None) == -5
+    assert g(ctypes.c_void_p(0x200010), need, 2, 4, f, 10, f, 10, 3, 16, None) == -5
+    assert g(ws, need, 2, 4, f, 10, f, 10, 1 << 20, 1 << 20, None) == -2   # items beyond 2^31
+    assert lib.hisparse_last_error()
