@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kFuseUnroll = 8;             // chunks in flight per lane, fused copy
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
 constexpr uint64_t kEmpty = ~0ull;         // (token -1, index 0xFFFFFFFF): never live
 
@@ -126,7 +127,7 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // independent LDS reads first and then works from registers; the hash is
 // bucketed (four 8-byte entries per 32-byte bucket, at most a quarter full)
 // so a lookup almost always ends after one bucket read.
-template <bool kSlotRows, bool kPoolRows>
+template <bool kSlotRows, bool kPoolRows, int kCopyW>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -461,6 +462,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
   int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
+  // With the copy fused in, the list is also kept in LDS (in the hash area,
+  // free since the probe phase: 8T >= 16K bytes >= 12K).
+  int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
+  int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
   run = miss_before;
   for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
     uint64_t wd[4];
@@ -489,15 +494,20 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const bool missed = ((wd[u] >> lane) & 1ull) && v[u] >= 0 && v[u] < H;
       if (mask) mask[i] = missed ? 1 : 0;
       if ((wd[u] >> lane) & 1ull) {
+        int64_t pr = 0;
         if (v[u] >= 0 && v[u] < H) {
           o = row_of(v[u]);
           tokens[v[u]] = t[u];
-          ws_src[m[u]] = pool_of(t[u]);
+          pr = pool_of(t[u]);
         } else {
           o = -1;
-          ws_src[m[u]] = 0;
         }
+        ws_src[m[u]] = pr;
         ws_dst[m[u]] = o;
+        if constexpr (kCopyW != 0) {
+          l_src[m[u]] = pr;
+          l_dst[m[u]] = o;
+        }
       }
       out[i] = o;
     }
@@ -506,15 +516,51 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     a.count[b] = m_total;
     if (a.miss_counts) a.miss_counts[b] = m_total;
   }
+
+  // ---- 5. (host pools) the request's own row copies -------------------------
+  // The workgroup copies its misses straight from the LDS list, as soon as its
+  // own resolution is done: over the host link a few dozen CUs with every
+  // lane keeping kFuseUnroll chunks in flight already fill the link, and this
+  // saves a second launch and its start-up and drain.
+  if constexpr (kCopyW != 0) {
+    typedef Chunk<kCopyW> CW;
+    __syncthreads();
+    const uint32_t C = a.cdiv.d;
+    const uint32_t total = static_cast<uint32_t>(m_total) * C;
+    for (uint32_t j0 = tid; j0 < total; j0 += kThreads * kFuseUnroll) {
+      typename CW::T cv[kFuseUnroll];
+      char* cd[kFuseUnroll];
+#pragma unroll
+      for (int u = 0; u < kFuseUnroll; ++u) {
+        const uint32_t j = j0 + u * kThreads;
+        cd[u] = nullptr;
+        if (j < total) {
+          const uint32_t mm = fdiv(j, a.cdiv);
+          const uint32_t c = j - mm * C;
+          const int64_t sr = l_src[mm];
+          const int32_t hr = l_dst[mm];
+          if (sr >= 0 && sr < a.pool_nrows && hr >= 0 && hr < a.hot_nrows) {
+            const int64_t off = static_cast<int64_t>(c) * kCopyW;
+            cv[u] = CW::load(a.pool + sr * a.row_bytes + off);
+            cd[u] = a.hot + static_cast<int64_t>(hr) * a.row_bytes + off;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kFuseUnroll; ++u)
+        if (cd[u]) CW::store(cd[u], cv[u]);
+    }
+  }
 }
 
 // Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
-// (pool row, hot row) and its length to the workspace for the copy kernel.
-template <bool kSlotRows, bool kPoolRows>
+// (pool row, hot row) and its length to the workspace for the copy kernel;
+// with kCopyW != 0 also copies the rows itself (W-byte chunks).
+template <bool kSlotRows, bool kPoolRows, int kCopyW>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0);
-  resolve<kSlotRows, kPoolRows>(a, blockIdx.x, lds, lay);
+  resolve<kSlotRows, kPoolRows, kCopyW>(a, blockIdx.x, lds, lay);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -568,10 +614,25 @@ int allow_lds(int device, const void* fn, uint32_t bytes) {
   return HS_OK;
 }
 
+// The resolve kernel for the given tables and fused copy width (0 = none).
+template <int kW>
+const void* pick_resolve(bool slot_rows, bool pool_rows) {
+  if (slot_rows)
+    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW>)
+                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW>);
+  return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true, kW>)
+                   : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW>);
+}
+
+#ifndef HS_FUSE_HOST_COPY
+#define HS_FUSE_HOST_COPY 1
+#endif
+
 // Everything a launch needs, validated once per call.
 struct Plan {
   SwapArgs s;
-  const void* resolve_fn;
+  const void* resolve_fn;   // resolution only
+  const void* fused_fn;     // resolution + the request's own copies, or null
   LdsLayout lay;
   int W;
   int64_t C;
@@ -636,11 +697,8 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   const bool stage = plans_stage[plan];
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
-  const void* resolve_fn =
-      a->slot_rows ? (a->pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true>)
-                                   : reinterpret_cast<const void*>(&resolve_kernel<true, false>))
-                   : (a->pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true>)
-                                   : reinterpret_cast<const void*>(&resolve_kernel<false, false>));
+  const bool sr = a->slot_rows != nullptr, prw = a->pool_rows != nullptr;
+  const void* resolve_fn = pick_resolve<0>(sr, prw);
   if (lay.total > 65536) {
     rc = allow_lds(di.device, resolve_fn, lay.total);
     if (rc != HS_OK) return rc;
@@ -660,6 +718,17 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     pool_dev = static_cast<const char*>(attr.devicePointer ? attr.devicePointer : a->pool);
   } else {
     return set_error(HS_EMEMKIND, "pool must be device memory or pinned host memory");
+  }
+  // Over the host link each request's workgroup copies its own misses (the
+  // link, not the CU count, bounds the copy); an HBM pool gets the wide copy
+  // kernel, which spreads every request over many CUs.
+  const void* fused_fn = nullptr;
+  if (HS_FUSE_HOST_COPY && attr.type == hipMemoryTypeHost) {
+    fused_fn = W == 16 ? pick_resolve<16>(sr, prw) : pick_resolve<4>(sr, prw);
+    if (lay.total > 65536) {
+      rc = allow_lds(di.device, fused_fn, lay.total);
+      if (rc != HS_OK) return rc;
+    }
   }
 
   char* ws = static_cast<char*>(workspace);
@@ -696,6 +765,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
 
   pl->resolve_fn = resolve_fn;
+  pl->fused_fn = fused_fn;
   pl->lay = lay;
   pl->W = W;
   pl->C = C;
@@ -703,9 +773,9 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   return HS_OK;
 }
 
-int launch_resolve(Plan& pl, hipStream_t stream) {
+int launch_resolve(Plan& pl, const void* fn, hipStream_t stream) {
   void* params[] = {&pl.s};
-  hipError_t e = hipLaunchKernel(pl.resolve_fn, dim3(pl.s.B), dim3(kThreads), params, pl.lay.total, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(pl.s.B), dim3(kThreads), params, pl.lay.total, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "resolve launch: %s", hipGetErrorString(e));
   return HS_OK;
@@ -753,7 +823,8 @@ extern "C" int hisparse_swap_in(const hs_swap_in_args* a, void* workspace, size_
   Plan pl;
   const int rc = prepare(a, workspace, workspace_bytes, &pl);
   if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
-  const int r1 = launch_resolve(pl, stream);
+  if (pl.fused_fn) return launch_resolve(pl, pl.fused_fn, stream);
+  const int r1 = launch_resolve(pl, pl.resolve_fn, stream);
   if (r1 != HS_OK) return r1;
   return launch_copy(pl, stream);
 }
@@ -763,7 +834,7 @@ extern "C" int hisparse_resolve(const hs_swap_in_args* a, void* workspace, size_
   Plan pl;
   const int rc = prepare(a, workspace, workspace_bytes, &pl);
   if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
-  return launch_resolve(pl, stream);
+  return launch_resolve(pl, pl.resolve_fn, stream);
 }
 
 extern "C" int hisparse_gather_compact(const hs_swap_in_args* a, void* workspace,
