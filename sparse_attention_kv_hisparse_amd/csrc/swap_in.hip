@@ -36,7 +36,6 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kFuseUnroll = 8;             // chunks in flight per lane, fused copy
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
-constexpr uint64_t kEmpty = ~0ull;         // (token -1, index 0xFFFFFFFF): never live
 
 // Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by
 // floor(2^32 / golden ratio) = 2654435761 and keep the TOP bits of the 32-bit
@@ -79,7 +78,7 @@ struct SwapArgs {
 };
 
 struct LdsLayout {
-  uint32_t hash, out, topk, lru, tok, victim, hitpos, missw, wtot, dummy, total;
+  uint32_t hash, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
@@ -97,6 +96,7 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   // every region starts on a 16-byte boundary
   uint32_t o = 0;
   l.hash = o;   o = align_up(o + 8 * T, 16);                  // later: miss list
+  l.bcnt = o;   o = align_up(o + T, 16);                      // one count per 4-entry bucket
   l.out = o;    o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.topk = o;   o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
@@ -105,6 +105,7 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.wtot = o;   o = align_up(o + 4 * 3 * kWaves + 16, 16);
   l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
+  l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
   l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
   l.total = o;
   return l;
@@ -124,18 +125,23 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // outstanding stores (vmcnt counts both) ever stalls a phase.
 //
 // LDS latency is ~230 cycles on gfx950, so every phase issues all of its
-// independent LDS reads first and then works from registers; the hash is
-// bucketed (four 8-byte entries per 32-byte bucket, at most a quarter full)
-// so a lookup almost always ends after one bucket read.
+// independent LDS reads first and then works from registers. The hash is
+// bucketed: four 8-byte entries per 32-byte bucket plus a per-bucket count,
+// at most a quarter full, so an insert is almost always one atomicAdd and a
+// lookup one bucket read.
 template <bool kSlotRows, bool kPoolRows, int kCopyW>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // Wave-uniform, and held in a scalar register so that every segment bound
+  // derived from it compiles to scalar branches instead of exec masking.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int32_t K = a.K, H = a.H;
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
   uint64_t* hash = reinterpret_cast<uint64_t*>(lds + lay.hash);
+  uint32_t* bcnt = reinterpret_cast<uint32_t*>(lds + lay.bcnt);
+  int16_t* nlru = reinterpret_cast<int16_t*>(lds + lay.nlru);
   int32_t* s_out = reinterpret_cast<int32_t*>(lds + lay.out);
   int32_t* s_topk = reinterpret_cast<int32_t*>(lds + lay.topk);
   int32_t* s_tok = reinterpret_cast<int32_t*>(lds + lay.tok);
@@ -151,6 +157,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // query can be issued unconditionally and all are in flight together.
   unsigned long long* sink64 = reinterpret_cast<unsigned long long*>(lds + lay.dummy) + tid;
   int32_t* sink32 = reinterpret_cast<int32_t*>(sink64);
+  uint32_t* sinku = reinterpret_cast<uint32_t*>(sink64);
   const uint32_t bmask = a.T / 4 - 1;       // buckets - 1
   const uint32_t bshift = a.shift + 2;      // top log2(buckets) bits
   const int32_t* ids = a.topk + static_cast<int64_t>(b) * a.topk_stride;
@@ -197,8 +204,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
-    u64x2* h2 = reinterpret_cast<u64x2*>(hash);
-    for (uint32_t i = tid; i < a.T / 2; i += kThreads) h2[i] = u64x2{kEmpty, kEmpty};
+    // Only the bucket counts need clearing: entries past a bucket's count are
+    // never read as keys.
+    u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+    for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
     if (tid == 0) *s_pending = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -264,25 +273,22 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     int npend = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) npend += __popcll(__ballot(ins[u]));
-    // Linear probing in entry order from the first entry of the home bucket
-    // (a lookup reads whole buckets and stops at one with a free entry, which
-    // this order guarantees to be past the key). K < T, so it terminates.
-    uint32_t e[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) e[u] = 4 * bk[u];
-    const uint32_t emask = a.T - 1;
+    // Each pending id takes the next entry of its home bucket with one LDS
+    // atomicAdd on the bucket's count; a full bucket passes it on to the next
+    // bucket (linear probing over buckets). A lookup stops at the first bucket
+    // that is not full, which this order guarantees to be past the key; the
+    // table is at most half full, so insertion terminates.
+    const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
     while (__ballot(ins[0] | ins[1] | ins[2] | ins[3]) != 0) {
-      unsigned long long prev[4];
+      uint32_t p[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        prev[u] = atomicCAS(ins[u] ? reinterpret_cast<unsigned long long*>(hash + e[u]) : sink64,
-                            static_cast<unsigned long long>(kEmpty),
-                            static_cast<unsigned long long>(ent[u]));
+      for (int u = 0; u < 4; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool taken = prev[u] != kEmpty;
-        e[u] = (ins[u] && taken) ? ((e[u] + 1) & emask) : e[u];
-        ins[u] = ins[u] && taken;
+        if (ins[u] && p[u] < 4) hash[4 * bk[u] + p[u]] = ent[u];
+        const bool full = ins[u] && p[u] >= 4;
+        bk[u] = full ? ((bk[u] + 1) & bmask) : bk[u];
+        ins[u] = full;
       }
     }
 #pragma unroll
@@ -322,27 +328,31 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       bk[u] = bucket_of(key[u], bshift);
       idx[u] = -1;
     }
-    // Branch-free lookup step over one bucket per query; ends when no lane of
-    // the wave is still searching (a bucket with an empty entry ends a miss).
+    // Branch-free lookup step over one bucket per query: the bucket's count
+    // and its four entries are read together, entries past the count are
+    // ignored. Ends when no lane of the wave is still searching (a bucket that
+    // is not full ends a miss).
     while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
       u64x2 lo[4], hi[4];
+      uint32_t cn[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u64x2* bp = reinterpret_cast<const u64x2*>(hash + 4 * bk[u]);
         lo[u] = bp[0];
         hi[u] = bp[1];
+        cn[u] = bcnt[bk[u]];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int32_t kk = key[u];
-        const bool m0 = static_cast<int32_t>(static_cast<uint32_t>(lo[u].x)) == kk;
-        const bool m1 = static_cast<int32_t>(static_cast<uint32_t>(lo[u].y)) == kk;
-        const bool m2 = static_cast<int32_t>(static_cast<uint32_t>(hi[u].x)) == kk;
-        const bool m3 = static_cast<int32_t>(static_cast<uint32_t>(hi[u].y)) == kk;
+        const uint32_t c = cn[u];
+        const bool m0 = c > 0 && static_cast<int32_t>(static_cast<uint32_t>(lo[u].x)) == kk;
+        const bool m1 = c > 1 && static_cast<int32_t>(static_cast<uint32_t>(lo[u].y)) == kk;
+        const bool m2 = c > 2 && static_cast<int32_t>(static_cast<uint32_t>(hi[u].x)) == kk;
+        const bool m3 = c > 3 && static_cast<int32_t>(static_cast<uint32_t>(hi[u].y)) == kk;
         const uint64_t e = m0 ? lo[u].x : m1 ? lo[u].y : m2 ? hi[u].x : hi[u].y;
         const bool found = m0 | m1 | m2 | m3;
-        const bool open = lo[u].x == kEmpty || lo[u].y == kEmpty || hi[u].x == kEmpty ||
-                          hi[u].y == kEmpty;
+        const bool open = c < 4;
         idx[u] = (act[u] && found) ? static_cast<int>(e >> 32) : idx[u];
         act[u] = act[u] && !found && !open;
         bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
@@ -416,7 +426,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
             np = e - M;
           }
         }
-        lru[np] = sp[u];
+        nlru[np] = sp[u];
       }
       run += __popcll(wd[u]);
     }
@@ -512,6 +522,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       out[i] = o;
     }
   }
+  // The new LRU order, built in LDS by phase 3, goes out in one coalesced pass.
+  for (int p = tid; p < H; p += kThreads) lru[p] = nlru[p];
   if (tid == 0) {
     a.count[b] = m_total;
     if (a.miss_counts) a.miss_counts[b] = m_total;
