@@ -78,7 +78,7 @@ struct SwapArgs {
 };
 
 struct LdsLayout {
-  uint32_t hash, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, total;
+  uint32_t hash, hidx, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
@@ -95,8 +95,9 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   LdsLayout l;
   // every region starts on a 16-byte boundary
   uint32_t o = 0;
-  l.hash = o;   o = align_up(o + 8 * T, 16);                  // later: miss list
-  l.bcnt = o;   o = align_up(o + T, 16);                      // one count per 4-entry bucket
+  l.hash = o;   o = align_up(o + 4 * T, 16);                  // keys; later: miss list
+  l.hidx = o;   o = align_up(o + 2 * T, 16);                  // top-k index of each key
+  l.bcnt = o;   o = align_up(o + T, 16);                      // one count per 4-key bucket
   l.out = o;    o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.topk = o;   o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
@@ -126,9 +127,9 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 //
 // LDS latency is ~230 cycles on gfx950, so every phase issues all of its
 // independent LDS reads first and then works from registers. The hash is
-// bucketed: four 8-byte entries per 32-byte bucket plus a per-bucket count,
-// at most a quarter full, so an insert is almost always one atomicAdd and a
-// lookup one bucket read.
+// bucketed: four int32 keys per 16-byte bucket, a parallel int16 array with
+// each key's top-k index and a per-bucket count, at most a quarter full, so
+// an insert is almost always one atomicAdd and a lookup one 16-byte read.
 template <bool kSlotRows, bool kPoolRows, int kCopyW>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
@@ -139,7 +140,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   const int32_t K = a.K, H = a.H;
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
-  uint64_t* hash = reinterpret_cast<uint64_t*>(lds + lay.hash);
+  int32_t* hkey = reinterpret_cast<int32_t*>(lds + lay.hash);
+  int16_t* hidx = reinterpret_cast<int16_t*>(lds + lay.hidx);
   uint32_t* bcnt = reinterpret_cast<uint32_t*>(lds + lay.bcnt);
   int16_t* nlru = reinterpret_cast<int16_t*>(lds + lay.nlru);
   int32_t* s_out = reinterpret_cast<int32_t*>(lds + lay.out);
@@ -204,8 +206,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
-    // Only the bucket counts need clearing: entries past a bucket's count are
-    // never read as keys.
+    // Keys start empty (-1, never a token id) and bucket counts at 0.
+    u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
+    for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
     u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
     for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
     if (tid == 0) *s_pending = 0;
@@ -248,7 +251,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   for (int base = 0; base < K; base += 4 * kThreads) {
     int32_t t[4], o[4];
     uint32_t bk[4];
-    uint64_t ent[4];
     bool ins[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -267,7 +269,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const bool newest = valid && static_cast<int64_t>(t[u]) == L - 1;
       ins[u] = valid && !newest;
       o[u] = !valid ? -1 : (newest ? row_of(H) : kPending);
-      ent[u] = (static_cast<uint64_t>(static_cast<uint32_t>(i)) << 32) | static_cast<uint32_t>(t[u]);
       bk[u] = bucket_of(t[u], bshift);
     }
     int npend = 0;
@@ -285,7 +286,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       for (int u = 0; u < 4; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (ins[u] && p[u] < 4) hash[4 * bk[u] + p[u]] = ent[u];
+        if (ins[u] && p[u] < 4) {
+          hkey[4 * bk[u] + p[u]] = t[u];
+          hidx[4 * bk[u] + p[u]] = static_cast<int16_t>(base + u * kThreads + tid);
+        }
         const bool full = ins[u] && p[u] >= 4;
         bk[u] = full ? ((bk[u] + 1) & bmask) : bk[u];
         ins[u] = full;
@@ -328,35 +332,34 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       bk[u] = bucket_of(key[u], bshift);
       idx[u] = -1;
     }
-    // Branch-free lookup step over one bucket per query: the bucket's count
-    // and its four entries are read together, entries past the count are
-    // ignored. Ends when no lane of the wave is still searching (a bucket that
-    // is not full ends a miss).
+    // Branch-free lookup step over one bucket (four keys, 16 bytes) per
+    // query. Buckets fill in entry order, so a bucket whose last key is empty
+    // is not full and ends a miss. Ends when no lane of the wave is still
+    // searching; the top-k index of each found key is read once afterwards.
+    int pos[4] = {-1, -1, -1, -1};
     while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
-      u64x2 lo[4], hi[4];
-      uint32_t cn[4];
+      u32x4 kv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u64x2* bp = reinterpret_cast<const u64x2*>(hash + 4 * bk[u]);
-        lo[u] = bp[0];
-        hi[u] = bp[1];
-        cn[u] = bcnt[bk[u]];
-      }
+      for (int u = 0; u < 4; ++u) kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int32_t kk = key[u];
-        const uint32_t c = cn[u];
-        const bool m0 = c > 0 && static_cast<int32_t>(static_cast<uint32_t>(lo[u].x)) == kk;
-        const bool m1 = c > 1 && static_cast<int32_t>(static_cast<uint32_t>(lo[u].y)) == kk;
-        const bool m2 = c > 2 && static_cast<int32_t>(static_cast<uint32_t>(hi[u].x)) == kk;
-        const bool m3 = c > 3 && static_cast<int32_t>(static_cast<uint32_t>(hi[u].y)) == kk;
-        const uint64_t e = m0 ? lo[u].x : m1 ? lo[u].y : m2 ? hi[u].x : hi[u].y;
+        const bool m0 = static_cast<int32_t>(kv[u].x) == kk;
+        const bool m1 = static_cast<int32_t>(kv[u].y) == kk;
+        const bool m2 = static_cast<int32_t>(kv[u].z) == kk;
+        const bool m3 = static_cast<int32_t>(kv[u].w) == kk;
         const bool found = m0 | m1 | m2 | m3;
-        const bool open = c < 4;
-        idx[u] = (act[u] && found) ? static_cast<int>(e >> 32) : idx[u];
+        const int j = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : 3));
+        const bool open = static_cast<int32_t>(kv[u].w) == -1;
+        pos[u] = (act[u] && found) ? static_cast<int>(4 * bk[u]) + j : pos[u];
         act[u] = act[u] && !found && !open;
         bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
       }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int16_t ii = hidx[pos[u] >= 0 ? pos[u] : 0];
+      idx[u] = pos[u] >= 0 ? static_cast<int>(ii) : -1;
     }
     int32_t prev[4];
 #pragma unroll
@@ -472,8 +475,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
   int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
-  // With the copy fused in, the list is also kept in LDS (in the hash area,
-  // free since the probe phase: 8T >= 16K bytes >= 12K).
+  // With the copy fused in, the list is also kept in LDS (in the key and
+  // index arrays, free since the probe phase: 6T >= 12K bytes).
   int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
   int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
   run = miss_before;
