@@ -73,6 +73,7 @@ class _SwapArgs(ctypes.Structure):
         ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
         ("miss_mask", ctypes.c_void_p), ("list_count", ctypes.c_void_p),
         ("list_src", ctypes.c_void_p), ("list_dst", ctypes.c_void_p),
+        ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
     ]
 
 
@@ -102,6 +103,16 @@ def _load(path: Optional[str] = None):
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_int64]
         lib.oracle_gather_compact_layers.restype = ctypes.c_int64
+        lib.oracle_transfer_kv_all_layer.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_int64]
+        lib.oracle_transfer_kv_all_layer.restype = ctypes.c_int64
+        lib.oracle_store_kv_cache.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_store_kv_cache.restype = ctypes.c_int64
         _lib = lib
     return _lib
 
@@ -141,14 +152,20 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
             slot_tokens: np.ndarray, lru: np.ndarray, pool: np.ndarray, hot: np.ndarray,
             ctx_stride: int, num_real: int = -1, slot_rows: Optional[np.ndarray] = None,
             pool_rows: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None,
-            miss_counts: Optional[np.ndarray] = None, plan: bool = False):
+            miss_counts: Optional[np.ndarray] = None, plan: bool = False,
+            pool_v: Optional[np.ndarray] = None, hot_v: Optional[np.ndarray] = None):
     """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``,
     and with ``plan=True`` a third item: the plan index-sharing layers replay,
     ``{"miss_mask": int32[B,K], "count": int32[B], "src": int64[B,K], "dst": int32[B,K]}``
     (the compact miss list in miss order; entries past ``count[b]`` are unspecified).
 
     ``pool`` and ``hot`` are ``uint8[nrows, row_bytes]``. State arrays are updated in place.
+    ``pool_v``/``hot_v`` (non-MLA caches, both or neither) have the same shapes as
+    ``pool``/``hot``; every miss copies its V row too.
     """
+    assert (pool_v is None) == (hot_v is None)
+    if pool_v is not None:
+        assert pool_v.shape == pool.shape and hot_v.shape == hot.shape
     B, K = topk.shape
     R, S_r = slot_tokens.shape
     H = lru.shape[1]
@@ -175,7 +192,8 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
         out_rows=_ptr(out_rows, np.int32, True), miss_counts=_ptr(miss_counts, np.int32, True),
         miss_mask=p and _ptr(p["miss_mask"], np.int32, True),
         list_count=p and _ptr(p["count"], np.int32, True),
-        list_src=p and _ptr(p["src"], np.int64, True), list_dst=p and _ptr(p["dst"], np.int32, True))
+        list_src=p and _ptr(p["src"], np.int64, True), list_dst=p and _ptr(p["dst"], np.int32, True),
+        pool_v=_ptr(pool_v, np.uint8), hot_v=_ptr(hot_v, np.uint8, True))
     rc = _load().oracle_swap_in(ctypes.byref(a))
     if rc != ORACLE_OK:
         raise OracleError(rc)
@@ -218,6 +236,46 @@ def transfer_rows_all_layer(src_layers: Sequence[np.ndarray], dst_layers: Sequen
     r = _load().oracle_transfer_rows_all_layer(
         sp, dp, src_layers[0].shape[0], dst_layers[0].shape[0], _ptr(src_idx, np.int64),
         _ptr(dst_idx, np.int64), src_idx.shape[0], L, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
+
+
+def transfer_kv_all_layer(k_src: Sequence[np.ndarray], v_src: Sequence[np.ndarray],
+                          k_dst: Sequence[np.ndarray], v_dst: Sequence[np.ndarray],
+                          src_idx: np.ndarray, dst_idx: np.ndarray) -> int:
+    """K and V rows of every layer: ``k_dst[l][dst_idx[i]] = k_src[l][src_idx[i]]`` and the
+    same for V; returns the pairs skipped."""
+    L = len(k_src)
+    assert len(v_src) == len(k_dst) == len(v_dst) == L and L > 0
+    rb = k_src[0].shape[1]
+    for x in list(k_src) + list(v_src):
+        assert x.shape == k_src[0].shape
+    for x in list(k_dst) + list(v_dst):
+        assert x.shape == k_dst[0].shape and x.shape[1] == rb
+    arr = lambda xs, w: (ctypes.c_void_p * L)(*[_ptr(x, np.uint8, w) for x in xs])
+    r = _load().oracle_transfer_kv_all_layer(
+        arr(k_src, False), arr(v_src, False), arr(k_dst, True), arr(v_dst, True),
+        k_src[0].shape[0], k_dst[0].shape[0], _ptr(src_idx, np.int64), _ptr(dst_idx, np.int64),
+        src_idx.shape[0], L, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
+
+
+def store_kv_cache(k_src: np.ndarray, v_src: np.ndarray, k_dst: np.ndarray, v_dst: np.ndarray,
+                   loc: np.ndarray) -> int:
+    """``k_dst[loc[j]] = k_src[j]`` and ``v_dst[loc[j]] = v_src[j]`` over rows of
+    ``k_src.shape[1]`` bytes (row strides may differ per array); returns rows skipped."""
+    n, rb = k_src.shape
+    assert v_src.shape == (n, rb) and k_dst.shape[0] == v_dst.shape[0]
+    assert k_dst.shape[1] >= rb and v_dst.shape[1] >= rb
+    for x in (k_src, v_src, k_dst, v_dst):
+        assert x.strides[1] == 1
+    r = _load().oracle_store_kv_cache(
+        k_src.ctypes.data, k_src.strides[0], v_src.ctypes.data, v_src.strides[0],
+        k_dst.ctypes.data, k_dst.strides[0], v_dst.ctypes.data, v_dst.strides[0], k_dst.shape[0],
+        _ptr(loc, np.int64), n, rb)
     if r < 0:
         raise OracleError(int(r))
     return int(r)

@@ -64,6 +64,7 @@ static int check_args(const oracle_swap_in_args *a) {
       a->ctx_stride <= 0)
     return ORACLE_EARG;
   if (a->list_count && (!a->list_src || !a->list_dst)) return ORACLE_EARG;
+  if ((a->pool_v == NULL) != (a->hot_v == NULL)) return ORACLE_EARG;
   return ORACLE_OK;
 }
 
@@ -185,6 +186,10 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
       out[pending[j].index] = (int32_t)dst;
       tokens[v] = pending[j].token;
       memcpy(a->hot + dst * a->row_bytes, a->pool + src * a->row_bytes, (size_t)a->row_bytes);
+      /* Non-MLA caches: the V row travels with the K row (SGLang page,
+       * !IsMLA branch of the miss copy: same source and destination rows). */
+      if (a->pool_v)
+        memcpy(a->hot_v + dst * a->row_bytes, a->pool_v + src * a->row_bytes, (size_t)a->row_bytes);
       /* The plan (vLLM page: miss_mask, and the compact swap lists in miss
        * order) that index-sharing layers replay. */
       if (mask) mask[pending[j].index] = 1;
@@ -259,6 +264,48 @@ int64_t oracle_transfer_rows_all_layer(const uint8_t *const *src_layers, uint8_t
     if (s < 0 || s >= src_nrows || d < 0 || d >= dst_nrows) { ++skipped; continue; }
     for (int32_t l = 0; l < num_layers; ++l)
       memcpy(dst_layers[l] + d * row_bytes, src_layers[l] + s * row_bytes, (size_t)row_bytes);
+  }
+  return skipped;
+}
+
+int64_t oracle_transfer_kv_all_layer(const uint8_t *const *k_src_layers,
+                                     const uint8_t *const *v_src_layers,
+                                     uint8_t *const *k_dst_layers, uint8_t *const *v_dst_layers,
+                                     int64_t src_nrows, int64_t dst_nrows, const int64_t *src_idx,
+                                     const int64_t *dst_idx, int64_t n, int32_t num_layers,
+                                     int64_t row_bytes) {
+  if (n < 0 || num_layers < 0 || row_bytes <= 0) return ORACLE_EARG;
+  if (n == 0 || num_layers == 0) return 0;
+  if (!k_src_layers || !v_src_layers || !k_dst_layers || !v_dst_layers || !src_idx || !dst_idx)
+    return ORACLE_EARG;
+  int64_t skipped = 0;
+  /* tokenspeed page, all-layer K+V transfer: for every index pair, for every
+   * layer, the K row and then the V row. */
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t s = src_idx[i], d = dst_idx[i];
+    if (s < 0 || s >= src_nrows || d < 0 || d >= dst_nrows) { ++skipped; continue; }
+    for (int32_t l = 0; l < num_layers; ++l) {
+      memcpy(k_dst_layers[l] + d * row_bytes, k_src_layers[l] + s * row_bytes, (size_t)row_bytes);
+      memcpy(v_dst_layers[l] + d * row_bytes, v_src_layers[l] + s * row_bytes, (size_t)row_bytes);
+    }
+  }
+  return skipped;
+}
+
+int64_t oracle_store_kv_cache(const uint8_t *k_src, int64_t k_src_stride, const uint8_t *v_src,
+                              int64_t v_src_stride, uint8_t *k_dst, int64_t k_dst_stride,
+                              uint8_t *v_dst, int64_t v_dst_stride, int64_t dst_nrows,
+                              const int64_t *loc, int64_t n, int64_t row_bytes) {
+  if (n < 0 || row_bytes <= 0) return ORACLE_EARG;
+  if (n == 0) return 0;
+  if (!k_src || !v_src || !k_dst || !v_dst || !loc) return ORACLE_EARG;
+  int64_t skipped = 0;
+  /* tokenspeed page, _store_kv_cache_kernel: row j of each source goes to row
+   * loc[j] of its destination. */
+  for (int64_t j = 0; j < n; ++j) {
+    if (loc[j] < 0 || loc[j] >= dst_nrows) { ++skipped; continue; }
+    memcpy(k_dst + loc[j] * k_dst_stride, k_src + j * k_src_stride, (size_t)row_bytes);
+    memcpy(v_dst + loc[j] * v_dst_stride, v_src + j * v_src_stride, (size_t)row_bytes);
   }
   return skipped;
 }

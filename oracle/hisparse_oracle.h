@@ -12,8 +12,8 @@
  *          transfer_cache_dsv4_mla_kernel.
  *   [VLLM] vLLM hisparse_kernels.cu, hisparse_resolve_residency_kernel,
  *          hisparse_gather_compact_kernel, hisparse_gather_plan_kernel.
- *   [TS]   tokenspeed kvcache/triton.py, _store_kv_cache_kernel and
- *          _kv_transfer_all_layer_mla_kernel.
+ *   [TS]   tokenspeed kvcache/triton.py, _store_kv_cache_kernel,
+ *          _kv_transfer_all_layer_mla_kernel and _kv_transfer_all_layer_kernel.
  *
  * All arrays are host memory and row-major. Nothing here is floating point.
  */
@@ -62,6 +62,10 @@ typedef struct {
   int32_t *list_count;      /* [B] or NULL: misses of row b (the compact plan's length) */
   int64_t *list_src;        /* [B, K]: pool row of miss m of row b, m < list_count[b] */
   int32_t *list_dst;        /* [B, K]: hot row of miss m of row b */
+  /* Non-MLA caches ([SGL] !IsMLA): a V pool and V hot buffer with the K
+   * pool's and K hot buffer's geometry; every miss copies its V row too. */
+  const uint8_t *pool_v;    /* [pool_nrows, row_bytes] or NULL */
+  uint8_t *hot_v;           /* [hot_nrows, row_bytes], NULL when pool_v is */
 } oracle_swap_in_args;
 
 /* One decode-step swap-in call. Returns ORACLE_OK or a negative code when a
@@ -88,6 +92,27 @@ int64_t oracle_transfer_rows_all_layer(const uint8_t *const *src_layers, uint8_t
                                        int64_t src_nrows, int64_t dst_nrows,
                                        const int64_t *src_idx, const int64_t *dst_idx, int64_t n,
                                        int32_t num_layers, int64_t row_bytes);
+
+/* The K+V all-layer transfer ([TS] _kv_transfer_all_layer_kernel): for every
+ * index pair i and layer l, the K row src_idx[i] of k_src_layers[l] goes to
+ * row dst_idx[i] of k_dst_layers[l], then the V row likewise. Pairs with an
+ * index outside [0, nrows) are skipped and counted; returns that count, or
+ * ORACLE_EARG. */
+int64_t oracle_transfer_kv_all_layer(const uint8_t *const *k_src_layers,
+                                     const uint8_t *const *v_src_layers,
+                                     uint8_t *const *k_dst_layers, uint8_t *const *v_dst_layers,
+                                     int64_t src_nrows, int64_t dst_nrows, const int64_t *src_idx,
+                                     const int64_t *dst_idx, int64_t n, int32_t num_layers,
+                                     int64_t row_bytes);
+
+/* The K+V scatter ([TS] _store_kv_cache_kernel, both halves): for j < n with
+ * 0 <= loc[j] < dst_nrows, K row j goes to K row loc[j] and V row j to V row
+ * loc[j], each side with its own row stride in bytes. Returns the number of
+ * entries skipped, or ORACLE_EARG. */
+int64_t oracle_store_kv_cache(const uint8_t *k_src, int64_t k_src_stride, const uint8_t *v_src,
+                              int64_t v_src_stride, uint8_t *k_dst, int64_t k_dst_stride,
+                              uint8_t *v_dst, int64_t v_dst_stride, int64_t dst_nrows,
+                              const int64_t *loc, int64_t n, int64_t row_bytes);
 
 /* dst row loc[j] <- src row j for j < n; entries with loc outside
  * [0, dst_nrows) are skipped. Returns the number skipped, or ORACLE_EARG. */

@@ -24,7 +24,8 @@ from typing import Dict, List, Optional
 
 
 def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, ctx_stride,
-                      num_real=-1, slot_rows=None, pool_rows=None, plan=False):
+                      num_real=-1, slot_rows=None, pool_rows=None, plan=False, pool_v=None,
+                      hot_v=None):
     """Same contract as ``oracle.swap_in`` (numpy arrays updated in place). With
     ``plan=True`` also returns the plan: ``miss_mask`` [B,K] (1 for each entry
     whose token no slot held) and, per row, the list of (pool row, hot row)
@@ -78,6 +79,8 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
             cache[v] = None
             slot_tokens[r, v] = t
             hot[row_of(r, v)] = pool[pool_of(r, t)]
+            if pool_v is not None:
+                hot_v[row_of(r, v)] = pool_v[pool_of(r, t)]
             out[b, i] = row_of(r, v)
             mask[b, i] = 1
             copies[b].append((pool_of(r, t), row_of(r, v)))

@@ -29,20 +29,26 @@ def _pool(n, rb):
 
 
 def _run_both(calls, *, R, H, S_r, ctx_stride, rb=8, slot_rows=None, pool_rows=None,
-              hot_nrows=None, pool_nrows=None):
+              hot_nrows=None, pool_nrows=None, kv=False):
     pool = _pool(pool_nrows or R * ctx_stride, rb)
     hot_nrows = hot_nrows or R * S_r
     st_o, lru_o = gen.initial_state(R, H, S_r)
     st_m, lru_m = st_o.copy(), lru_o.copy()
     hot_o = np.zeros((hot_nrows, rb), dtype=np.uint8)
     hot_m = hot_o.copy()
+    pool_v = (255 - pool) if kv else None
+    hv_o = np.zeros_like(hot_o) if kv else None
+    hv_m = np.zeros_like(hot_o) if kv else None
     for c in calls:
         kw = dict(topk=c["topk"], req_rows=c["req_rows"], seq_lens=c["seq_lens"],
                   ctx_stride=ctx_stride, num_real=c.get("num_real", -1), slot_rows=slot_rows,
                   pool_rows=pool_rows, pool=pool)
-        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True, **kw)
+        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True,
+                                              pool_v=pool_v, hot_v=hv_o, **kw)
         out_m, cnt_m, plan_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, plan=True,
-                                                 **kw)
+                                                 pool_v=pool_v, hot_v=hv_m, **kw)
+        if kv:
+            assert np.array_equal(hv_o, hv_m)
         # the plan: which entries missed, and the copies in the order made
         assert plan_o["miss_mask"].tolist() == plan_m["miss_mask"].tolist()
         assert plan_o["count"].tolist() == cnt_m.tolist()
@@ -94,7 +100,7 @@ def test_exhaustive_k3_h4_growing_seq():
 
 
 @pytest.mark.parametrize("seed", range(6))
-def test_random_multirow_with_tables(seed):
+def test_random_multirow_with_tables(seed, kv=False):
     """Random calls over permuted state rows, padding, invalid ids, slot-row and
     pool-row tables."""
     rng = np.random.default_rng(seed)
@@ -108,7 +114,13 @@ def test_random_multirow_with_tables(seed):
         calls.append(dict(topk=topk, req_rows=rows, seq_lens=seq,
                           num_real=int(rng.integers(1, B + 1)) if rng.random() < 0.3 else -1))
     _run_both(calls, R=R, H=H, S_r=S_r, ctx_stride=ctx, slot_rows=slot_rows, pool_rows=pool_rows,
-              hot_nrows=R * S_r + 7, pool_nrows=R * ctx + 9)
+              hot_nrows=R * S_r + 7, pool_nrows=R * ctx + 9, kv=kv)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_multirow_kv(seed):
+    """The same random calls with a V pool: V rows follow the K rows."""
+    test_random_multirow_with_tables(100 + seed, kv=True)
 
 
 def test_tiny_workload_trace_matches_model():

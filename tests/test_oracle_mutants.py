@@ -46,6 +46,11 @@ MUTANTS = {
     "replay_count_clamp_off_by_one": ("if (n > K) n = K;", "if (n > K) n = K - 1;"),
     "replay_no_zero_fill": ("memset(to, 0, (size_t)row_bytes);", ""),
     "replay_row_zero_has_no_source": ("if (s < pool_nrows) {", "if (s > 0 && s < pool_nrows) {"),
+    "kv_swap_v_from_k_pool": ("memcpy(a->hot_v + dst * a->row_bytes, a->pool_v + src * a->row_bytes",
+                              "memcpy(a->hot_v + dst * a->row_bytes, a->pool + src * a->row_bytes"),
+    "kv_swap_v_not_copied": ("      if (a->pool_v)\n        memcpy(a->hot_v", "      if (0)\n        memcpy(a->hot_v"),
+    "kv_transfer_v_from_k": ("v_src_layers[l] + s * row_bytes", "k_src_layers[l] + s * row_bytes"),
+    "kv_scatter_v_k_stride": ("v_src + j * v_src_stride", "v_src + j * k_src_stride"),
     "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
                                       "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }
@@ -57,6 +62,7 @@ def _pins():
     import test_oracle_golden as g
     import test_oracle_model as m
     import test_oracle_plan as pl
+    import test_oracle_kv as kvt
     failed = []
     checks = [
         ("golden1", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_1.json")),
@@ -67,6 +73,9 @@ def _pins():
         ("disjoint", lambda: cf.test_disjoint_step_evicts_oldest(0)),
         ("replay_golden", pl.test_replay_worked_example),
         ("replay_numpy", lambda: pl.test_replay_layers_matches_numpy(1)),
+        ("kv_golden", kvt.test_kv_copies_worked_example),
+        ("kv_swap_golden", lambda: kvt.test_swap_in_v_rows_follow_k_rows("swap_in_worked_example_1.json")),
+        ("kv_model", lambda: m.test_random_multirow_kv(0)),
     ]
     for name, fn in checks:
         try:
