@@ -14,6 +14,8 @@ Also reported in the same JSON line:
   * adversarial: B=64, hot_size 8192, 65,536-token contexts, ids that collide
     in the low-bit multiplicative hash, 1152-byte and 132-byte rows: the cold
     step and the steps after it;
+  * kv_decode: non-MLA caches -- the headline's shape with 1024-byte K and V
+    rows in two pinned pools, every miss moving both;
   * plan_replay: the headline trace with index-sharing layers (1 resolving
     layer + 3 replaying its plan): one fused replay launch for all layers
     against one copy launch per layer;
@@ -56,6 +58,7 @@ def parse():
     p.add_argument("--no-all-layer", action="store_true")
     p.add_argument("--no-adversarial", action="store_true")
     p.add_argument("--no-plan-replay", action="store_true")
+    p.add_argument("--no-kv", action="store_true")
     p.add_argument("--replay-layers", type=int, default=4,
                    help="layers per index-sharing group in the plan-replay leg (1 resolving "
                         "layer + the rest replaying its plan)")
@@ -86,7 +89,7 @@ class Trace:
         self.rows = torch.arange(cfg.B, dtype=torch.int64, device="cuda")
 
 
-def run_gpu(cfg, warmup, steps, torch, hs, wdev):
+def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False):
     """Time K swap-in calls after W warm-up calls.
 
     Pass 1 (the timed region of the contract): W untimed calls, then K plain
@@ -98,11 +101,18 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     kernel's total bracketed by two events and no gaps between launches.
     The first warm-up call is the cold step (every id a miss) and is timed on
     its own with two events.
+    With kv=True the workload has non-MLA caches: a V pool (its own bytes) and
+    a V hot buffer, and every miss moves its K row and its V row.
     Returns dict(us_total, us_resolve, us_copy, us_cold, cold_rows, counts, wall).
     """
-    log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})")
+    log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})"
+        + (" x 2 (K and V)" if kv else ""))
     pool = wdev.make_pool(cfg)
     st = wdev.DeviceSwapState(cfg)
+    kvkw = {}
+    if kv:
+        kvkw = dict(pool_v=wdev.make_pool(cfg.with_(seed=cfg.seed + 777)),
+                    hot_v=torch.zeros_like(st.hot))
     tr = Trace(cfg, warmup + steps, torch)
     counts = torch.empty((warmup + steps, cfg.B), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -110,7 +120,7 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     def call(t, fn, ws):
         fn(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t], slot_tokens=st.slot_tokens,
            lru=st.lru, pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx, workspace=ws,
-           miss_counts=counts[t], stream=stream)
+           miss_counts=counts[t], stream=stream, **kvkw)
 
     def events():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -124,7 +134,7 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev):
     hs.hisparse_swap_in(topk=tr.topk[0], req_rows=tr.rows, seq_lens=tr.seq[0],
                         slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
                         out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws, num_real=pad,
-                        stream=stream)
+                        stream=stream, **kvkw)
     torch.cuda.synchronize()
     c0, c1 = events()
     for t in range(warmup):
@@ -585,6 +595,32 @@ def main():
             if peak else None,
             "GBps_step_fused": round(link_bytes / pr["us_fused"] / 1e3, 2),
             "GBps_step_separate": round(link_bytes / pr["us_separate"] / 1e3, 2),
+        }
+
+    if not args.no_kv:
+        # Non-MLA caches: the headline's shape with 1024-byte K rows and V
+        # rows (e.g. 4 KV heads x 128 dims x 2 bytes) in two pinned pools.
+        kcfg = gen.KV_DECODE
+        n = kcfg.steps - 1
+        kr = run_gpu(kcfg, 1, n, torch, hs, wdev, kv=True)
+        krows = int(kr["counts"].sum())
+        kbytes = krows * kcfg.row_bytes * 2
+        kach = kbytes / kr["us_total"] / 1e3
+        out["kv_decode"] = {
+            "workload": "kv_decode_swap_in_pinned_host_pools", "batch": kcfg.B,
+            "context": kcfg.ctx, "hot_size": kcfg.H, "top_k": kcfg.K,
+            "row_bytes_k": kcfg.row_bytes, "row_bytes_v": kcfg.row_bytes, "steps": n,
+            "rows_per_call": round(krows / n, 1), "us_per_call": round(kr["us_total"] / n, 2),
+            "rows_per_s": round(krows / kr["wall"], 1),
+            "cold_step": {"us": round(kr["us_cold"], 2), "rows": kr["cold_rows"],
+                          "GBps": round(kr["cold_rows"] * kcfg.row_bytes * 2 / kr["us_cold"] / 1e3, 2)},
+            "split_api": {"us_resolve_kernel": round(kr["us_resolve"] / n, 2),
+                          "us_copy_kernel": round(kr["us_copy"] / n, 2)},
+            "roofline": {"bound": "host_link",
+                         "kernel": "resolve_kernel<false, false, 16> (resolution + K and V row copies)",
+                         "achieved": round(kach, 2), "peak": round(peak, 2) if peak else None,
+                         "unit": "GB/s", "frac": round(kach / peak, 4) if peak else None,
+                         "traffic": measured_traffic("kv_decode")},
         }
 
     if not args.no_adversarial:

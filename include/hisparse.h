@@ -16,6 +16,7 @@
  *                                 (plan replay on index-sharing layers), host
  *                                 argument checks.
  *   tokenspeed kvcache/triton.py -- _kv_transfer_all_layer_mla_kernel,
+ *                                 _kv_transfer_all_layer_kernel (K+V),
  *                                 _store_kv_cache_kernel.
  *
  * Conventions for every call:
@@ -102,6 +103,13 @@ typedef struct hs_swap_in_args {
   int32_t* miss_mask;        /* device [B, K] out, or NULL: 1 where the entry    */
                              /* missed and was given a slot (step 3), else 0     */
                              /* (vLLM hisparse_kernels.cu, miss_mask)            */
+
+  /* Non-MLA caches (SGLang hisparse.cuh, !IsMLA): a V pool and a V hot buffer
+   * with the same rows, row_bytes and kind of memory as pool / hot. Each miss
+   * then copies its V row with the same pool row and hot row as its K row.
+   * Both NULL for MLA (one latent row per token). */
+  const void* pool_v;        /* [pool_nrows, row_bytes], or NULL                 */
+  void* hot_v;               /* device [hot_nrows, row_bytes], or NULL           */
 } hs_swap_in_args;
 
 /* Bytes of device workspace hisparse_swap_in needs for B rows of K ids
@@ -236,6 +244,25 @@ int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_
                             int64_t dst_nrows, hipStream_t stream);
 
 /*
+ * transfer_kv_all_layer -- the non-MLA form of transfer_rows_all_layer.
+ * tokenspeed kvcache/triton.py, _kv_transfer_all_layer_kernel.
+ *
+ * For every pair i < n and layer l < num_layers, the K row and the V row:
+ *   k_dst_layer_ptrs[l] + dst_idx[i]*row_bytes  <-  k_src_layer_ptrs[l] + src_idx[i]*row_bytes
+ *   v_dst_layer_ptrs[l] + dst_idx[i]*row_bytes  <-  v_src_layer_ptrs[l] + src_idx[i]*row_bytes
+ * Four device uint64 [num_layers] arrays of layer base addresses; K and V
+ * layers have the same row counts (src_nrows, dst_nrows) and row_bytes.
+ * Everything else (alignment, directions, skipped pairs, index width,
+ * uniqueness, errors) is as for transfer_rows_all_layer; all 2 * num_layers
+ * streams move in one launch.
+ */
+int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs, const uint64_t* v_src_layer_ptrs,
+                          const uint64_t* k_dst_layer_ptrs, const uint64_t* v_dst_layer_ptrs,
+                          const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
+                          int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
+                          int64_t dst_nrows, hipStream_t stream);
+
+/*
  * store_kv_scatter -- write rows into a cache at given row indices.
  * tokenspeed kvcache/triton.py, _store_kv_cache_kernel (one cache, the MLA case).
  *
@@ -248,6 +275,22 @@ int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_
 int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
                      int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
                      int64_t n, int64_t row_bytes, hipStream_t stream);
+
+/*
+ * store_kv_cache -- the K+V form of store_kv_scatter, both halves in one
+ * launch (tokenspeed kvcache/triton.py, _store_kv_cache_kernel).
+ *
+ * For j < n with 0 <= loc[j] < dst_nrows:
+ *   k_dst + loc[j]*k_dst_row_stride_bytes  <-  k_src + j*k_src_row_stride_bytes
+ *   v_dst + loc[j]*v_dst_row_stride_bytes  <-  v_src + j*v_src_row_stride_bytes
+ * (row_bytes bytes each). Each of the four arrays has its own row stride
+ * (bytes, >= row_bytes, multiple of 4); K and V caches have dst_nrows rows.
+ * Skipped entries, loc uniqueness and errors as for store_kv_scatter.
+ */
+int store_kv_cache(const void* k_src, int64_t k_src_row_stride_bytes, const void* v_src,
+                   int64_t v_src_row_stride_bytes, void* k_dst, int64_t k_dst_row_stride_bytes,
+                   void* v_dst, int64_t v_dst_row_stride_bytes, int64_t dst_nrows,
+                   const int64_t* loc, int64_t n, int64_t row_bytes, hipStream_t stream);
 
 /*
  * hisparse_state_reset -- put state rows into the initial state: every entry

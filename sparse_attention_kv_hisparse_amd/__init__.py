@@ -16,7 +16,7 @@ import torch
 from ._lib import EXPORTS, HisparseError, SwapInArgs, check, load
 
 __all__ = ["hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
-           "hisparse_gather_compact_layers",
+           "hisparse_gather_compact_layers", "transfer_kv_all_layer", "store_kv_cache",
            "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
            "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
 
@@ -57,16 +57,27 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                      num_real: Optional[torch.Tensor] = None,
                      slot_rows: Optional[torch.Tensor] = None,
                      pool_rows: Optional[torch.Tensor] = None,
-                     miss_mask: Optional[torch.Tensor] = None, stream=None,
-                     _entry: str = "hisparse_swap_in") -> None:
+                     miss_mask: Optional[torch.Tensor] = None,
+                     pool_v: Optional[torch.Tensor] = None, hot_v: Optional[torch.Tensor] = None,
+                     stream=None, _entry: str = "hisparse_swap_in") -> None:
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
     slot_tokens int32 [R, S_r], lru int16 [R, H], pool uint8 [rows, row_bytes]
     (pinned host or device), hot uint8 [rows, row_bytes] (device), out_rows int32 [B, K],
     workspace uint8 device tensor of at least ``swap_in_workspace_bytes(B, K)`` bytes,
-    miss_mask int32 [B, K] (optional output: 1 where the entry missed and got a slot).
+    miss_mask int32 [B, K] (optional output: 1 where the entry missed and got a slot),
+    pool_v / hot_v (non-MLA caches, both or neither): the V pool and V hot buffer, shaped
+    and placed like pool / hot.
     """
+    if (pool_v is None) != (hot_v is None):
+        raise ValueError("pool_v and hot_v go together")
+    if pool_v is not None:
+        if pool_v.shape != pool.shape or hot_v.shape != hot.shape or pool_v.dtype != torch.uint8 \
+                or hot_v.dtype != torch.uint8 or not pool_v.is_contiguous() or not hot_v.is_contiguous():
+            raise ValueError("pool_v / hot_v must be contiguous uint8 shaped like pool / hot")
+        if not hot_v.is_cuda:
+            raise ValueError("hot_v must be a device tensor")
     B, K = out_rows.shape
     if topk.dim() != 2 or topk.shape[0] != B or topk.shape[1] < K or topk.stride(1) != 1:
         raise ValueError("topk must be [B, >=K] with contiguous columns")
@@ -95,7 +106,9 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         hot=hot.data_ptr(), hot_nrows=hot.shape[0], row_bytes=hot.shape[1],
         out_rows=_dev(out_rows, torch.int32, "out_rows"),
         miss_counts=_opt(miss_counts, torch.int32, "miss_counts"),
-        miss_mask=_opt(miss_mask, torch.int32, "miss_mask"))
+        miss_mask=_opt(miss_mask, torch.int32, "miss_mask"),
+        pool_v=None if pool_v is None else pool_v.data_ptr(),
+        hot_v=None if hot_v is None else hot_v.data_ptr())
     if miss_mask is not None and (tuple(miss_mask.shape) != (B, K) or not miss_mask.is_contiguous()):
         raise ValueError("miss_mask must be a contiguous [B, K] int32 tensor")
     ws = _dev(workspace, torch.uint8, "workspace")
@@ -142,6 +155,43 @@ def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: tor
         _dev(dst_layer_ptrs, torch.int64, "dst_layer_ptrs"),
         _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
         src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, _stream(stream)))
+
+
+def transfer_kv_all_layer(*, k_src_layer_ptrs: torch.Tensor, v_src_layer_ptrs: torch.Tensor,
+                          k_dst_layer_ptrs: torch.Tensor, v_dst_layer_ptrs: torch.Tensor,
+                          src_idx: torch.Tensor, dst_idx: torch.Tensor, row_bytes: int,
+                          src_nrows: int, dst_nrows: int, stream=None) -> None:
+    """K+V all-layer indexed row copy; the four layer pointer arrays are device
+    uint64 (torch int64) [L]."""
+    L = k_src_layer_ptrs.numel()
+    if not (v_src_layer_ptrs.numel() == k_dst_layer_ptrs.numel() == v_dst_layer_ptrs.numel() == L):
+        raise ValueError("layer pointer arrays must have equal lengths")
+    if src_idx.numel() != dst_idx.numel():
+        raise ValueError("index arrays must have equal lengths")
+    check("transfer_kv_all_layer", load().transfer_kv_all_layer(
+        _dev(k_src_layer_ptrs, torch.int64, "k_src_layer_ptrs"),
+        _dev(v_src_layer_ptrs, torch.int64, "v_src_layer_ptrs"),
+        _dev(k_dst_layer_ptrs, torch.int64, "k_dst_layer_ptrs"),
+        _dev(v_dst_layer_ptrs, torch.int64, "v_dst_layer_ptrs"),
+        _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
+        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, _stream(stream)))
+
+
+def store_kv_cache(*, k_src: torch.Tensor, v_src: torch.Tensor, k_dst: torch.Tensor,
+                   v_dst: torch.Tensor, loc: torch.Tensor, row_bytes: int = 0, stream=None) -> None:
+    """``k_dst[loc[j]] = k_src[j]; v_dst[loc[j]] = v_src[j]`` for 2-D uint8 row tensors whose
+    leading axes may be strided."""
+    for t, n in ((k_src, "k_src"), (v_src, "v_src"), (k_dst, "k_dst"), (v_dst, "v_dst")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{n} must be a 2-D uint8 tensor with contiguous rows")
+    if k_dst.shape[0] != v_dst.shape[0] or k_src.shape != v_src.shape:
+        raise ValueError("K and V sides must have matching row counts")
+    rb = row_bytes or k_src.shape[1]
+    check("store_kv_cache", load().store_kv_cache(
+        _dev(k_src, torch.uint8, "k_src"), k_src.stride(0), _dev(v_src, torch.uint8, "v_src"),
+        v_src.stride(0), _dev(k_dst, torch.uint8, "k_dst"), k_dst.stride(0),
+        _dev(v_dst, torch.uint8, "v_dst"), v_dst.stride(0), k_dst.shape[0],
+        _dev(loc, torch.int64, "loc"), loc.numel(), rb, _stream(stream)))
 
 
 def store_kv_scatter(*, src: torch.Tensor, dst: torch.Tensor, loc: torch.Tensor, row_bytes: int = 0,

@@ -19,8 +19,8 @@ STATUS = {0: "HS_OK", -1: "HS_EINVAL", -2: "HS_ERANGE", -3: "HS_EMEMKIND", -4: "
 # Every function include/hisparse.h declares.
 EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_resolve",
            "hisparse_gather_compact", "hisparse_gather_compact_layers",
-           "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
-           "hisparse_state_reset", "hisparse_last_error")
+           "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_kv_all_layer",
+           "store_kv_scatter", "store_kv_cache", "hisparse_state_reset", "hisparse_last_error")
 
 
 class SwapInArgs(ctypes.Structure):
@@ -40,6 +40,7 @@ class SwapInArgs(ctypes.Structure):
         ("row_bytes", ctypes.c_int64),
         ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
         ("miss_mask", ctypes.c_void_p),
+        ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
     ]
 
 
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.transfer_rows_all_layer.restype = ctypes.c_int
     lib.store_kv_scatter.argtypes = [vp, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.store_kv_scatter.restype = ctypes.c_int
+    lib.transfer_kv_all_layer.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
+    lib.transfer_kv_all_layer.restype = ctypes.c_int
+    lib.store_kv_cache.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64, i64, vp]
+    lib.store_kv_cache.restype = ctypes.c_int
     lib.hisparse_state_reset.argtypes = [vp, vp, vp, i64, i32, i64, i64, vp]
     lib.hisparse_state_reset.restype = ctypes.c_int
     lib.hisparse_last_error.argtypes = []

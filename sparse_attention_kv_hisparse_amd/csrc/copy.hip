@@ -2,7 +2,10 @@
 //   transfer_rows_all_layer -- tokenspeed kvcache/triton.py,
 //     _kv_transfer_all_layer_mla_kernel; SGLang hisparse.cuh,
 //     transfer_cache_dsv4_mla_kernel (generic row layout);
-//   store_kv_scatter -- tokenspeed kvcache/triton.py, _store_kv_cache_kernel;
+//   transfer_kv_all_layer -- tokenspeed, _kv_transfer_all_layer_kernel (K and
+//     V caches of every layer);
+//   store_kv_scatter / store_kv_cache -- tokenspeed, _store_kv_cache_kernel
+//     (K half / both halves);
 //   hisparse_state_reset -- initial per-request state.
 //
 // Work is one flat stream of (pair, layer, chunk) items rather than one warp
@@ -21,20 +24,31 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kMaxStagedLayers = 256;
 
+// Layer bases: streams [0, lk) come from the K arrays, [lk, num_layers) from
+// the V arrays (null for MLA, where num_layers == lk).
+struct LayerPtrs {
+  const uint64_t* src_k;
+  const uint64_t* dst_k;
+  const uint64_t* src_v;
+  const uint64_t* dst_v;
+  int32_t lk;
+};
+
 template <int W>
 __global__ __launch_bounds__(kThreads) void transfer_kernel(
-    const uint64_t* __restrict__ src_layers, const uint64_t* __restrict__ dst_layers,
-    const int64_t* __restrict__ src_idx, const int64_t* __restrict__ dst_idx, uint32_t total,
-    int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows, FastDiv cdiv,
-    FastDiv ldiv) {
+    LayerPtrs lp, const int64_t* __restrict__ src_idx, const int64_t* __restrict__ dst_idx,
+    uint32_t total, int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
+    FastDiv cdiv, FastDiv ldiv) {
   typedef Chunk<W> C;
   __shared__ uint64_t s_src[kMaxStagedLayers];
   __shared__ uint64_t s_dst[kMaxStagedLayers];
   const bool staged = num_layers <= kMaxStagedLayers;
+  auto src_base = [&](int l) { return l < lp.lk ? lp.src_k[l] : lp.src_v[l - lp.lk]; };
+  auto dst_base = [&](int l) { return l < lp.lk ? lp.dst_k[l] : lp.dst_v[l - lp.lk]; };
   if (staged) {
     for (int l = threadIdx.x; l < num_layers; l += kThreads) {
-      s_src[l] = src_layers[l];
-      s_dst[l] = dst_layers[l];
+      s_src[l] = src_base(l);
+      s_dst[l] = dst_base(l);
     }
     __syncthreads();
   }
@@ -53,8 +67,8 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
         const uint32_t l = row - i * ldiv.d;        // layer
         const int64_t si = src_idx[i], di = dst_idx[i];
         if (si >= 0 && si < src_nrows && di >= 0 && di < dst_nrows) {
-          const uint64_t sb = staged ? s_src[l] : src_layers[l];
-          const uint64_t db = staged ? s_dst[l] : dst_layers[l];
+          const uint64_t sb = staged ? s_src[l] : src_base(static_cast<int>(l));
+          const uint64_t db = staged ? s_dst[l] : dst_base(static_cast<int>(l));
           const int64_t off = static_cast<int64_t>(c) * W;
           const char* sp = reinterpret_cast<const char*>(sb) + si * row_bytes + off;
           char* dp = reinterpret_cast<char*>(db) + di * row_bytes + off;
@@ -75,33 +89,48 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
   }
 }
 
+// One scatter stream: rows of a source (leading-axis stride in bytes) go to
+// the destination rows loc[j].
+struct ScatterSide {
+  const char* src;
+  int64_t src_stride;
+  char* dst;
+  int64_t dst_stride;
+};
+
+// Items are (entry, stream, chunk) with the chunk fastest; with a V side each
+// entry has two streams, K then V (tokenspeed _store_kv_cache_kernel moves
+// both halves in one launch).
 template <int W>
-__global__ __launch_bounds__(kThreads) void scatter_kernel(
-    const char* __restrict__ src, int64_t src_stride, char* __restrict__ dst, int64_t dst_stride,
-    int64_t dst_nrows, const int64_t* __restrict__ loc, uint32_t total, FastDiv cdiv) {
+__global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterSide k, ScatterSide v, bool kv,
+                                                           int64_t dst_nrows,
+                                                           const int64_t* __restrict__ loc,
+                                                           uint32_t total, FastDiv cdiv) {
   typedef Chunk<W> C;
   const uint32_t step = gridDim.x * kThreads * kUnroll;
   for (uint32_t j0 = blockIdx.x * kThreads * kUnroll + threadIdx.x; j0 < total; j0 += step) {
-    typename C::T v[kUnroll];
+    typename C::T val[kUnroll];
     char* d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t j = j0 + u * kThreads;
       d[u] = nullptr;
       if (j < total) {
-        const uint32_t row = fdiv(j, cdiv);
-        const uint32_t c = j - row * cdiv.d;
+        const uint32_t q = fdiv(j, cdiv);
+        const uint32_t c = j - q * cdiv.d;
+        const uint32_t row = kv ? q >> 1 : q;
+        const ScatterSide& sd = (kv && (q & 1)) ? v : k;
         const int64_t to = loc[row];
         if (to >= 0 && to < dst_nrows) {
           const int64_t off = static_cast<int64_t>(c) * W;
-          v[u] = C::load(src + static_cast<int64_t>(row) * src_stride + off);
-          d[u] = dst + to * dst_stride + off;
+          val[u] = C::load(sd.src + static_cast<int64_t>(row) * sd.src_stride + off);
+          d[u] = sd.dst + to * sd.dst_stride + off;
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (d[u]) C::store(d[u], v[u]);
+      if (d[u]) C::store(d[u], val[u]);
   }
 }
 
@@ -127,30 +156,35 @@ inline unsigned copy_grid(uint64_t items, int num_cus) {
 
 using namespace hs;
 
-extern "C" int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
-                                       const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
-                                       int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
-                                       int64_t dst_nrows, hipStream_t stream) {
+namespace {
+
+// Shared host side of both all-layer transfers: lp.lk layers of K, and as many
+// of V when lp.src_v is set.
+int launch_transfer(const LayerPtrs& lp, const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
+                    int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
+                    hipStream_t stream) {
   if (n < 0 || num_layers < 0) return set_error(HS_EINVAL, "n and num_layers must be >= 0");
   if (n == 0 || num_layers == 0) return HS_OK;
-  if (!src_layer_ptrs || !dst_layer_ptrs || !src_idx || !dst_idx)
+  if (!lp.src_k || !lp.dst_k || !src_idx || !dst_idx || (lp.src_v && !lp.dst_v))
     return set_error(HS_EINVAL, "a required pointer is NULL");
   if (row_bytes <= 0 || (row_bytes & 3) != 0)
     return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
   if (row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
   if (src_nrows < 0 || dst_nrows < 0) return set_error(HS_EINVAL, "row counts must be >= 0");
+  if (num_layers > (1 << 24)) return set_error(HS_ERANGE, "too many layers");
+  const int32_t streams = lp.src_v ? 2 * num_layers : num_layers;
   // Layer base addresses live on the device; rows are 16-byte chunks when
-  // row_bytes allows (layer bases are checked by the kernel's caller contract:
-  // cache allocations are at least 256-byte aligned).
+  // row_bytes allows (a base that is only 4-byte aligned is moved as dwords
+  // by the kernel).
   const int W = (row_bytes & 15) == 0 ? 16 : 4;
   const int64_t C = row_bytes / W;
   DeviceInfo di;
   int rc = device_info(&di);
   if (rc != HS_OK) return rc;
   const FastDiv cdiv = make_fastdiv(static_cast<uint32_t>(C));
-  const FastDiv ldiv = make_fastdiv(static_cast<uint32_t>(num_layers));
+  const FastDiv ldiv = make_fastdiv(static_cast<uint32_t>(streams));
   // Items must stay below 2^31 per launch: split the pairs into batches.
-  const int64_t per_pair = C * num_layers;
+  const int64_t per_pair = C * streams;
   const int64_t max_pairs = ((1ll << 30) / per_pair) > 0 ? ((1ll << 30) / per_pair) : 0;
   if (max_pairs == 0) return set_error(HS_ERANGE, "one pair spans more than 2^30 chunks");
   for (int64_t p0 = 0; p0 < n; p0 += max_pairs) {
@@ -158,55 +192,109 @@ extern "C" int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uin
     const uint32_t total = static_cast<uint32_t>(np * per_pair);
     const unsigned grid = copy_grid(total, di.num_cus);
     if (W == 16)
-      hipLaunchKernelGGL(transfer_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, src_layer_ptrs,
-                         dst_layer_ptrs, src_idx + p0, dst_idx + p0, total, num_layers, row_bytes,
-                         src_nrows, dst_nrows, cdiv, ldiv);
+      hipLaunchKernelGGL(transfer_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, lp,
+                         src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
+                         dst_nrows, cdiv, ldiv);
     else
-      hipLaunchKernelGGL(transfer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, src_layer_ptrs,
-                         dst_layer_ptrs, src_idx + p0, dst_idx + p0, total, num_layers, row_bytes,
-                         src_nrows, dst_nrows, cdiv, ldiv);
+      hipLaunchKernelGGL(transfer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, lp,
+                         src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
+                         dst_nrows, cdiv, ldiv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(HS_ELAUNCH, "transfer launch: %s", hipGetErrorString(e));
   }
   return HS_OK;
 }
 
-extern "C" int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
-                                int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
-                                int64_t n, int64_t row_bytes, hipStream_t stream) {
+bool side_ok(const ScatterSide& sd, int64_t row_bytes) {
+  return sd.src_stride >= row_bytes && sd.dst_stride >= row_bytes && (sd.src_stride & 3) == 0 &&
+         (sd.dst_stride & 3) == 0 && aligned(sd.src, 4) && aligned(sd.dst, 4);
+}
+
+bool side_w16(const ScatterSide& sd) {
+  return aligned(sd.src, 16) && aligned(sd.dst, 16) && (sd.src_stride & 15) == 0 &&
+         (sd.dst_stride & 15) == 0;
+}
+
+int launch_scatter(const ScatterSide& k, const ScatterSide* v, int64_t dst_nrows, const int64_t* loc,
+                   int64_t n, int64_t row_bytes, hipStream_t stream) {
   if (n < 0) return set_error(HS_EINVAL, "n must be >= 0");
   if (n == 0) return HS_OK;
-  if (!src || !dst || !loc) return set_error(HS_EINVAL, "a required pointer is NULL");
+  if (!k.src || !k.dst || !loc || (v && (!v->src || !v->dst)))
+    return set_error(HS_EINVAL, "a required pointer is NULL");
   if (row_bytes <= 0 || (row_bytes & 3) != 0)
     return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
   if (row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
-  if (src_row_stride_bytes < row_bytes || dst_row_stride_bytes < row_bytes ||
-      (src_row_stride_bytes & 3) || (dst_row_stride_bytes & 3))
-    return set_error(HS_EINVAL, "row strides must be >= row_bytes and multiples of 4");
-  if (!aligned(src, 4) || !aligned(dst, 4)) return set_error(HS_EINVAL, "src/dst must be 4-byte aligned");
+  if (!side_ok(k, row_bytes) || (v && !side_ok(*v, row_bytes)))
+    return set_error(HS_EINVAL,
+                     "row strides must be >= row_bytes and multiples of 4, bases 4-byte aligned");
   if (dst_nrows < 0) return set_error(HS_EINVAL, "dst_nrows must be >= 0");
-  const bool w16 = aligned(src, 16) && aligned(dst, 16) && (row_bytes & 15) == 0 &&
-                   (src_row_stride_bytes & 15) == 0 && (dst_row_stride_bytes & 15) == 0;
+  const bool w16 = (row_bytes & 15) == 0 && side_w16(k) && (!v || side_w16(*v));
   const int W = w16 ? 16 : 4;
   const int64_t C = row_bytes / W;
-  if (n * C >= (1ll << 31)) return set_error(HS_ERANGE, "n * chunks per row exceeds 2^31");
+  const int64_t streams = v ? 2 : 1;
+  if (n * C * streams >= (1ll << 31)) return set_error(HS_ERANGE, "n * chunks per entry exceeds 2^31");
   DeviceInfo di;
   int rc = device_info(&di);
   if (rc != HS_OK) return rc;
-  const uint32_t total = static_cast<uint32_t>(n * C);
+  const uint32_t total = static_cast<uint32_t>(n * C * streams);
   const FastDiv cdiv = make_fastdiv(static_cast<uint32_t>(C));
   const unsigned grid = copy_grid(total, di.num_cus);
+  const ScatterSide vv = v ? *v : k;
   if (W == 16)
-    hipLaunchKernelGGL(scatter_kernel<16>, dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const char*>(src), src_row_stride_bytes, static_cast<char*>(dst),
-                       dst_row_stride_bytes, dst_nrows, loc, total, cdiv);
+    hipLaunchKernelGGL(scatter_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, k, vv, v != nullptr,
+                       dst_nrows, loc, total, cdiv);
   else
-    hipLaunchKernelGGL(scatter_kernel<4>, dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const char*>(src), src_row_stride_bytes, static_cast<char*>(dst),
-                       dst_row_stride_bytes, dst_nrows, loc, total, cdiv);
+    hipLaunchKernelGGL(scatter_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, k, vv, v != nullptr,
+                       dst_nrows, loc, total, cdiv);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "scatter launch: %s", hipGetErrorString(e));
   return HS_OK;
+}
+
+}  // namespace
+
+extern "C" int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
+                                       const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
+                                       int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
+                                       int64_t dst_nrows, hipStream_t stream) {
+  const LayerPtrs lp{src_layer_ptrs, dst_layer_ptrs, nullptr, nullptr, num_layers};
+  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows, stream);
+}
+
+extern "C" int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs,
+                                     const uint64_t* v_src_layer_ptrs,
+                                     const uint64_t* k_dst_layer_ptrs,
+                                     const uint64_t* v_dst_layer_ptrs, const int64_t* src_idx,
+                                     const int64_t* dst_idx, int64_t n, int32_t num_layers,
+                                     int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
+                                     hipStream_t stream) {
+  if (!v_src_layer_ptrs || !v_dst_layer_ptrs) {
+    if (n == 0 || num_layers == 0) return HS_OK;
+    return set_error(HS_EINVAL, "a required pointer is NULL");
+  }
+  const LayerPtrs lp{k_src_layer_ptrs, k_dst_layer_ptrs, v_src_layer_ptrs, v_dst_layer_ptrs,
+                     num_layers};
+  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows, stream);
+}
+
+extern "C" int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
+                                int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
+                                int64_t n, int64_t row_bytes, hipStream_t stream) {
+  const ScatterSide k{static_cast<const char*>(src), src_row_stride_bytes, static_cast<char*>(dst),
+                      dst_row_stride_bytes};
+  return launch_scatter(k, nullptr, dst_nrows, loc, n, row_bytes, stream);
+}
+
+extern "C" int store_kv_cache(const void* k_src, int64_t k_src_row_stride_bytes, const void* v_src,
+                              int64_t v_src_row_stride_bytes, void* k_dst,
+                              int64_t k_dst_row_stride_bytes, void* v_dst,
+                              int64_t v_dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
+                              int64_t n, int64_t row_bytes, hipStream_t stream) {
+  const ScatterSide k{static_cast<const char*>(k_src), k_src_row_stride_bytes,
+                      static_cast<char*>(k_dst), k_dst_row_stride_bytes};
+  const ScatterSide v{static_cast<const char*>(v_src), v_src_row_stride_bytes,
+                      static_cast<char*>(v_dst), v_dst_row_stride_bytes};
+  return launch_scatter(k, &v, dst_nrows, loc, n, row_bytes, stream);
 }
 
 extern "C" int hisparse_state_reset(int32_t* slot_tokens, int16_t* lru, const int64_t* rows,

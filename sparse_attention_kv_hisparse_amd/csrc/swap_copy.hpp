@@ -31,6 +31,8 @@ struct MissList {
   const int32_t* dst;    // [B, K] hot row of miss m
   const char* pool;      // device-visible address of the pool (single pair)
   char* hot;             // (single pair)
+  const char* pool_v;    // non-MLA caches: the V pool and V hot buffer (same
+  char* hot_v;           // geometry), or null; each miss then moves two rows
   const uint64_t* pool_layers;  // [layers] pool bases (layered replay)
   const uint64_t* hot_layers;   // [layers] hot bases (layered replay)
   int64_t pool_nrows;
@@ -43,9 +45,10 @@ struct MissList {
 };
 
 // Workgroup g serves request g % B, part g / B of `parts`. Items are
-// (miss, layer, chunk) with the chunk fastest: consecutive lanes take
-// consecutive chunks of one row, so each wave's accesses coalesce, and every
-// lane keeps kCopyUnroll independent loads in flight.
+// (miss, layer, chunk) -- or (miss, K/V, chunk) for a single non-MLA pair --
+// with the chunk fastest: consecutive lanes take consecutive chunks of one
+// row, so each wave's accesses coalesce, and every lane keeps kCopyUnroll
+// independent loads in flight.
 template <int W, bool kLayers>
 __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int32_t parts) {
   typedef Chunk<W> C;
@@ -63,7 +66,8 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
   const int part = blockIdx.x / a.B;
   int M = a.count[b];
   M = M < 0 ? 0 : (M > a.K ? a.K : M);
-  const uint32_t per_miss = (kLayers ? static_cast<uint32_t>(a.layers) : 1u) * a.cdiv.d;
+  const bool kv = !kLayers && a.pool_v != nullptr;   // uniform
+  const uint32_t per_miss = (kLayers ? static_cast<uint32_t>(a.layers) : (kv ? 2u : 1u)) * a.cdiv.d;
   const uint32_t total = static_cast<uint32_t>(M) * per_miss;
   const int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
   const int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
@@ -83,12 +87,15 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
         if (kLayers) {
           m = fdiv(q, a.ldiv);
           l = q - m * a.ldiv.d;
+        } else if (kv) {
+          m = q >> 1;
+          l = q & 1;
         }
         const int64_t s = src[m];
         const int32_t hr = dst[m];
         if (s >= 0 && hr >= 0 && hr < a.hot_nrows) {
-          const char* pbase = a.pool;
-          char* hbase = a.hot;
+          const char* pbase = l ? a.pool_v : a.pool;
+          char* hbase = l ? a.hot_v : a.hot;
           if (kLayers) {
             pbase = reinterpret_cast<const char*>(staged ? s_pool[l] : a.pool_layers[l]);
             hbase = reinterpret_cast<char*>(staged ? s_hot[l] : a.hot_layers[l]);
@@ -120,7 +127,8 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
 // overall. W is 16 when the bases and row_bytes are 16-byte aligned, else 4.
 inline int launch_swap_copy(const MissList& a, int W, int num_cus, hipStream_t stream) {
   const bool layered = a.pool_layers != nullptr;
-  const int64_t max_items = static_cast<int64_t>(a.K) * a.layers * a.cdiv.d;
+  const int64_t streams = layered ? a.layers : (a.pool_v ? 2 : 1);
+  const int64_t max_items = static_cast<int64_t>(a.K) * streams * a.cdiv.d;
   int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
   const int64_t cap = (8LL * num_cus + a.B - 1) / a.B;
   if (parts > cap) parts = cap;

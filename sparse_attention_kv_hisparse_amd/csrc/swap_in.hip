@@ -66,6 +66,8 @@ struct SwapArgs {
   int32_t* out_rows;
   int32_t* miss_counts;
   int32_t* miss_mask; // [B, K] or null: 1 where the entry missed and got a slot
+  const char* pool_v; // non-MLA caches: V pool / V hot buffer, or null
+  char* hot_v;
   int32_t* count;     // [B] misses of request b
   int64_t* src;       // [B, K] pool row of miss m
   int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
@@ -541,7 +543,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     typedef Chunk<kCopyW> CW;
     __syncthreads();
     const uint32_t C = a.cdiv.d;
-    const uint32_t total = static_cast<uint32_t>(m_total) * C;
+    const bool kv = a.pool_v != nullptr;    // uniform: a V row per miss too
+    const uint32_t total = static_cast<uint32_t>(m_total) * (kv ? 2u : 1u) * C;
     for (uint32_t j0 = tid; j0 < total; j0 += kThreads * kFuseUnroll) {
       typename CW::T cv[kFuseUnroll];
       char* cd[kFuseUnroll];
@@ -550,14 +553,16 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         const uint32_t j = j0 + u * kThreads;
         cd[u] = nullptr;
         if (j < total) {
-          const uint32_t mm = fdiv(j, a.cdiv);
-          const uint32_t c = j - mm * C;
+          const uint32_t q = fdiv(j, a.cdiv);     // (miss, K/V) row
+          const uint32_t c = j - q * C;
+          const uint32_t mm = kv ? q >> 1 : q;
+          const bool isv = kv && (q & 1);
           const int64_t sr = l_src[mm];
           const int32_t hr = l_dst[mm];
           if (sr >= 0 && sr < a.pool_nrows && hr >= 0 && hr < a.hot_nrows) {
             const int64_t off = static_cast<int64_t>(c) * kCopyW;
-            cv[u] = CW::load(a.pool + sr * a.row_bytes + off);
-            cd[u] = a.hot + static_cast<int64_t>(hr) * a.row_bytes + off;
+            cv[u] = CW::load((isv ? a.pool_v : a.pool) + sr * a.row_bytes + off);
+            cd[u] = (isv ? a.hot_v : a.hot) + static_cast<int64_t>(hr) * a.row_bytes + off;
           }
         }
       }
@@ -680,10 +685,18 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     if (a->hot_nrows < a->R * a->S_r)
       return set_error(HS_EINVAL, "hot_nrows < R*S_r with flat regions");
   }
-  const int W = (aligned(a->pool, 16) && aligned(a->hot, 16) && (a->row_bytes & 15) == 0) ? 16 : 4;
+  if ((a->pool_v == nullptr) != (a->hot_v == nullptr))
+    return set_error(HS_EINVAL, "pool_v and hot_v are given together or not at all");
+  if (a->pool_v && (!aligned(a->pool_v, 4) || !aligned(a->hot_v, 4)))
+    return set_error(HS_EINVAL, "pool_v and hot_v must be 4-byte aligned");
+  const bool kv = a->pool_v != nullptr;
+  const int W = (aligned(a->pool, 16) && aligned(a->hot, 16) && (a->row_bytes & 15) == 0 &&
+                 (!kv || (aligned(a->pool_v, 16) && aligned(a->hot_v, 16))))
+                    ? 16
+                    : 4;
   const int64_t C = a->row_bytes / W;
-  if (static_cast<int64_t>(a->K) * C >= (1ll << 31))
-    return set_error(HS_ERANGE, "top_k * chunks per row exceeds 2^31");
+  if (static_cast<int64_t>(a->K) * (kv ? 2 : 1) * C >= (1ll << 31))
+    return set_error(HS_ERANGE, "top_k * streams * chunks per row exceeds 2^31");
   const WsLayout wl = ws_layout(a->B, a->K);
   if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256))
     return set_error(HS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned", wl.total);
@@ -734,6 +747,19 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   } else {
     return set_error(HS_EMEMKIND, "pool must be device memory or pinned host memory");
   }
+  const char* pool_v_dev = nullptr;
+  if (kv) {
+    // The V pool lives where the K pool does (one copy strategy for both).
+    hipPointerAttribute_t va;
+    if (hipPointerGetAttributes(&va, a->pool_v) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(HS_EMEMKIND, "pool_v is not a HIP allocation (device or pinned host)");
+    }
+    if (va.type != attr.type)
+      return set_error(HS_EMEMKIND, "pool_v must be the same kind of memory as pool");
+    pool_v_dev = static_cast<const char*>(
+        (va.type == hipMemoryTypeHost && va.devicePointer) ? va.devicePointer : a->pool_v);
+  }
   // Over the host link each request's workgroup copies its own misses (the
   // link, not the CU count, bounds the copy); an HBM pool gets the wide copy
   // kernel, which spreads every request over many CUs.
@@ -759,6 +785,8 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.pool_rows = a->pool_rows;
   s.ctx_stride = a->ctx_stride;
   s.pool = pool_dev;
+  s.pool_v = pool_v_dev;
+  s.hot_v = static_cast<char*>(a->hot_v);
   s.pool_nrows = a->pool_nrows;
   s.hot = static_cast<char*>(a->hot);
   s.hot_nrows = a->hot_nrows;
@@ -803,6 +831,8 @@ int launch_copy(Plan& pl, hipStream_t stream) {
   l.dst = pl.s.dst;
   l.pool = pl.s.pool;
   l.hot = pl.s.hot;
+  l.pool_v = pl.s.pool_v;
+  l.hot_v = pl.s.hot_v;
   l.pool_layers = nullptr;
   l.hot_layers = nullptr;
   l.pool_nrows = pl.s.pool_nrows;
@@ -890,6 +920,8 @@ extern "C" int hisparse_gather_compact_layers(const void* workspace, size_t work
   l.dst = reinterpret_cast<const int32_t*>(ws + wl.dst);
   l.pool = nullptr;
   l.hot = nullptr;
+  l.pool_v = nullptr;
+  l.hot_v = nullptr;
   l.pool_layers = pool_layer_ptrs;
   l.hot_layers = hot_layer_ptrs;
   l.pool_nrows = pool_nrows;

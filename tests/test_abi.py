@@ -174,3 +174,32 @@ def test_gather_layers_rejects(lib):
     assert g(ctypes.c_void_p(0x200010), need, 2, 4, f, 10, f, 10, 3, 16, None) == -5
     assert g(ws, need, 2, 4, f, 10, f, 10, 1 << 20, 1 << 20, None) == -2   # items beyond 2^31
     assert lib.hisparse_last_error()
+
+
+def test_kv_entries_reject(lib):
+    f = 0x100000
+    t = lib.transfer_kv_all_layer
+    assert t(f, f, f, f, f, f, 0, 3, 16, 10, 10, None) == 0               # empty
+    assert t(f, f, f, f, f, f, 5, 0, 16, 10, 10, None) == 0               # no layers
+    assert t(f, None, f, f, f, f, 5, 3, 16, 10, 10, None) == -1           # V arrays missing
+    assert t(f, f, f, None, f, f, 5, 3, 16, 10, 10, None) == -1
+    assert t(f, f, f, f, f, f, 5, 3, 14, 10, 10, None) == -1              # row_bytes % 4
+    assert t(f, f, f, f, f, f, -1, 3, 16, 10, 10, None) == -1
+    s = lib.store_kv_cache
+    assert s(None, 16, None, 16, None, 16, None, 16, 10, None, 0, 16, None) == 0
+    assert s(f, 16, f, 8, f, 16, f, 16, 10, f, 3, 16, None) == -1         # v src stride < rb
+    assert s(f, 16, f, 16, f, 16, f + 2, 16, 10, f, 3, 16, None) == -1    # misaligned v dst
+    assert s(f, 16, None, 16, f, 16, f, 16, 10, f, 3, 16, None) == -1
+    assert s(f, 16, f, 16, f, 16, f, 16, 10, f, 3, 10, None) == -1        # row_bytes % 4
+    assert lib.hisparse_last_error()
+
+
+def test_swap_in_rejects_half_kv(lib):
+    a = _args()
+    a.pool_v = 0x300000
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+    a.pool_v = None
+    a.hot_v = 0x300000
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+    a.pool_v = 0x300002
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1

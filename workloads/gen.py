@@ -103,6 +103,9 @@ ADVERSARIAL = SwapConfig("adversarial", B=64, H=8192, K=2048, ctx=65536,
                          row_bytes=1152, steps=4, rho=0.5, dist="collide",
                          pool_kind="host", seed=20260005, collide_table=16384)
 ADVERSARIAL_132 = ADVERSARIAL.with_(name="adversarial_132", row_bytes=132)
+# Non-MLA caches (K and V rows per token): the DeepSeek-V3.2-like decode shape
+# with 1024-byte rows, as for 4 KV heads x 128 dims x 2 bytes.
+KV_DECODE = DSV32.with_(name="kv_decode", row_bytes=1024, seed=20260006)
 
 SWAP_CONFIGS = {c.name: c for c in (TINY, DSV32, DEVPOOL, ADVERSARIAL, ADVERSARIAL_132)}
 
