@@ -57,6 +57,20 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+class _Paged(ctypes.Structure):
+    _fields_ = [
+        ("hot_block_table", ctypes.c_void_p), ("hot_table_stride", ctypes.c_int64),
+        ("hot_block_size", ctypes.c_int32),
+        ("src_block_table", ctypes.c_void_p), ("src_table_stride", ctypes.c_int64),
+        ("src_num_blocks", ctypes.c_int32), ("src_block_size", ctypes.c_int32),
+        ("resident_block_table", ctypes.c_void_p), ("resident_table_stride", ctypes.c_int64),
+        ("resident_num_blocks", ctypes.c_int32), ("resident_block_size", ctypes.c_int32),
+        ("resident_null_block", ctypes.c_int32),
+        ("attention_indices", ctypes.c_void_p), ("attention_row_stride", ctypes.c_int64),
+        ("attention_block_stride", ctypes.c_int64),
+    ]
+
+
 class _SwapArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("H", ctypes.c_int32),
@@ -74,6 +88,7 @@ class _SwapArgs(ctypes.Structure):
         ("miss_mask", ctypes.c_void_p), ("list_count", ctypes.c_void_p),
         ("list_src", ctypes.c_void_p), ("list_dst", ctypes.c_void_p),
         ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
+        ("paged", ctypes.POINTER(_Paged)),
     ]
 
 
@@ -113,6 +128,10 @@ def _load(path: Optional[str] = None):
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64]
         lib.oracle_store_kv_cache.restype = ctypes.c_int64
+        lib.oracle_invalidate_written.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64]
+        lib.oracle_invalidate_written.restype = ctypes.c_int64
         _lib = lib
     return _lib
 
@@ -153,7 +172,8 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
             ctx_stride: int, num_real: int = -1, slot_rows: Optional[np.ndarray] = None,
             pool_rows: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None,
             miss_counts: Optional[np.ndarray] = None, plan: bool = False,
-            pool_v: Optional[np.ndarray] = None, hot_v: Optional[np.ndarray] = None):
+            pool_v: Optional[np.ndarray] = None, hot_v: Optional[np.ndarray] = None,
+            paged: Optional[dict] = None):
     """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``,
     and with ``plan=True`` a third item: the plan index-sharing layers replay,
     ``{"miss_mask": int32[B,K], "count": int32[B], "src": int64[B,K], "dst": int32[B,K]}``
@@ -162,6 +182,11 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
     ``pool`` and ``hot`` are ``uint8[nrows, row_bytes]``. State arrays are updated in place.
     ``pool_v``/``hot_v`` (non-MLA caches, both or neither) have the same shapes as
     ``pool``/``hot``; every miss copies its V row too.
+    ``paged`` selects vLLM-style addressing (global-id keys, block tables), a dict with
+    ``hot_block_table`` int32 [R, n] and ``hot_block_size``, and optionally
+    ``src_block_table`` int32 [R, n] + ``src_block_size``, ``resident_block_table`` int32
+    [R, n] + ``resident_block_size`` + ``resident_null_block``, ``attention_indices`` int32
+    [B, K] (output) + ``attention_block_stride``; ``seq_lens`` and ``ctx_stride`` are unused.
     """
     assert (pool_v is None) == (hot_v is None)
     if pool_v is not None:
@@ -178,10 +203,31 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
     if plan:
         p = {"miss_mask": np.empty((B, K), np.int32), "count": np.empty(B, np.int32),
              "src": np.zeros((B, K), np.int64), "dst": np.zeros((B, K), np.int32)}
+    pg = None
+    if paged is not None:
+        hbt = paged["hot_block_table"]
+        sbt = paged.get("src_block_table")
+        rbt = paged.get("resident_block_table")
+        att = paged.get("attention_indices")
+        pg = _Paged(hot_block_table=_ptr(hbt, np.int32), hot_table_stride=hbt.shape[1],
+                    hot_block_size=paged["hot_block_size"],
+                    src_block_table=_ptr(sbt, np.int32),
+                    src_table_stride=0 if sbt is None else sbt.shape[1],
+                    src_num_blocks=0 if sbt is None else sbt.shape[1],
+                    src_block_size=paged.get("src_block_size", 1),
+                    resident_block_table=_ptr(rbt, np.int32),
+                    resident_table_stride=0 if rbt is None else rbt.shape[1],
+                    resident_num_blocks=0 if rbt is None else rbt.shape[1],
+                    resident_block_size=paged.get("resident_block_size", 1),
+                    resident_null_block=paged.get("resident_null_block", -1),
+                    attention_indices=_ptr(att, np.int32, True),
+                    attention_row_stride=0 if att is None else att.shape[1],
+                    attention_block_stride=paged.get("attention_block_stride", 0))
     a = _SwapArgs(
         B=B, K=K, H=H, S_r=S_r, R=R,
         topk=_rows_ptr(topk, np.int32), topk_stride=_row_stride(topk),
-        req_rows=_ptr(req_rows, np.int64), seq_lens=_ptr(seq_lens, np.int64),
+        req_rows=_ptr(req_rows, np.int64),
+        seq_lens=None if seq_lens is None else _ptr(seq_lens, np.int64),
         num_real=num_real,
         slot_tokens=_ptr(slot_tokens, np.int32, True), lru=_ptr(lru, np.int16, True),
         slot_rows=_ptr(slot_rows, np.int32), pool_rows=_ptr(pool_rows, np.int64),
@@ -193,7 +239,8 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
         miss_mask=p and _ptr(p["miss_mask"], np.int32, True),
         list_count=p and _ptr(p["count"], np.int32, True),
         list_src=p and _ptr(p["src"], np.int64, True), list_dst=p and _ptr(p["dst"], np.int32, True),
-        pool_v=_ptr(pool_v, np.uint8), hot_v=_ptr(hot_v, np.uint8, True))
+        pool_v=_ptr(pool_v, np.uint8), hot_v=_ptr(hot_v, np.uint8, True),
+        paged=ctypes.pointer(pg) if pg is not None else None)
     rc = _load().oracle_swap_in(ctypes.byref(a))
     if rc != ORACLE_OK:
         raise OracleError(rc)
@@ -288,6 +335,18 @@ def store_kv_scatter(src: np.ndarray, dst: np.ndarray, loc: np.ndarray) -> int:
     r = _load().oracle_store_kv_scatter(
         src.ctypes.data, src.strides[0], dst.ctypes.data, dst.strides[0], dst.shape[0],
         _ptr(loc, np.int64), n, rb)
+    if r < 0:
+        raise OracleError(int(r))
+    return int(r)
+
+
+def invalidate_written(slot_keys: np.ndarray, rows: np.ndarray, written: np.ndarray) -> int:
+    """Clear every slot of state row ``rows[j]`` that holds global row ``written[j]``;
+    returns the number of slots cleared."""
+    R, S_r = slot_keys.shape
+    r = _load().oracle_invalidate_written(_ptr(slot_keys, np.int32, True), R, S_r,
+                                          _ptr(rows, np.int64), _ptr(written, np.int64),
+                                          rows.shape[0])
     if r < 0:
         raise OracleError(int(r))
     return int(r)

@@ -24,6 +24,7 @@
  */
 #include "hisparse_oracle.h"
 
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -44,9 +45,55 @@ static int cmp_by_index(const void *x, const void *y) {
 }
 
 /* Row(r, s): the hot-buffer row of slot s of state row r. The SGLang page
- * reads it from device_buffer_locs; with no table it is the flat region. */
+ * reads it from device_buffer_locs; with no table it is the flat region; the
+ * vLLM page pages it through a hot block table (get_physical_hot_row). */
 static int64_t hot_row(const oracle_swap_in_args *a, int64_t r, int64_t s) {
+  if (a->paged) {
+    const oracle_paged *p = a->paged;
+    const int64_t blk = p->hot_block_table[r * p->hot_table_stride + s / p->hot_block_size];
+    return blk * p->hot_block_size + s % p->hot_block_size;
+  }
   return a->slot_rows ? (int64_t)a->slot_rows[r * a->S_r + s] : r * a->S_r + s;
+}
+
+/* vLLM page, first phase of hisparse_resolve_residency_kernel: position t of
+ * state row r becomes a global id *g (or -1: no row) and, with a resident
+ * table, a row *res of the device cache that already holds it (or -1). */
+static void paged_translate(const oracle_swap_in_args *a, int64_t r, int64_t t, int64_t *g,
+                            int64_t *res) {
+  const oracle_paged *p = a->paged;
+  *g = t;
+  *res = -1;
+  if (p->src_block_table) {
+    const int64_t blk = t >= 0 ? t / p->src_block_size : -1;
+    *g = -1;
+    if (blk >= 0 && blk < p->src_num_blocks) {
+      const int64_t pb = p->src_block_table[r * p->src_table_stride + blk];
+      if (pb > 0) *g = pb * p->src_block_size + t % p->src_block_size;
+    }
+  }
+  if (*g >= a->pool_nrows) *g = -1;
+  if (p->resident_block_table) {
+    const int64_t blk = t >= 0 ? t / p->resident_block_size : -1;
+    if (blk >= 0 && blk < p->resident_num_blocks) {
+      const int64_t pb = p->resident_block_table[r * p->resident_table_stride + blk];
+      if (pb != p->resident_null_block && pb >= 0)
+        *res = pb * p->resident_block_size + t % p->resident_block_size;
+    }
+  }
+}
+
+/* vLLM page, store_hot_index: the attention kernel's index of a row. */
+static void store_attention(const oracle_swap_in_args *a, int32_t b, const int32_t *out) {
+  const oracle_paged *p = a->paged;
+  if (!p || !p->attention_indices) return;
+  int32_t *att = p->attention_indices + (int64_t)b * p->attention_row_stride;
+  for (int32_t i = 0; i < a->K; ++i) {
+    const int64_t o = out[i];
+    att[i] = o < 0 ? -1
+                   : (int32_t)((o / p->hot_block_size) * p->attention_block_stride +
+                               o % p->hot_block_size);
+  }
 }
 
 /* The pool row holding token t of state row r (SGLang page: host_cache_locs). */
@@ -57,14 +104,23 @@ static int64_t pool_row(const oracle_swap_in_args *a, int64_t r, int64_t t) {
 static int check_args(const oracle_swap_in_args *a) {
   if (!a || a->B < 0 || a->K < 0 || a->H < 0 || a->R < 0) return ORACLE_EARG;
   if (a->B == 0 || a->K == 0) return ORACLE_OK;
-  if (!a->topk || !a->req_rows || !a->seq_lens || !a->slot_tokens || !a->lru ||
+  if (!a->topk || !a->req_rows || (!a->seq_lens && !a->paged) || !a->slot_tokens || !a->lru ||
       !a->pool || !a->hot || !a->out_rows)
     return ORACLE_EARG;
   if (a->H < a->K || a->S_r < (int64_t)a->H + 1 || a->topk_stride < a->K || a->row_bytes <= 0 ||
-      a->ctx_stride <= 0)
+      (a->ctx_stride <= 0 && !a->paged))
     return ORACLE_EARG;
   if (a->list_count && (!a->list_src || !a->list_dst)) return ORACLE_EARG;
   if ((a->pool_v == NULL) != (a->hot_v == NULL)) return ORACLE_EARG;
+  if (a->paged) {
+    const oracle_paged *p = a->paged;
+    if (!p->hot_block_table || p->hot_block_size <= 0 || p->hot_table_stride * p->hot_block_size < a->H)
+      return ORACLE_EARG;
+    if (p->src_block_table && (p->src_block_size <= 0 || p->src_num_blocks < 0)) return ORACLE_EARG;
+    if (p->resident_block_table && (p->resident_block_size <= 0 || p->resident_num_blocks < 0))
+      return ORACLE_EARG;
+    if (a->pool_nrows > INT32_MAX) return ORACLE_EARG;   /* keys are int32 global ids */
+  }
   return ORACLE_OK;
 }
 
@@ -87,8 +143,9 @@ static int check_state_rows(const oracle_swap_in_args *a, int32_t nreal) {
       seen[s] = 1;
     }
     free(seen);
-    /* Every hot row a slot can name lies inside the hot buffer. */
-    for (int64_t s = 0; s <= a->H; ++s) {
+    /* Every hot row a slot can name lies inside the hot buffer (paged
+     * addressing has no newest slot). */
+    for (int64_t s = 0; s < (a->paged ? a->H : a->H + 1); ++s) {
       int64_t hr = hot_row(a, r, s);
       if (hr < 0 || hr >= a->hot_nrows) return ORACLE_EHOT;
     }
@@ -127,9 +184,10 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
     if (b >= nreal || r < 0 || r >= a->R) {
       for (int32_t i = 0; i < K; ++i) out[i] = -1;
       if (a->miss_counts) a->miss_counts[b] = 0;
+      store_attention(a, b, out);
       continue;
     }
-    const int64_t L = a->seq_lens[b];
+    const int64_t L = a->paged ? 0 : a->seq_lens[b];
     const int64_t newest = L - 1;
     int32_t *tokens = a->slot_tokens + r * a->S_r;
     int16_t *lru = a->lru + r * H;
@@ -139,6 +197,20 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
     int32_t np = 0;
     for (int32_t i = 0; i < K; ++i) {
       const int64_t t = ids[i];
+      if (a->paged) {
+        /* vLLM addressing: a resident entry is served from the device cache
+         * as is, an entry without a global id is -1, and every other entry
+         * is pending under its global id (no newest slot). */
+        int64_t g, res;
+        paged_translate(a, r, t, &g, &res);
+        if (res >= 0) { out[i] = (int32_t)res; continue; }
+        if (g < 0) { out[i] = -1; continue; }
+        pending[np].token = (int32_t)g;
+        pending[np].index = i;
+        pending[np].hit = 0;
+        ++np;
+        continue;
+      }
       if (t < 0 || t >= L || t >= a->ctx_stride) { out[i] = -1; continue; }
       const int64_t pr = pool_row(a, r, t);
       if (pr < 0 || pr >= a->pool_nrows) { out[i] = -1; continue; }
@@ -182,7 +254,8 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
       if (pending[j].hit) continue;
       const int16_t v = evict[M];   /* M < ne because H >= K */
       const int64_t dst = hot_row(a, r, v);
-      const int64_t src = pool_row(a, r, pending[j].token);
+      /* The pool row: the key itself under global keying. */
+      const int64_t src = a->paged ? pending[j].token : pool_row(a, r, pending[j].token);
       out[pending[j].index] = (int32_t)dst;
       tokens[v] = pending[j].token;
       memcpy(a->hot + dst * a->row_bytes, a->pool + src * a->row_bytes, (size_t)a->row_bytes);
@@ -210,6 +283,7 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
     memcpy(lru, new_lru, sizeof(int16_t) * (size_t)H);
 
     if (a->miss_counts) a->miss_counts[b] = M;
+    store_attention(a, b, out);
   }
 
 done:
@@ -323,6 +397,23 @@ int64_t oracle_store_kv_scatter(const uint8_t *src, int64_t src_row_stride_bytes
     memcpy(dst + loc[j] * dst_row_stride_bytes, src + j * src_row_stride_bytes, (size_t)row_bytes);
   }
   return skipped;
+}
+
+int64_t oracle_invalidate_written(int32_t *slot_keys, int64_t R, int64_t S_r, const int64_t *rows,
+                                  const int64_t *written, int64_t n) {
+  if (R < 0 || S_r < 0 || n < 0) return ORACLE_EARG;
+  if (n == 0) return 0;
+  if (!slot_keys || !rows || !written) return ORACLE_EARG;
+  int64_t cleared = 0;
+  /* vLLM page, hisparse_invalidate_written_slots_kernel: a rewritten global
+   * row must not be served from a stale hot copy. */
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t r = rows[j], g = written[j];
+    if (r < 0 || r >= R || g < 0) continue;
+    for (int64_t s = 0; s < S_r; ++s)
+      if (slot_keys[r * S_r + s] == g) { slot_keys[r * S_r + s] = -1; ++cleared; }
+  }
+  return cleared;
 }
 
 int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,

@@ -37,6 +37,38 @@ enum {
   ORACLE_EINDEX = -7     /* transfer/scatter index outside its buffer */
 };
 
+/* vLLM-style addressing ([VLLM] hisparse_resolve_residency_kernel and
+ * get_physical_hot_row). With it, slots are keyed by global pool rows instead
+ * of in-request positions, there is no newest-token slot and no seq_len
+ * check, and slot_rows / pool_rows / ctx_stride are not used. Every table is
+ * indexed by the batch row's state row r. */
+typedef struct {
+  /* Row(r, s) = hot_block_table[r][s / hot_block_size] * hot_block_size
+   *             + s % hot_block_size. */
+  const int32_t *hot_block_table;
+  int64_t hot_table_stride;
+  int32_t hot_block_size;
+  /* Global id of position t: with a source table, block t / src_block_size
+   * (below src_num_blocks) maps to physical block p; p > 0 gives
+   * g = p * src_block_size + t % src_block_size, anything else no row.
+   * Without one, the id is the global id. Ids at or past pool_nrows have no
+   * row either. */
+  const int32_t *src_block_table;
+  int64_t src_table_stride;
+  int32_t src_num_blocks, src_block_size;
+  /* Optional: positions still resident in the device cache. Block
+   * t / resident_block_size (below resident_num_blocks) maps to p; p >= 0 and
+   * p != resident_null_block makes the entry resident at row
+   * p * resident_block_size + t % resident_block_size, served as is. */
+  const int32_t *resident_block_table;
+  int64_t resident_table_stride;
+  int32_t resident_num_blocks, resident_block_size, resident_null_block;
+  /* Optional output: attention_indices[b][i] = -1 for out < 0, else
+   * (out / hot_block_size) * attention_block_stride + out % hot_block_size. */
+  int32_t *attention_indices;
+  int64_t attention_row_stride, attention_block_stride;
+} oracle_paged;
+
 typedef struct {
   int32_t B, K, H;          /* batch rows, top_k, hot_size */
   int64_t S_r, R;           /* region_stride (>= H+1), state rows */
@@ -66,6 +98,7 @@ typedef struct {
    * pool's and K hot buffer's geometry; every miss copies its V row too. */
   const uint8_t *pool_v;    /* [pool_nrows, row_bytes] or NULL */
   uint8_t *hot_v;           /* [hot_nrows, row_bytes], NULL when pool_v is */
+  const oracle_paged *paged; /* NULL: SGLang-style addressing (above) */
 } oracle_swap_in_args;
 
 /* One decode-step swap-in call. Returns ORACLE_OK or a negative code when a
@@ -119,6 +152,14 @@ int64_t oracle_store_kv_cache(const uint8_t *k_src, int64_t k_src_stride, const 
 int64_t oracle_store_kv_scatter(const uint8_t *src, int64_t src_row_stride_bytes,
                                 uint8_t *dst, int64_t dst_row_stride_bytes, int64_t dst_nrows,
                                 const int64_t *loc, int64_t n, int64_t row_bytes);
+
+/* Write invalidation ([VLLM] hisparse_invalidate_written_slots_kernel): for
+ * each written token j with state row rows[j] in [0, R) and global row
+ * written[j] >= 0, every slot of that state row (all S_r of them) holding
+ * written[j] becomes empty (-1). LRU order is untouched. Returns the number
+ * of slots cleared, or ORACLE_EARG. */
+int64_t oracle_invalidate_written(int32_t *slot_keys, int64_t R, int64_t S_r, const int64_t *rows,
+                                  const int64_t *written, int64_t n);
 
 /* Initial state of the listed state rows: every token -1, LRU = 0..H-1. */
 int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,

@@ -23,9 +23,19 @@ from collections import OrderedDict
 from typing import Dict, List, Optional
 
 
+def _paged_lookup(table, block_size, r, t):
+    """Physical block of position t in row r of a block table, or None past its end."""
+    if t < 0:
+        return None
+    blk = t // block_size
+    if blk >= table.shape[1]:
+        return None
+    return int(table[r, blk])
+
+
 def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, ctx_stride,
                       num_real=-1, slot_rows=None, pool_rows=None, plan=False, pool_v=None,
-                      hot_v=None):
+                      hot_v=None, paged=None):
     """Same contract as ``oracle.swap_in`` (numpy arrays updated in place). With
     ``plan=True`` also returns the plan: ``miss_mask`` [B,K] (1 for each entry
     whose token no slot held) and, per row, the list of (pool row, hot row)
@@ -41,7 +51,27 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
     copies = [[] for _ in range(B)]
 
     def row_of(r, s):
+        if paged is not None:
+            bs = paged["hot_block_size"]
+            return int(paged["hot_block_table"][r, s // bs]) * bs + s % bs
         return int(slot_rows[r, s]) if slot_rows is not None else r * S_r + s
+
+    def global_id(r, t):
+        """vLLM addressing: (global id or None, resident row or None)."""
+        g = t
+        if paged.get("src_block_table") is not None:
+            bs = paged["src_block_size"]
+            p = _paged_lookup(paged["src_block_table"], bs, r, t)
+            g = p * bs + t % bs if (p is not None and p > 0) else None
+        if g is not None and g >= pool.shape[0]:
+            g = None
+        res = None
+        if paged.get("resident_block_table") is not None:
+            bs = paged["resident_block_size"]
+            p = _paged_lookup(paged["resident_block_table"], bs, r, t)
+            if p is not None and p >= 0 and p != paged["resident_null_block"]:
+                res = p * bs + t % bs
+        return g, res
 
     def pool_of(r, t):
         return int(pool_rows[r, t]) if pool_rows is not None else r * ctx_stride + t
@@ -51,9 +81,20 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
         r = int(req_rows[b])
         if b >= nreal or not (0 <= r < R):
             continue
-        L = int(seq_lens[b])
         wanted: Dict[int, int] = {}
-        for i in range(K):
+        if paged is not None:
+            # keys are global ids; resident entries are served in place
+            for i in range(K):
+                g, res = global_id(r, int(topk[b, i]))
+                if res is not None:
+                    out[b, i] = res
+                elif g is not None:
+                    assert g not in wanted, "duplicate id"
+                    wanted[g] = i
+            L = None
+        else:
+            L = int(seq_lens[b])
+        for i in range(K if paged is None else 0):
             t = int(topk[b, i])
             if not (0 <= t < L and t < ctx_stride):
                 continue
@@ -73,17 +114,19 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
         order = [int(s) for s in lru[r]]
         cache: "OrderedDict[int, None]" = OrderedDict((s, None) for s in order if s not in hit_slots)
         misses = sorted(i for t, i in wanted.items() if t not in where)
+        key_of = {i: t for t, i in wanted.items()}
         for i in misses:
-            t = int(topk[b, i])
+            t = key_of[i]
             v, _ = cache.popitem(last=False)
             cache[v] = None
             slot_tokens[r, v] = t
-            hot[row_of(r, v)] = pool[pool_of(r, t)]
+            src = t if paged is not None else pool_of(r, t)
+            hot[row_of(r, v)] = pool[src]
             if pool_v is not None:
-                hot_v[row_of(r, v)] = pool_v[pool_of(r, t)]
+                hot_v[row_of(r, v)] = pool_v[src]
             out[b, i] = row_of(r, v)
             mask[b, i] = 1
-            copies[b].append((pool_of(r, t), row_of(r, v)))
+            copies[b].append((src, row_of(r, v)))
         lru[r] = np.asarray(list(cache) + [s for s in order if s in hit_slots], dtype=np.int16)
         counts[b] = len(misses)
     if plan:

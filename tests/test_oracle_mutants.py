@@ -27,8 +27,8 @@ MUTANTS = {
                            "for (int32_t e = 0; e < M; ++e) new_lru[q++] = evict[e];\n"
                            "    for (int32_t e = M; e < ne; ++e) new_lru[q++] = evict[e];"),
     "newest_not_bound": ("if (t == newest) {", "if (t == L) {"),
-    "pool_row_off_by_one": ("const int64_t src = pool_row(a, r, pending[j].token);",
-                            "const int64_t src = pool_row(a, r, pending[j].token) + 1;"),
+    "pool_row_off_by_one": ("pending[j].token : pool_row(a, r, pending[j].token);",
+                            "pending[j].token : pool_row(a, r, pending[j].token) + 1;"),
     "misses_in_token_order": ("qsort(pending, (size_t)np, sizeof(pending_t), cmp_by_index);", ""),
     "table_not_updated": ("tokens[v] = pending[j].token;", ""),
     "seq_len_bound_inclusive": ("if (t < 0 || t >= L || t >= a->ctx_stride)",
@@ -51,6 +51,15 @@ MUTANTS = {
     "kv_swap_v_not_copied": ("      if (a->pool_v)\n        memcpy(a->hot_v", "      if (0)\n        memcpy(a->hot_v"),
     "kv_transfer_v_from_k": ("v_src_layers[l] + s * row_bytes", "k_src_layers[l] + s * row_bytes"),
     "kv_scatter_v_k_stride": ("v_src + j * v_src_stride", "v_src + j * k_src_stride"),
+    "paged_null_block_accepted": ("      if (pb > 0) *g = pb * p->src_block_size", "      if (pb >= 0) *g = pb * p->src_block_size"),
+    "paged_resident_ignored": ("if (res >= 0) { out[i] = (int32_t)res; continue; }", ""),
+    "paged_hot_offset_divides": ("return blk * p->hot_block_size + s % p->hot_block_size;",
+                                 "return blk * p->hot_block_size + s / p->hot_block_size;"),
+    "paged_key_is_position": ("pending[np].token = (int32_t)g;", "pending[np].token = (int32_t)t;"),
+    "invalidate_row_zero": ("if (slot_keys[r * S_r + s] == g) { slot_keys[r * S_r + s] = -1;",
+                            "if (slot_keys[s] == g) { slot_keys[s] = -1;"),
+    "attention_offset_wrong": ("                               o % p->hot_block_size);",
+                               "                               o % p->attention_block_stride);"),
     "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
                                       "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }
@@ -63,6 +72,7 @@ def _pins():
     import test_oracle_model as m
     import test_oracle_plan as pl
     import test_oracle_kv as kvt
+    import test_oracle_paged as pgt
     failed = []
     checks = [
         ("golden1", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_1.json")),
@@ -76,6 +86,8 @@ def _pins():
         ("kv_golden", kvt.test_kv_copies_worked_example),
         ("kv_swap_golden", lambda: kvt.test_swap_in_v_rows_follow_k_rows("swap_in_worked_example_1.json")),
         ("kv_model", lambda: m.test_random_multirow_kv(0)),
+        ("paged_golden", pgt.test_paged_worked_example),
+        ("paged_model", lambda: pgt.test_paged_matches_model(0)),
     ]
     for name, fn in checks:
         try:

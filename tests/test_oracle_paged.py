@@ -1,0 +1,185 @@
+"""Pin the oracle's vLLM-style paged addressing and write invalidation.
+
+* ``tests/golden/swap_in_paged_worked_example.json``: three calls and an
+  invalidation derived by hand (vLLM hisparse_kernels.cu:
+  hisparse_resolve_residency_kernel, get_physical_hot_row, store_hot_index,
+  hisparse_invalidate_written_slots_kernel) -- outputs, counts, slot keys,
+  LRU rows, attention indices and hot rows after every step.
+* The OrderedDict model (``tests/model.py``) with its own block-table
+  translation, on random multi-row calls with random hot, source and resident
+  tables, null blocks, padding and invalidations in between.
+* Reduction: with a one-row-per-block hot table that reproduces the flat
+  layout and a source table that reproduces a pool-row table, paged keying
+  gives the position-keyed swap-in's outputs, LRU and hot buffer, and its
+  slot keys are the pool rows of the position-keyed slots' tokens.
+* Invalidation against a numpy mask.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from model import lru_model_swap_in
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _paged_dict(fx_paged, B, K):
+    d = {k: (np.asarray(v, np.int32) if k.endswith("table") else v) for k, v in fx_paged.items()}
+    d["attention_indices"] = np.full((B, K), 7777, np.int32)
+    return d
+
+
+def test_paged_worked_example():
+    fx = json.load(open(os.path.join(GOLDEN, "swap_in_paged_worked_example.json")))
+    H, S_r, R, K, rb = fx["H"], fx["S_r"], fx["R"], fx["K"], fx["row_bytes"]
+    pool = np.array([[(p + j) % 256 for j in range(rb)] for p in range(fx["pool_nrows"])], np.uint8)
+    hot = np.zeros((fx["hot_nrows"], rb), np.uint8)
+    keys = np.full((R, S_r), -1, np.int32)
+    lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
+    for step in fx["steps"]:
+        e = step["expect"]
+        if "invalidate" in step:
+            inv = step["invalidate"]
+            n = oracle.invalidate_written(keys, np.asarray(inv["rows"], np.int64),
+                                          np.asarray(inv["written"], np.int64))
+            assert n == e["cleared"]
+        else:
+            c = step["call"]
+            B = len(c["req_rows"])
+            pg = _paged_dict(fx["paged"], B, K)
+            out, cnt = oracle.swap_in(topk=np.asarray(c["topk"], np.int32),
+                                      req_rows=np.asarray(c["req_rows"], np.int64), seq_lens=None,
+                                      slot_tokens=keys, lru=lru, pool=pool, hot=hot, ctx_stride=0,
+                                      num_real=c["num_real"], paged=pg)
+            assert out.tolist() == e["out"]
+            assert cnt.tolist() == e["miss_counts"]
+            assert pg["attention_indices"].tolist() == e["attention"]
+            want = np.zeros_like(hot)
+            for row, p in e["hot_from_pool"].items():
+                want[int(row)] = pool[p]
+            assert np.array_equal(hot, want)
+        assert keys.tolist() == e["slot_tokens"]
+        assert lru.tolist() == e["lru"]
+
+
+def _random_tables(rng, R, H, ctx):
+    hb = int(rng.choice([1, 2, 4, 8]))
+    nhb = -(-H // hb)
+    extra = 3
+    hot_blocks = rng.permutation(R * nhb + extra)[:R * nhb].reshape(R, nhb).astype(np.int32)
+    hot_nrows = (R * nhb + extra) * hb
+    sb = int(rng.choice([4, 16]))
+    nsb = -(-ctx // sb) + 1
+    phys = rng.permutation(np.arange(1, R * nsb + 4))[:R * nsb].reshape(R, nsb).astype(np.int32)
+    nulls = rng.random((R, nsb)) < 0.1
+    phys[nulls] = rng.choice([0, -1], size=int(nulls.sum()))
+    pool_nrows = (R * nsb + 4) * sb - sb // 2           # the last block is cut: some ids have no row
+    rbs = 8
+    nrb = -(-ctx // rbs)
+    res = np.full((R, nrb), -1, np.int32)
+    hit = rng.random((R, nrb)) < 0.15
+    res[hit] = rng.integers(0, 50, int(hit.sum()))
+    paged = {"hot_block_table": hot_blocks, "hot_block_size": hb, "src_block_table": phys,
+             "src_block_size": sb, "resident_block_table": res, "resident_block_size": rbs,
+             "resident_null_block": -1}
+    return paged, hot_nrows, pool_nrows
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_paged_matches_model(seed):
+    rng = np.random.default_rng(1000 + seed)
+    R, B, H, K, ctx, rb = 5, 3, 16, 8, 120, 4
+    S_r = H + 1
+    paged, hot_nrows, pool_nrows = _random_tables(rng, R, H, ctx)
+    if seed % 2:
+        paged = {k: v for k, v in paged.items() if not k.startswith("resident")}
+    pool = rng.integers(0, 256, (pool_nrows, rb), dtype=np.uint8)
+    st_o, lru_o = gen.initial_state(R, H, S_r)
+    st_m, lru_m = st_o.copy(), lru_o.copy()
+    hot_o = np.zeros((hot_nrows, rb), np.uint8)
+    hot_m = hot_o.copy()
+    for call in range(14):
+        if call % 5 == 4:
+            # invalidate a few global rows that some slots hold
+            rows = rng.integers(-1, R + 1, 6).astype(np.int64)
+            written = np.array([st_o[r % R, rng.integers(0, H)] for r in rows], np.int64)
+            n_o = oracle.invalidate_written(st_o, rows, written)
+            for r, g in zip(rows, written):
+                if 0 <= r < R and g >= 0:
+                    st_m[r][st_m[r] == g] = -1
+            assert np.array_equal(st_o, st_m) and n_o >= 0
+            continue
+        req = rng.permutation(R)[:B].astype(np.int64)
+        topk = np.stack([rng.permutation(np.arange(-3, ctx + 5))[:K] for _ in range(B)]).astype(np.int32)
+        nreal = int(rng.integers(1, B + 1)) if rng.random() < 0.3 else -1
+        kw = dict(topk=topk, req_rows=req, seq_lens=None, pool=pool, ctx_stride=0, num_real=nreal,
+                  paged=paged)
+        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True, **kw)
+        out_m, cnt_m, plan_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, plan=True, **kw)
+        assert out_o.tolist() == out_m.tolist(), call
+        assert cnt_o.tolist() == cnt_m.tolist()
+        assert st_o.tolist() == st_m.tolist()
+        assert lru_o.tolist() == lru_m.tolist()
+        assert np.array_equal(hot_o, hot_m)
+        assert plan_o["miss_mask"].tolist() == plan_m["miss_mask"].tolist()
+        for b, cp in enumerate(plan_m["copies"]):
+            n = len(cp)
+            assert list(zip(plan_o["src"][b, :n].tolist(), plan_o["dst"][b, :n].tolist())) == cp
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_paged_reduces_to_position_keying(seed):
+    rng = np.random.default_rng(2000 + seed)
+    R, B, H, K, ctx, rb = 4, 3, 24, 10, 200, 8
+    S_r = H + 1
+    # hot table with one row per block: Row(r, s) = r * S_r + s, the flat layout
+    hot_table = np.array([[r * S_r + s for s in range(H)] for r in range(R)], np.int32)
+    # source table with one block per request: g = (r + 1) * ctx + t
+    src_table = np.array([[r + 1] for r in range(R)], np.int32)
+    pool_rows = np.array([[(r + 1) * ctx + t for t in range(ctx)] for r in range(R)], np.int64)
+    paged = {"hot_block_table": hot_table, "hot_block_size": 1, "src_block_table": src_table,
+             "src_block_size": ctx}
+    pool = rng.integers(0, 256, ((R + 1) * ctx, rb), dtype=np.uint8)
+    st_p, lru_p = gen.initial_state(R, H, S_r)
+    st_q, lru_q = st_p.copy(), lru_p.copy()
+    hot_p = np.zeros((R * S_r, rb), np.uint8)
+    hot_q = hot_p.copy()
+    for _ in range(10):
+        req = rng.permutation(R)[:B].astype(np.int64)
+        # positions below ctx - 1: no newest-token binding on the position side
+        topk = np.stack([rng.permutation(ctx - 1)[:K] for _ in range(B)]).astype(np.int32)
+        out_p, cnt_p = oracle.swap_in(topk=topk, req_rows=req, seq_lens=None, slot_tokens=st_p,
+                                      lru=lru_p, pool=pool, hot=hot_p, ctx_stride=0, paged=paged)
+        out_q, cnt_q = oracle.swap_in(topk=topk, req_rows=req, seq_lens=np.full(B, ctx, np.int64),
+                                      slot_tokens=st_q, lru=lru_q, pool=pool, hot=hot_q,
+                                      ctx_stride=ctx, pool_rows=pool_rows)
+        assert out_p.tolist() == out_q.tolist()
+        assert cnt_p.tolist() == cnt_q.tolist()
+        assert lru_p.tolist() == lru_q.tolist()
+        assert np.array_equal(hot_p, hot_q)
+        keys_from_q = np.where(st_q[:, :H] >= 0,
+                               np.take_along_axis(pool_rows, np.maximum(st_q[:, :H], 0).astype(np.int64), 1),
+                               -1)
+        assert st_p[:, :H].tolist() == keys_from_q.tolist()
+
+
+def test_invalidate_matches_numpy():
+    rng = np.random.default_rng(7)
+    R, S_r, n = 6, 20, 40
+    keys = rng.integers(-1, 30, (R, S_r)).astype(np.int32)
+    rows = rng.integers(-2, R + 2, n).astype(np.int64)
+    written = rng.integers(-3, 30, n).astype(np.int64)
+    want = keys.copy()
+    cleared = 0
+    for r, g in zip(rows, written):
+        if 0 <= r < R and g >= 0:
+            m = want[r] == g
+            cleared += int(m.sum())
+            want[r][m] = -1
+    assert oracle.invalidate_written(keys, rows, written) == cleared
+    assert np.array_equal(keys, want)
