@@ -72,6 +72,47 @@ typedef enum {
  * pool_row(r, t) = pool_rows ? pool_rows[r*ctx_stride + t] : r*ctx_stride + t
  * is the pool row holding token t of state row r (SGLang: host_cache_locs).
  */
+/*
+ * vLLM-style paged addressing (vLLM hisparse_kernels.cu:
+ * hisparse_resolve_residency_kernel, get_physical_hot_row, store_hot_index).
+ * With hs_swap_in_args.paged set, the swap-in keys slots by global pool rows
+ * instead of in-request positions:
+ *   - Row(r, s) = hot_block_table[r][s / hot_block_size] * hot_block_size
+ *                 + s % hot_block_size: a paged hot buffer;
+ *   - position t of state row r has global id g: with src_block_table, the
+ *     physical block p = src_block_table[r][t / src_block_size] (blocks past
+ *     src_num_blocks: none) gives g = p * src_block_size + t % src_block_size
+ *     when p > 0, else no row; without it the id is already global (g = t).
+ *     Ids at or past pool_nrows have no row. slot_tokens holds global ids,
+ *     and g is the pool row a miss copies;
+ *   - with resident_block_table, a position whose block maps to p >= 0,
+ *     p != resident_null_block, is resident in the device cache at row
+ *     p * resident_block_size + t % resident_block_size and is output as is,
+ *     with no slot or copy;
+ *   - an id with no row outputs -1; there is no newest-token slot and no
+ *     seq_len check (seq_lens may be NULL; ctx_stride is unused);
+ *   - attention_indices (optional output, [B, attention_row_stride]) gets, for
+ *     each entry, -1 or (out / hot_block_size) * attention_block_stride
+ *     + out % hot_block_size.
+ * Every table is a device int32 array indexed by the batch row's state row
+ * (row r at r * stride). slot_rows and pool_rows must be NULL. pool_nrows and
+ * hot_nrows must fit int32. Victim choice, LRU update, padding, the miss list
+ * and the copies are as without paging.
+ */
+typedef struct hs_paged_addressing {
+  const int32_t* hot_block_table;       /* [R, hot_table_stride], required     */
+  int64_t hot_table_stride;             /* >= ceil(H / hot_block_size)         */
+  int32_t hot_block_size;               /* > 0                                 */
+  const int32_t* src_block_table;       /* [R, src_table_stride] or NULL       */
+  int64_t src_table_stride;
+  int32_t src_num_blocks, src_block_size;
+  const int32_t* resident_block_table;  /* [R, resident_table_stride] or NULL  */
+  int64_t resident_table_stride;
+  int32_t resident_num_blocks, resident_block_size, resident_null_block;
+  int32_t* attention_indices;           /* [B, attention_row_stride] or NULL   */
+  int64_t attention_row_stride, attention_block_stride;
+} hs_paged_addressing;
+
 typedef struct hs_swap_in_args {
   int32_t B;                 /* batch rows in this call                          */
   int32_t K;                 /* top_k ids per batch row, 0 < K <= H              */
@@ -110,6 +151,10 @@ typedef struct hs_swap_in_args {
    * Both NULL for MLA (one latent row per token). */
   const void* pool_v;        /* [pool_nrows, row_bytes], or NULL                 */
   void* hot_v;               /* device [hot_nrows, row_bytes], or NULL           */
+
+  /* vLLM-style paged addressing (host pointer to a struct whose tables are
+   * device arrays), or NULL for the addressing described above. */
+  const hs_paged_addressing* paged;
 } hs_swap_in_args;
 
 /* Bytes of device workspace hisparse_swap_in needs for B rows of K ids
@@ -291,6 +336,21 @@ int store_kv_cache(const void* k_src, int64_t k_src_row_stride_bytes, const void
                    int64_t v_src_row_stride_bytes, void* k_dst, int64_t k_dst_row_stride_bytes,
                    void* v_dst, int64_t v_dst_row_stride_bytes, int64_t dst_nrows,
                    const int64_t* loc, int64_t n, int64_t row_bytes, hipStream_t stream);
+
+/*
+ * hisparse_invalidate_written -- drop hot copies of rewritten pool rows.
+ * vLLM hisparse_kernels.cu, hisparse_invalidate_written_slots_kernel.
+ *
+ * For every j < n with 0 <= rows[j] < R and written[j] >= 0, every entry of
+ * slot_keys[rows[j]][0..S_r) equal to written[j] becomes -1 (empty), so the
+ * next swap-in that wants that global row copies it again instead of serving
+ * the stale hot row. For slot tables keyed by global ids (paged addressing).
+ * The LRU order is left as is: an emptied slot is simply evictable.
+ * slot_keys: device int32 [R, S_r]; rows, written: device int64 [n].
+ * n == 0 returns HS_OK.
+ */
+int hisparse_invalidate_written(int32_t* slot_keys, int64_t R, int64_t S_r, const int64_t* rows,
+                                const int64_t* written, int64_t n, hipStream_t stream);
 
 /*
  * hisparse_state_reset -- put state rows into the initial state: every entry

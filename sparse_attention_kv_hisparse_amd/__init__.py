@@ -13,10 +13,11 @@ from typing import Optional
 
 import torch
 
-from ._lib import EXPORTS, HisparseError, SwapInArgs, check, load
+from ._lib import EXPORTS, HisparseError, PagedAddressing, SwapInArgs, check, load
 
 __all__ = ["hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
            "hisparse_gather_compact_layers", "transfer_kv_all_layer", "store_kv_cache",
+           "hisparse_invalidate_written",
            "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
            "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
 
@@ -59,7 +60,8 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                      pool_rows: Optional[torch.Tensor] = None,
                      miss_mask: Optional[torch.Tensor] = None,
                      pool_v: Optional[torch.Tensor] = None, hot_v: Optional[torch.Tensor] = None,
-                     stream=None, _entry: str = "hisparse_swap_in") -> None:
+                     paged: Optional[dict] = None, stream=None,
+                     _entry: str = "hisparse_swap_in") -> None:
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
@@ -69,6 +71,11 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
     miss_mask int32 [B, K] (optional output: 1 where the entry missed and got a slot),
     pool_v / hot_v (non-MLA caches, both or neither): the V pool and V hot buffer, shaped
     and placed like pool / hot.
+    paged (vLLM-style addressing): dict with ``hot_block_table`` int32 [R, n] and
+    ``hot_block_size``; optionally ``src_block_table`` int32 [R, n] + ``src_block_size``,
+    ``resident_block_table`` int32 [R, n] + ``resident_block_size`` + ``resident_null_block``,
+    ``attention_indices`` int32 [B, >=K] output + ``attention_block_stride``. seq_lens may
+    then be None and ctx_stride is unused.
     """
     if (pool_v is None) != (hot_v is None):
         raise ValueError("pool_v and hot_v go together")
@@ -92,11 +99,36 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
     if not hot.is_cuda:
         raise ValueError("hot must be a device tensor")
     R, S_r = slot_tokens.shape
+    pg = None
+    if paged is not None:
+        def tab(name):
+            t = paged.get(name)
+            if t is None:
+                return None, 0
+            if t.dim() != 2 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous 2-D int32 tensor")
+            return _dev(t, torch.int32, name), t.shape[1]
+        hbt, hst = tab("hot_block_table")
+        sbt, sst = tab("src_block_table")
+        rbt, rst = tab("resident_block_table")
+        att = paged.get("attention_indices")
+        if att is not None and (att.dim() != 2 or att.shape[0] != B or not att.is_contiguous()):
+            raise ValueError("attention_indices must be a contiguous [B, >=K] int32 tensor")
+        pg = PagedAddressing(
+            hot_block_table=hbt, hot_table_stride=hst, hot_block_size=paged["hot_block_size"],
+            src_block_table=sbt, src_table_stride=sst, src_num_blocks=sst,
+            src_block_size=paged.get("src_block_size", 1),
+            resident_block_table=rbt, resident_table_stride=rst, resident_num_blocks=rst,
+            resident_block_size=paged.get("resident_block_size", 1),
+            resident_null_block=paged.get("resident_null_block", -1),
+            attention_indices=_opt(att, torch.int32, "attention_indices"),
+            attention_row_stride=0 if att is None else att.shape[1],
+            attention_block_stride=paged.get("attention_block_stride", 0))
     a = SwapInArgs(
         B=B, K=K, H=lru.shape[1], S_r=S_r, R=R,
         topk_ids=_dev(topk, torch.int32, "topk"), topk_stride=topk.stride(0),
         req_rows=_dev(req_rows, torch.int64, "req_rows"),
-        seq_lens=_dev(seq_lens, torch.int64, "seq_lens"),
+        seq_lens=None if seq_lens is None else _dev(seq_lens, torch.int64, "seq_lens"),
         num_real=_opt(num_real, torch.int32, "num_real"),
         slot_tokens=_dev(slot_tokens, torch.int32, "slot_tokens"),
         lru=_dev(lru, torch.int16, "lru"),
@@ -108,7 +140,8 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         miss_counts=_opt(miss_counts, torch.int32, "miss_counts"),
         miss_mask=_opt(miss_mask, torch.int32, "miss_mask"),
         pool_v=None if pool_v is None else pool_v.data_ptr(),
-        hot_v=None if hot_v is None else hot_v.data_ptr())
+        hot_v=None if hot_v is None else hot_v.data_ptr(),
+        paged=ctypes.pointer(pg) if pg is not None else None)
     if miss_mask is not None and (tuple(miss_mask.shape) != (B, K) or not miss_mask.is_contiguous()):
         raise ValueError("miss_mask must be a contiguous [B, K] int32 tensor")
     ws = _dev(workspace, torch.uint8, "workspace")
@@ -205,6 +238,19 @@ def store_kv_scatter(*, src: torch.Tensor, dst: torch.Tensor, loc: torch.Tensor,
     check("store_kv_scatter", load().store_kv_scatter(
         _dev(src, torch.uint8, "src"), src.stride(0), _dev(dst, torch.uint8, "dst"), dst.stride(0),
         dst.shape[0], _dev(loc, torch.int64, "loc"), loc.numel(), rb, _stream(stream)))
+
+
+def hisparse_invalidate_written(*, slot_keys: torch.Tensor, rows: torch.Tensor,
+                                written: torch.Tensor, stream=None) -> None:
+    """Empty every slot of state row ``rows[j]`` whose global-id key is ``written[j]``."""
+    if slot_keys.dim() != 2 or not slot_keys.is_contiguous():
+        raise ValueError("slot_keys must be a contiguous [R, S_r] int32 tensor")
+    if rows.numel() != written.numel():
+        raise ValueError("rows and written must have equal lengths")
+    R, S_r = slot_keys.shape
+    check("hisparse_invalidate_written", load().hisparse_invalidate_written(
+        _dev(slot_keys, torch.int32, "slot_keys"), R, S_r, _dev(rows, torch.int64, "rows"),
+        _dev(written, torch.int64, "written"), rows.numel(), _stream(stream)))
 
 
 def hisparse_state_reset(*, slot_tokens: torch.Tensor, lru: torch.Tensor, rows: torch.Tensor,

@@ -20,7 +20,24 @@ STATUS = {0: "HS_OK", -1: "HS_EINVAL", -2: "HS_ERANGE", -3: "HS_EMEMKIND", -4: "
 EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_resolve",
            "hisparse_gather_compact", "hisparse_gather_compact_layers",
            "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_kv_all_layer",
-           "store_kv_scatter", "store_kv_cache", "hisparse_state_reset", "hisparse_last_error")
+           "store_kv_scatter", "store_kv_cache", "hisparse_invalidate_written",
+           "hisparse_state_reset", "hisparse_last_error")
+
+
+class PagedAddressing(ctypes.Structure):
+    """Mirror of ``hs_paged_addressing``."""
+
+    _fields_ = [
+        ("hot_block_table", ctypes.c_void_p), ("hot_table_stride", ctypes.c_int64),
+        ("hot_block_size", ctypes.c_int32),
+        ("src_block_table", ctypes.c_void_p), ("src_table_stride", ctypes.c_int64),
+        ("src_num_blocks", ctypes.c_int32), ("src_block_size", ctypes.c_int32),
+        ("resident_block_table", ctypes.c_void_p), ("resident_table_stride", ctypes.c_int64),
+        ("resident_num_blocks", ctypes.c_int32), ("resident_block_size", ctypes.c_int32),
+        ("resident_null_block", ctypes.c_int32),
+        ("attention_indices", ctypes.c_void_p), ("attention_row_stride", ctypes.c_int64),
+        ("attention_block_stride", ctypes.c_int64),
+    ]
 
 
 class SwapInArgs(ctypes.Structure):
@@ -41,6 +58,7 @@ class SwapInArgs(ctypes.Structure):
         ("out_rows", ctypes.c_void_p), ("miss_counts", ctypes.c_void_p),
         ("miss_mask", ctypes.c_void_p),
         ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
+        ("paged", ctypes.POINTER(PagedAddressing)),
     ]
 
 
@@ -80,6 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.transfer_kv_all_layer.restype = ctypes.c_int
     lib.store_kv_cache.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.store_kv_cache.restype = ctypes.c_int
+    lib.hisparse_invalidate_written.argtypes = [vp, i64, i64, vp, vp, i64, vp]
+    lib.hisparse_invalidate_written.restype = ctypes.c_int
     lib.hisparse_state_reset.argtypes = [vp, vp, vp, i64, i32, i64, i64, vp]
     lib.hisparse_state_reset.restype = ctypes.c_int
     lib.hisparse_last_error.argtypes = []

@@ -143,6 +143,22 @@ __global__ __launch_bounds__(kThreads) void state_reset_kernel(int32_t* slot_tok
   for (int32_t p = threadIdx.x; p < H; p += kThreads) lru[r * H + p] = static_cast<int16_t>(p);
 }
 
+// Write invalidation (vLLM hisparse_invalidate_written_slots_kernel): the
+// workgroup of written entry j clears every slot of state row rows[j] whose
+// key is the rewritten global row written[j]. Different keys never share a
+// slot, so concurrent entries touch disjoint words.
+__global__ __launch_bounds__(kThreads) void invalidate_kernel(int32_t* keys, int64_t R, int64_t S_r,
+                                                              const int64_t* rows,
+                                                              const int64_t* written, int64_t n) {
+  for (int64_t j = blockIdx.x; j < n; j += gridDim.x) {
+    const int64_t r = rows[j], g = written[j];
+    if (r < 0 || r >= R || g < 0) continue;
+    int32_t* row = keys + r * S_r;
+    for (int64_t s = threadIdx.x; s < S_r; s += kThreads)
+      if (static_cast<int64_t>(row[s]) == g) row[s] = -1;
+  }
+}
+
 // Workgroups for a grid-stride copy of `items` chunks: enough to fill every
 // CU several times over, never more than the work needs.
 inline unsigned copy_grid(uint64_t items, int num_cus) {
@@ -310,5 +326,23 @@ extern "C" int hisparse_state_reset(int32_t* slot_tokens, int16_t* lru, const in
                      stream, slot_tokens, lru, rows, H, S_r, R);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "reset launch: %s", hipGetErrorString(e));
+  return HS_OK;
+}
+
+extern "C" int hisparse_invalidate_written(int32_t* slot_keys, int64_t R, int64_t S_r,
+                                           const int64_t* rows, const int64_t* written, int64_t n,
+                                           hipStream_t stream) {
+  if (n < 0 || R < 0 || S_r < 0) return set_error(HS_EINVAL, "sizes must be >= 0");
+  if (n == 0 || R == 0 || S_r == 0) return HS_OK;
+  if (!slot_keys || !rows || !written) return set_error(HS_EINVAL, "a required pointer is NULL");
+  DeviceInfo di;
+  const int rc = device_info(&di);
+  if (rc != HS_OK) return rc;
+  const int64_t cap = 16ll * (di.num_cus > 0 ? di.num_cus : 256);
+  const unsigned grid = static_cast<unsigned>(n < cap ? n : cap);
+  hipLaunchKernelGGL(invalidate_kernel, dim3(grid), dim3(kThreads), 0, stream, slot_keys, R, S_r,
+                     rows, written, n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(HS_ELAUNCH, "invalidate launch: %s", hipGetErrorString(e));
   return HS_OK;
 }

@@ -68,6 +68,19 @@ struct SwapArgs {
   int32_t* miss_mask; // [B, K] or null: 1 where the entry missed and got a slot
   const char* pool_v; // non-MLA caches: V pool / V hot buffer, or null
   char* hot_v;
+  // vLLM-style paged addressing (kPaged instantiations only): hot block
+  // table, source block table, resident block table, attention indices.
+  const int32_t* hbt;
+  int64_t hbt_stride;
+  int32_t hbs;
+  const int32_t* sbt;
+  int64_t sbt_stride;
+  int32_t sbt_nblocks, sbs;
+  const int32_t* rbt;
+  int64_t rbt_stride;
+  int32_t rbt_nblocks, rbs, r_null;
+  int32_t* att;
+  int64_t att_stride, att_block_stride;
   int32_t* count;     // [B] misses of request b
   int64_t* src;       // [B, K] pool row of miss m
   int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
@@ -132,7 +145,11 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // bucketed: four int32 keys per 16-byte bucket, a parallel int16 array with
 // each key's top-k index and a per-bucket count, at most a quarter full, so
 // an insert is almost always one atomicAdd and a lookup one 16-byte read.
-template <bool kSlotRows, bool kPoolRows, int kCopyW>
+// kPaged: vLLM-style addressing -- ids translate through the source block
+// table to global ids, which are the slot keys and the pool rows; resident
+// ids are served from the device cache as they are; slots live where the hot
+// block table says; there is no newest-token slot.
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -168,10 +185,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 
   const int64_t r = a.req_rows[b];
   const int32_t nreal = a.num_real ? *a.num_real : a.B;
-  const int64_t L = a.seq_lens[b];
+  const int64_t L = kPaged ? 0 : a.seq_lens[b];
   if (b >= nreal || r < 0 || r >= a.R) {
     // Padding row (vLLM page's V2 convention): -1 everywhere, no misses.
     for (int i = tid; i < K; i += kThreads) out[i] = -1;
+    if (kPaged && a.att)
+      for (int i = tid; i < K; i += kThreads) a.att[static_cast<int64_t>(b) * a.att_stride + i] = -1;
     if (a.miss_mask)
       for (int i = tid; i < K; i += kThreads) a.miss_mask[static_cast<int64_t>(b) * K + i] = 0;
     if (tid == 0) {
@@ -186,10 +205,15 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   const int64_t* prow = kPoolRows ? a.pool_rows + r * a.ctx_stride : nullptr;
   const int64_t hot_base = r * a.S_r;
   auto row_of = [&](int32_t s) -> int32_t {
+    if constexpr (kPaged) {
+      const int32_t blk = a.hbt[r * a.hbt_stride + s / a.hbs];
+      return blk * a.hbs + s % a.hbs;
+    }
     if constexpr (kSlotRows) return srows[s];
     return static_cast<int32_t>(hot_base + s);
   };
   auto pool_of = [&](int64_t t) -> int64_t {
+    if constexpr (kPaged) return t;            // the key is the global id
     if constexpr (kPoolRows) return prow[t];
     return r * a.ctx_stride + t;
   };
@@ -262,15 +286,45 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = base + u * kThreads + tid;
-      bool valid = i < K && t[u] >= 0 && static_cast<int64_t>(t[u]) < L &&
-                   static_cast<int64_t>(t[u]) < a.ctx_stride;
-      if (valid) {
-        const int64_t pr = pool_of(t[u]);
-        valid = pr >= 0 && pr < a.pool_nrows;
+      if constexpr (kPaged) {
+        // vLLM page, first phase: position -> global id through the source
+        // block table (a physical block of 0 or below has no row), and a
+        // resident row when the resident table holds the position.
+        const int32_t tt = t[u];
+        int64_t g = -1, res = -1;
+        if (i < K) {
+          g = tt;
+          if (a.sbt) {
+            g = -1;
+            if (tt >= 0 && tt / a.sbs < a.sbt_nblocks) {
+              const int32_t pb = a.sbt[r * a.sbt_stride + tt / a.sbs];
+              if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + tt % a.sbs;
+            }
+          }
+          if (g >= a.pool_nrows) g = -1;
+          if (a.rbt && tt >= 0 && tt / a.rbs < a.rbt_nblocks) {
+            const int32_t pb = a.rbt[r * a.rbt_stride + tt / a.rbs];
+            if (pb != a.r_null && pb >= 0) {
+              res = static_cast<int64_t>(pb) * a.rbs + tt % a.rbs;
+              if (res > INT32_MAX) res = -1;
+            }
+          }
+        }
+        ins[u] = i < K && res < 0 && g >= 0;
+        o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
+        t[u] = static_cast<int32_t>(g);            // the key from here on
+        if (ins[u]) s_topk[i] = t[u];
+      } else {
+        bool valid = i < K && t[u] >= 0 && static_cast<int64_t>(t[u]) < L &&
+                     static_cast<int64_t>(t[u]) < a.ctx_stride;
+        if (valid) {
+          const int64_t pr = pool_of(t[u]);
+          valid = pr >= 0 && pr < a.pool_nrows;
+        }
+        const bool newest = valid && static_cast<int64_t>(t[u]) == L - 1;
+        ins[u] = valid && !newest;
+        o[u] = !valid ? -1 : (newest ? row_of(H) : kPending);
       }
-      const bool newest = valid && static_cast<int64_t>(t[u]) == L - 1;
-      ins[u] = valid && !newest;
-      o[u] = !valid ? -1 : (newest ? row_of(H) : kPending);
       bk[u] = bucket_of(t[u], bshift);
     }
     int npend = 0;
@@ -525,6 +579,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         }
       }
       out[i] = o;
+      if (kPaged && a.att)   // vLLM page, store_hot_index
+        a.att[static_cast<int64_t>(b) * a.att_stride + i] =
+            o < 0 ? -1
+                  : static_cast<int32_t>((o / a.hbs) * a.att_block_stride + o % a.hbs);
     }
   }
   // The new LRU order, built in LDS by phase 3, goes out in one coalesced pass.
@@ -576,11 +634,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 // Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
 // (pool row, hot row) and its length to the workspace for the copy kernel;
 // with kCopyW != 0 also copies the rows itself (W-byte chunks).
-template <bool kSlotRows, bool kPoolRows, int kCopyW>
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0);
-  resolve<kSlotRows, kPoolRows, kCopyW>(a, blockIdx.x, lds, lay);
+  resolve<kSlotRows, kPoolRows, kCopyW, kPaged>(a, blockIdx.x, lds, lay);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -636,12 +694,13 @@ int allow_lds(int device, const void* fn, uint32_t bytes) {
 
 // The resolve kernel for the given tables and fused copy width (0 = none).
 template <int kW>
-const void* pick_resolve(bool slot_rows, bool pool_rows) {
+const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged) {
+  if (paged) return reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true>);
   if (slot_rows)
-    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW>)
-                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW>);
-  return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true, kW>)
-                   : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW>);
+    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW, false>)
+                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW, false>);
+  return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true, kW, false>)
+                   : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false>);
 }
 
 #ifndef HS_FUSE_HOST_COPY
@@ -663,8 +722,10 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   if (!a) return set_error(HS_EINVAL, "args is NULL");
   if (a->B < 0 || a->K < 0) return set_error(HS_EINVAL, "B and K must be >= 0");
   if (a->B == 0 || a->K == 0) return kEmptyCall;
-  if (!a->topk_ids || !a->req_rows || !a->seq_lens || !a->slot_tokens || !a->lru || !a->pool ||
-      !a->hot || !a->out_rows)
+  const hs_paged_addressing* pa = a->paged;
+  const bool pg = pa != nullptr;
+  if (!a->topk_ids || !a->req_rows || (!a->seq_lens && !pg) || !a->slot_tokens || !a->lru ||
+      !a->pool || !a->hot || !a->out_rows)
     return set_error(HS_EINVAL, "a required pointer is NULL");
   if (a->H < a->K) return set_error(HS_EINVAL, "hot_size H=%d must be >= top_k K=%d", a->H, a->K);
   if (a->H > 32768) return set_error(HS_ERANGE, "hot_size H=%d exceeds 32768 (int16 slots)", a->H);
@@ -672,14 +733,35 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     return set_error(HS_EINVAL, "region_stride S_r=%lld must be >= H+1", (long long)a->S_r);
   if (a->R <= 0) return set_error(HS_EINVAL, "R must be > 0");
   if (a->topk_stride < a->K) return set_error(HS_EINVAL, "topk_stride must be >= K");
-  if (a->ctx_stride <= 0) return set_error(HS_EINVAL, "ctx_stride must be > 0");
+  if (a->ctx_stride <= 0 && !pg) return set_error(HS_EINVAL, "ctx_stride must be > 0");
+  if (pg) {
+    // vLLM-style addressing: the tables replace slot_rows / pool_rows /
+    // ctx_stride, keys are int32 global ids and rows int32.
+    if (a->slot_rows || a->pool_rows)
+      return set_error(HS_EINVAL, "slot_rows / pool_rows are not used with paged addressing");
+    if (!pa->hot_block_table || pa->hot_block_size <= 0)
+      return set_error(HS_EINVAL, "paged addressing needs a hot block table and block size");
+    if (pa->hot_table_stride * pa->hot_block_size < a->H)
+      return set_error(HS_EINVAL, "the hot block table does not cover H slots");
+    if (pa->src_block_table &&
+        (pa->src_block_size <= 0 || pa->src_num_blocks < 0 || pa->src_table_stride < pa->src_num_blocks))
+      return set_error(HS_EINVAL, "bad source block table geometry");
+    if (pa->resident_block_table &&
+        (pa->resident_block_size <= 0 || pa->resident_num_blocks < 0 ||
+         pa->resident_table_stride < pa->resident_num_blocks))
+      return set_error(HS_EINVAL, "bad resident block table geometry");
+    if (pa->attention_indices && pa->attention_row_stride < a->K)
+      return set_error(HS_EINVAL, "attention_row_stride must be >= K");
+    if (a->pool_nrows > 0x7fffffffll || a->hot_nrows > 0x7fffffffll)
+      return set_error(HS_ERANGE, "paged addressing keeps global ids and rows in int32");
+  }
   if (a->pool_nrows < 0 || a->hot_nrows <= 0) return set_error(HS_EINVAL, "bad pool/hot row counts");
   if (a->row_bytes <= 0 || (a->row_bytes & 3) != 0)
     return set_error(HS_EINVAL, "row_bytes=%lld must be a positive multiple of 4", (long long)a->row_bytes);
   if (a->row_bytes > (1ll << 20)) return set_error(HS_ERANGE, "row_bytes above 1 MiB");
   if (!aligned(a->pool, 4) || !aligned(a->hot, 4))
     return set_error(HS_EINVAL, "pool and hot must be 4-byte aligned");
-  if (!a->slot_rows) {
+  if (!a->slot_rows && !pg) {
     if (a->R * a->S_r > 0x7fffffffll)
       return set_error(HS_ERANGE, "R*S_r exceeds int32 hot-row indices");
     if (a->hot_nrows < a->R * a->S_r)
@@ -726,7 +808,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
   const bool sr = a->slot_rows != nullptr, prw = a->pool_rows != nullptr;
-  const void* resolve_fn = pick_resolve<0>(sr, prw);
+  const void* resolve_fn = pick_resolve<0>(sr, prw, pg);
   if (lay.total > 65536) {
     rc = allow_lds(di.device, resolve_fn, lay.total);
     if (rc != HS_OK) return rc;
@@ -765,7 +847,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // kernel, which spreads every request over many CUs.
   const void* fused_fn = nullptr;
   if (HS_FUSE_HOST_COPY && attr.type == hipMemoryTypeHost) {
-    fused_fn = W == 16 ? pick_resolve<16>(sr, prw) : pick_resolve<4>(sr, prw);
+    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg) : pick_resolve<4>(sr, prw, pg);
     if (lay.total > 65536) {
       rc = allow_lds(di.device, fused_fn, lay.total);
       if (rc != HS_OK) return rc;
@@ -787,6 +869,29 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.pool = pool_dev;
   s.pool_v = pool_v_dev;
   s.hot_v = static_cast<char*>(a->hot_v);
+  if (pg) {
+    s.hbt = pa->hot_block_table;
+    s.hbt_stride = pa->hot_table_stride;
+    s.hbs = pa->hot_block_size;
+    s.sbt = pa->src_block_table;
+    s.sbt_stride = pa->src_table_stride;
+    s.sbt_nblocks = pa->src_num_blocks;
+    s.sbs = pa->src_block_table ? pa->src_block_size : 1;
+    s.rbt = pa->resident_block_table;
+    s.rbt_stride = pa->resident_table_stride;
+    s.rbt_nblocks = pa->resident_num_blocks;
+    s.rbs = pa->resident_block_table ? pa->resident_block_size : 1;
+    s.r_null = pa->resident_null_block;
+    s.att = pa->attention_indices;
+    s.att_stride = pa->attention_row_stride;
+    s.att_block_stride = pa->attention_block_stride;
+  } else {
+    s.hbt = nullptr;
+    s.sbt = nullptr;
+    s.rbt = nullptr;
+    s.att = nullptr;
+    s.hbs = s.sbs = s.rbs = 1;
+  }
   s.pool_nrows = a->pool_nrows;
   s.hot = static_cast<char*>(a->hot);
   s.hot_nrows = a->hot_nrows;

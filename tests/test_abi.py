@@ -203,3 +203,39 @@ def test_swap_in_rejects_half_kv(lib):
     assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
     a.pool_v = 0x300002
     assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+
+
+def test_paged_addressing_validation(lib):
+    from sparse_attention_kv_hisparse_amd._lib import PagedAddressing
+    f = 0x100000
+    good = dict(hot_block_table=f, hot_table_stride=4, hot_block_size=2)
+
+    def call(**kw):
+        pg = PagedAddressing(**{**good, **kw})
+        a = _args(seq_lens=None, ctx_stride=0)
+        a.paged = ctypes.pointer(pg)
+        return lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None)
+
+    assert call(hot_block_table=None) == -1
+    assert call(hot_block_size=0) == -1
+    assert call(hot_table_stride=3) == -1                       # 3 blocks of 2 < H = 8
+    assert call(src_block_table=f, src_block_size=0) == -1
+    assert call(src_block_table=f, src_block_size=4, src_num_blocks=5, src_table_stride=4) == -1
+    assert call(resident_block_table=f, resident_block_size=4, resident_num_blocks=2,
+                resident_table_stride=1) == -1
+    assert call(attention_indices=f, attention_row_stride=3) == -1   # < K = 4
+    a = _args(seq_lens=None)
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+    pg = PagedAddressing(**good)
+    a = _args(slot_rows=f)
+    a.paged = ctypes.pointer(pg)
+    assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+
+
+def test_invalidate_rejects(lib):
+    f = 0x100000
+    g = lib.hisparse_invalidate_written
+    assert g(f, 4, 9, f, f, 0, None) == 0
+    assert g(f, 4, 9, f, f, -1, None) == -1
+    assert g(None, 4, 9, f, f, 3, None) == -1
+    assert g(f, 4, 9, None, f, 3, None) == -1

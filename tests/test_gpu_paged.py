@@ -1,0 +1,107 @@
+"""vLLM-style paged addressing and write invalidation on the GPU, against the
+oracle, bit for bit: random hot, source and resident block tables (null
+blocks, ids past the pool, padding rows), global-id slot keys, attention
+indices, host and device pools, the fused and the split paths, K+V, and
+hisparse_invalidate_written between calls."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from test_oracle_paged import _random_tables
+from workloads import device as wdev
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import sparse_attention_kv_hisparse_amd as hs
+    hs.load()
+    torch.cuda.set_device(0)
+
+
+def _np(t):
+    return t.cpu().numpy() if t.is_cuda else t.numpy()
+
+
+CASES = [
+    # (name, R, B, H, K, ctx, row_bytes, pool kind, split, kv)
+    ("host_fused", 8, 6, 512, 256, 3000, 656, "host", False, False),
+    ("host_split", 8, 6, 512, 256, 3000, 656, "host", True, False),
+    ("device", 10, 8, 600, 300, 4000, 512, "device", False, False),
+    ("host_132B_kv", 6, 4, 256, 200, 2000, 132, "host", False, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_paged_swap_in_matches_oracle(case):
+    import sparse_attention_kv_hisparse_amd as hs
+    name, R, B, H, K, ctx, rb, kind, split, kv = case
+    print(f"  paged {name}: R={R} B={B} H={H} K={K} rb={rb}", flush=True)
+    rng = np.random.default_rng(abs(hash(name)) % (1 << 31))
+    S_r = H + 1
+    paged_np, hot_nrows, pool_nrows = _random_tables(rng, R, H, ctx)
+    cfg = gen.SwapConfig(name, B=B, H=H, K=K, ctx=pool_nrows, row_bytes=rb, steps=1, rho=0.5,
+                         dist="uniform", pool_kind=kind, seed=61)
+    pool = wdev.make_pool(cfg.with_(B=1), kind=kind)[:pool_nrows]
+    pool_v = wdev.make_pool(cfg.with_(B=1, seed=62), kind=kind)[:pool_nrows] if kv else None
+    pool_np = _np(pool)
+    pool_v_np = _np(pool_v) if kv else None
+    keys = torch.full((R, S_r), -1, dtype=torch.int32, device="cuda")
+    lru = torch.tensor(np.tile(np.arange(H, dtype=np.int16), (R, 1)), device="cuda")
+    hot = torch.zeros((hot_nrows, rb), dtype=torch.uint8, device="cuda")
+    hot_v = torch.zeros_like(hot) if kv else None
+    out = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    att = torch.empty((B, K + 3), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
+    paged_dev = {k: (torch.as_tensor(v).cuda() if isinstance(v, np.ndarray) else v)
+                 for k, v in paged_np.items()}
+    paged_dev["attention_indices"] = att
+    paged_dev["attention_block_stride"] = 40
+    o_keys = np.full((R, S_r), -1, np.int32)
+    o_lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
+    o_hot = np.zeros((hot_nrows, rb), np.uint8)
+    o_hot_v = np.zeros_like(o_hot) if kv else None
+    for call in range(8):
+        if call % 4 == 3:
+            rows = rng.integers(-1, R + 1, 40).astype(np.int64)
+            written = np.array([o_keys[r % R, rng.integers(0, H)] for r in rows], np.int64)
+            hs.hisparse_invalidate_written(slot_keys=keys, rows=torch.as_tensor(rows).cuda(),
+                                           written=torch.as_tensor(written).cuda())
+            oracle.invalidate_written(o_keys, rows, written)
+            torch.cuda.synchronize()
+            assert np.array_equal(_np(keys), o_keys), f"call {call}: keys after invalidation"
+            continue
+        req = rng.permutation(R)[:B].astype(np.int64)
+        topk = np.stack([rng.permutation(np.arange(-3, ctx + 5))[:K] for _ in range(B)]).astype(np.int32)
+        nreal = int(rng.integers(1, B + 1)) if call == 2 else -1
+        kw = dict(topk=torch.as_tensor(topk).cuda(), req_rows=torch.as_tensor(req).cuda(),
+                  seq_lens=None, slot_tokens=keys, lru=lru, pool=pool, hot=hot, out_rows=out,
+                  ctx_stride=0, workspace=ws, miss_counts=counts,
+                  num_real=torch.tensor([nreal if nreal >= 0 else B], dtype=torch.int32, device="cuda"),
+                  paged=paged_dev)
+        if kv:
+            kw.update(pool_v=pool_v, hot_v=hot_v)
+        if split:
+            hs.hisparse_resolve(**kw)
+            hs.hisparse_gather_compact(**kw)
+        else:
+            hs.hisparse_swap_in(**kw)
+        o_att = np.full((B, K + 3), 0, np.int32)
+        pg = dict(paged_np, attention_indices=o_att, attention_block_stride=40)
+        o_out, o_cnt = oracle.swap_in(topk=topk, req_rows=req, seq_lens=None, slot_tokens=o_keys,
+                                      lru=o_lru, pool=pool_np, hot=o_hot, ctx_stride=0, num_real=nreal,
+                                      paged=pg, pool_v=pool_v_np, hot_v=o_hot_v)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(out), o_out), f"call {call}: out_rows"
+        assert np.array_equal(_np(counts), o_cnt), f"call {call}: miss_counts"
+        assert np.array_equal(_np(att)[:, :K], o_att[:, :K]), f"call {call}: attention_indices"
+        assert np.array_equal(_np(keys), o_keys), f"call {call}: slot keys"
+        assert np.array_equal(_np(lru), o_lru), f"call {call}: lru"
+        assert np.array_equal(_np(hot), o_hot), f"call {call}: hot buffer"
+        if kv:
+            assert np.array_equal(_np(hot_v), o_hot_v), f"call {call}: V hot buffer"
