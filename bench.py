@@ -16,6 +16,8 @@ Also reported in the same JSON line:
     step and the steps after it;
   * kv_decode: non-MLA caches -- the headline's shape with 1024-byte K and V
     rows in two pinned pools, every miss moving both;
+  * paged: vLLM-style paged addressing (64-row source and hot blocks, global
+    ids as slot keys) on the device-pool and headline traces;
   * plan_replay: the headline trace with index-sharing layers (1 resolving
     layer + 3 replaying its plan): one fused replay launch for all layers
     against one copy launch per layer;
@@ -59,6 +61,7 @@ def parse():
     p.add_argument("--no-adversarial", action="store_true")
     p.add_argument("--no-plan-replay", action="store_true")
     p.add_argument("--no-kv", action="store_true")
+    p.add_argument("--no-paged", action="store_true")
     p.add_argument("--replay-layers", type=int, default=4,
                    help="layers per index-sharing group in the plan-replay leg (1 resolving "
                         "layer + the rest replaying its plan)")
@@ -262,6 +265,54 @@ def run_plan_replay(cfg, layers, warmup, steps, torch, hs, wdev):
     del pools, hots, st, tr, wss
     torch.cuda.empty_cache()
     return dict(rows=int(c.sum()), us_fused=us_fused, us_separate=us_sep, us_replay=us_replay)
+
+
+def run_paged(cfg, warmup, steps, torch, hs, wdev, block=64):
+    """The workload's trace with vLLM-style paged addressing: every request's
+    positions map through a source block table of `block`-row blocks (a
+    seeded permutation of physical blocks, block 0 unused) to global pool
+    rows, and its slots through a hot block table of `block`-slot blocks (a
+    seeded permutation). W warm-up calls, then K hisparse_swap_in calls
+    between two events. Returns dict(us_total, rows)."""
+    rng = np.random.default_rng(cfg.seed + 99)
+    R, B, H, K, ctx = cfg.R, cfg.B, cfg.H, cfg.K, cfg.ctx
+    nsb = -(-ctx // block)
+    src = (rng.permutation(B * nsb) + 1).astype(np.int32).reshape(B, nsb)
+    pool_nrows = (B * nsb + 1) * block
+    nhb = -(-H // block)
+    hot_tab = rng.permutation(R * nhb).astype(np.int32).reshape(R, nhb)
+    log(f"[bench] paged {cfg.name}: building pool ({pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})")
+    pool = wdev.make_pool(cfg.with_(B=1, ctx=pool_nrows))
+    keys = torch.full((R, H + 1), -1, dtype=torch.int32, device="cuda")
+    lru = torch.tensor(np.tile(np.arange(H, dtype=np.int16), (R, 1)), device="cuda")
+    hot = torch.zeros((R * nhb * block, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    counts = torch.empty((warmup + steps, B), dtype=torch.int32, device="cuda")
+    ws = torch.empty(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
+    tr = Trace(cfg, warmup + steps, torch)
+    paged = {"hot_block_table": torch.as_tensor(hot_tab).cuda(), "hot_block_size": block,
+             "src_block_table": torch.as_tensor(src).cuda(), "src_block_size": block}
+    stream = torch.cuda.current_stream()
+
+    def call(t):
+        hs.hisparse_swap_in(topk=tr.topk[t], req_rows=tr.rows, seq_lens=None, slot_tokens=keys,
+                            lru=lru, pool=pool, hot=hot, out_rows=out, ctx_stride=0, workspace=ws,
+                            miss_counts=counts[t], paged=paged, stream=stream)
+
+    for t in range(warmup):
+        call(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(steps):
+        call(warmup + k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0
+    rows = int(counts[warmup:].sum().item())
+    del pool, hot, keys, lru, tr
+    torch.cuda.empty_cache()
+    return dict(us_total=us, rows=rows)
 
 
 def sources_hash(files):
@@ -622,6 +673,29 @@ def main():
                          "unit": "GB/s", "frac": round(kach / peak, 4) if peak else None,
                          "traffic": measured_traffic("kv_decode")},
         }
+
+    if not args.no_paged:
+        # vLLM-style paged addressing (64-row source and hot blocks) on the
+        # device-pool and DeepSeek-V3.2-like traces: the same work as the
+        # flat legs plus the block-table translation.
+        paged_out = {}
+        for pcfg, n, flat in ((gen.DEVPOOL, args.device_pool_steps, out.get("device_pool")),
+                              (cfg, K, out)):
+            pr = run_paged(pcfg, 1, n, torch, hs, wdev)
+            us = pr["us_total"] / n
+            if pcfg.pool_kind == "device":
+                gbs = pr["rows"] * 2 * pcfg.row_bytes / pr["us_total"] / 1e3
+                frac = gbs / HBM_PEAK_GBS
+            else:
+                gbs = pr["rows"] * pcfg.row_bytes / pr["us_total"] / 1e3
+                frac = gbs / peak if peak else None
+            paged_out[pcfg.name] = {
+                "block_size": 64, "steps": n, "us_per_call": round(us, 2),
+                "rows_per_call": round(pr["rows"] / n, 1),
+                "GBps_call": round(gbs, 1), "frac_bound_call": round(frac, 4) if frac else None,
+                "flat_us_per_call": flat.get("us_per_call") if flat else None,
+            }
+        out["paged"] = paged_out
 
     if not args.no_adversarial:
         # cold step (all misses, ids that collide in the pages' low-bit hash),
