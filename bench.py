@@ -21,6 +21,8 @@ Also reported in the same JSON line:
   * plan_replay: the headline trace with index-sharing layers (1 resolving
     layer + 3 replaying its plan): one fused replay launch for all layers
     against one copy launch per layer;
+  * scatter: store_kv_scatter / store_kv_cache of one 8192-row prefill chunk
+    into a 1M-row cache in HBM;
   * all_layer: the fused all-layer transfer (61 layers x 262,144 rows x 656 B,
     8192 pairs) in both directions against the host-link ceiling;
   * host_link: the measured host-link ceiling the host-pool rooflines use;
@@ -62,6 +64,7 @@ def parse():
     p.add_argument("--no-plan-replay", action="store_true")
     p.add_argument("--no-kv", action="store_true")
     p.add_argument("--no-paged", action="store_true")
+    p.add_argument("--no-scatter", action="store_true")
     p.add_argument("--replay-layers", type=int, default=4,
                    help="layers per index-sharing group in the plan-replay leg (1 resolving "
                         "layer + the rest replaying its plan)")
@@ -313,6 +316,41 @@ def run_paged(cfg, warmup, steps, torch, hs, wdev, block=64):
     del pool, hot, keys, lru, tr
     torch.cuda.empty_cache()
     return dict(us_total=us, rows=rows)
+
+
+def run_scatter(torch, hs, n=8192, rb=656, cache_rows=1 << 20, reps=5):
+    """store_kv_scatter and store_kv_cache on one prefill chunk: n rows of rb
+    bytes (contiguous source in HBM) written to seeded distinct rows of a
+    cache of `cache_rows` rows in HBM; the K+V form moves a second, separate
+    pair. A 512 MiB write between repetitions evicts L2 and MALL. Returns
+    median µs of each."""
+    g = torch.Generator(device="cpu").manual_seed(5)
+    src = torch.randint(0, 256, (n, rb), dtype=torch.uint8, generator=g).cuda()
+    src_v = torch.randint(0, 256, (n, rb), dtype=torch.uint8, generator=g).cuda()
+    dst = torch.zeros((cache_rows, rb), dtype=torch.uint8, device="cuda")
+    dst_v = torch.zeros((cache_rows, rb), dtype=torch.uint8, device="cuda")
+    loc = torch.randperm(cache_rows, generator=g)[:n].cuda()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("k", lambda: hs.store_kv_scatter(src=src, dst=dst, loc=loc)),
+                     ("kv", lambda: hs.store_kv_cache(k_src=src, v_src=src_v, k_dst=dst,
+                                                      v_dst=dst_v, loc=loc))):
+        us = []
+        for rep in range(reps + 1):
+            flush.fill_(rep)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            if rep:
+                us.append(e0.elapsed_time(e1) * 1000.0)
+        us.sort()
+        res[name] = us[len(us) // 2]
+    del src, src_v, dst, dst_v, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def sources_hash(files):
@@ -732,6 +770,20 @@ def main():
                       "GBps": round(tbytes / med / 1e3, 2),
                       "frac_host_link": round(tbytes / med / 1e3 / ceil[name], 4) if ceil[name] else None}
                for name, (med, best) in tres.items()},
+        }
+
+    if not args.no_scatter:
+        n, rb = 8192, 656
+        sc = run_scatter(torch, hs, n=n, rb=rb)
+        out["scatter"] = {
+            "workload": "prefill_chunk_scatter_hbm", "rows": n, "row_bytes": rb,
+            "cache_rows": 1 << 20,
+            "store_kv_scatter": {"us_median": round(sc["k"], 2),
+                                 "GBps": round(n * 2 * rb / sc["k"] / 1e3, 1),
+                                 "frac_hbm": round(n * 2 * rb / sc["k"] / 1e3 / HBM_PEAK_GBS, 4)},
+            "store_kv_cache": {"us_median": round(sc["kv"], 2),
+                               "GBps": round(n * 4 * rb / sc["kv"] / 1e3, 1),
+                               "frac_hbm": round(n * 4 * rb / sc["kv"] / 1e3 / HBM_PEAK_GBS, 4)},
         }
 
     if not args.no_cpu_baseline:

@@ -120,12 +120,12 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterSide k, Scatte
         const uint32_t c = j - q * cdiv.d;
         const uint32_t row = kv ? q >> 1 : q;
         const ScatterSide& sd = (kv && (q & 1)) ? v : k;
+        // The source row is always in range (row < n): its load does not wait
+        // for loc, so the two loads are in flight together.
+        const int64_t off = static_cast<int64_t>(c) * W;
+        val[u] = C::load(sd.src + static_cast<int64_t>(row) * sd.src_stride + off);
         const int64_t to = loc[row];
-        if (to >= 0 && to < dst_nrows) {
-          const int64_t off = static_cast<int64_t>(c) * W;
-          val[u] = C::load(sd.src + static_cast<int64_t>(row) * sd.src_stride + off);
-          d[u] = sd.dst + to * sd.dst_stride + off;
-        }
+        if (to >= 0 && to < dst_nrows) d[u] = sd.dst + to * sd.dst_stride + off;
       }
     }
 #pragma unroll

@@ -34,7 +34,10 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kFuseUnroll = 8;             // chunks in flight per lane, fused copy
+#ifndef HS_FUSE_UNROLL
+#define HS_FUSE_UNROLL 8
+#endif
+constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused copy
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
 
 // Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by

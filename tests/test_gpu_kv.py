@@ -141,3 +141,37 @@ def test_store_kv_cache(n, rb, strides, dst_rows):
     torch.cuda.synchronize()
     assert np.array_equal(_np(k_dst), kdn)
     assert np.array_equal(_np(v_dst), vdn)
+
+
+def test_kv_swap_in_full_size():
+    """The non-MLA decode workload at full size (B=32, H=4096, K=2048, 32,768-token
+    contexts, 1024-byte K and V rows in two 1 GiB pinned pools): the cold step and
+    three steady steps, everything compared with the oracle."""
+    import sparse_attention_kv_hisparse_amd as hs
+    cfg = gen.KV_DECODE
+    _log(f"  kv full size: B={cfg.B} K={cfg.K} H={cfg.H} rb={cfg.row_bytes}, building pools")
+    pool = wdev.make_pool(cfg)
+    pool_v = wdev.make_pool(cfg.with_(seed=cfg.seed + 777))
+    st = wdev.DeviceSwapState(cfg)
+    hot_v = torch.zeros_like(st.hot)
+    o_tok, o_lru = gen.initial_state(cfg)
+    o_hot = np.zeros(tuple(st.hot.shape), np.uint8)
+    o_hot_v = np.zeros_like(o_hot)
+    rows = np.arange(cfg.B, dtype=np.int64)
+    for t, topk in enumerate(gen.topk_trace(cfg, 4)):
+        seq = gen.seq_lens(cfg, t)
+        hs.hisparse_swap_in(topk=torch.as_tensor(topk).cuda(), req_rows=torch.as_tensor(rows).cuda(),
+                            seq_lens=torch.as_tensor(seq).cuda(), slot_tokens=st.slot_tokens,
+                            lru=st.lru, pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx,
+                            workspace=st.ws, miss_counts=st.counts, pool_v=pool_v, hot_v=hot_v)
+        o_out, o_cnt = oracle.swap_in(topk=topk, req_rows=rows, seq_lens=seq, slot_tokens=o_tok,
+                                      lru=o_lru, pool=pool.numpy(), hot=o_hot, ctx_stride=cfg.ctx,
+                                      pool_v=pool_v.numpy(), hot_v=o_hot_v)
+        torch.cuda.synchronize()
+        _log(f"  kv full size step {t}: {int(o_cnt.sum())} misses")
+        assert np.array_equal(_np(st.out), o_out), f"step {t}: out_rows"
+        assert np.array_equal(_np(st.counts), o_cnt), f"step {t}: miss_counts"
+        assert np.array_equal(_np(st.slot_tokens), o_tok), f"step {t}: slot_tokens"
+        assert np.array_equal(_np(st.lru), o_lru), f"step {t}: lru"
+        assert np.array_equal(_np(st.hot), o_hot), f"step {t}: K hot buffer"
+        assert np.array_equal(_np(hot_v), o_hot_v), f"step {t}: V hot buffer"

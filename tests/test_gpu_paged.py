@@ -105,3 +105,57 @@ def test_paged_swap_in_matches_oracle(case):
         assert np.array_equal(_np(hot), o_hot), f"call {call}: hot buffer"
         if kv:
             assert np.array_equal(_np(hot_v), o_hot_v), f"call {call}: V hot buffer"
+
+
+def test_paged_full_size_dsv32():
+    """The DeepSeek-V3.2-like shape (B=32, H=4096, K=2048, 32,768-token contexts,
+    pinned-host pool) with vLLM-style addressing: 64-row source blocks (a seeded
+    permutation, block 0 unused) and 64-slot hot blocks; the cold step and three
+    steady steps against the oracle, with attention indices."""
+    import sparse_attention_kv_hisparse_amd as hs
+    cfg = gen.DSV32
+    block = 64
+    rng = np.random.default_rng(77)
+    B, H, K, ctx, rb = cfg.B, cfg.H, cfg.K, cfg.ctx, cfg.row_bytes
+    R = B
+    nsb = ctx // block
+    src = (rng.permutation(B * nsb) + 1).astype(np.int32).reshape(B, nsb)
+    pool_nrows = (B * nsb + 1) * block
+    nhb = H // block
+    hot_tab = rng.permutation(R * nhb).astype(np.int32).reshape(R, nhb)
+    print(f"  paged full size: pool {pool_nrows} rows", flush=True)
+    pool = wdev.make_pool(cfg.with_(B=1, ctx=pool_nrows))
+    keys = torch.full((R, H + 1), -1, dtype=torch.int32, device="cuda")
+    lru = torch.tensor(np.tile(np.arange(H, dtype=np.int16), (R, 1)), device="cuda")
+    hot = torch.zeros((R * nhb * block, rb), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    att = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
+    paged_dev = {"hot_block_table": torch.as_tensor(hot_tab).cuda(), "hot_block_size": block,
+                 "src_block_table": torch.as_tensor(src).cuda(), "src_block_size": block,
+                 "attention_indices": att, "attention_block_stride": 128}
+    o_keys = np.full((R, H + 1), -1, np.int32)
+    o_lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
+    o_hot = np.zeros((R * nhb * block, rb), np.uint8)
+    rows = np.arange(B, dtype=np.int64)
+    for t, topk in enumerate(gen.topk_trace(cfg, 4)):
+        hs.hisparse_swap_in(topk=torch.as_tensor(topk).cuda(), req_rows=torch.as_tensor(rows).cuda(),
+                            seq_lens=None, slot_tokens=keys, lru=lru, pool=pool, hot=hot,
+                            out_rows=out, ctx_stride=0, workspace=ws, miss_counts=counts,
+                            paged=paged_dev)
+        o_att = np.zeros((B, K), np.int32)
+        o_out, o_cnt = oracle.swap_in(
+            topk=topk, req_rows=rows, seq_lens=None, slot_tokens=o_keys, lru=o_lru,
+            pool=pool.numpy(), hot=o_hot, ctx_stride=0,
+            paged={"hot_block_table": hot_tab, "hot_block_size": block, "src_block_table": src,
+                   "src_block_size": block, "attention_indices": o_att,
+                   "attention_block_stride": 128})
+        torch.cuda.synchronize()
+        print(f"  paged full size step {t}: {int(o_cnt.sum())} misses", flush=True)
+        assert np.array_equal(_np(out), o_out), f"step {t}: out_rows"
+        assert np.array_equal(_np(counts), o_cnt), f"step {t}: miss_counts"
+        assert np.array_equal(_np(att), o_att), f"step {t}: attention_indices"
+        assert np.array_equal(_np(keys), o_keys), f"step {t}: slot keys"
+        assert np.array_equal(_np(lru), o_lru), f"step {t}: lru"
+        assert np.array_equal(_np(hot), o_hot), f"step {t}: hot buffer"
