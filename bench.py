@@ -600,7 +600,7 @@ def main():
     # request's copies fused in, so its average launch is the timed pass's
     # per-call time. (Pass 2 still reports the split API's two kernels.)
     us_kernel = r["us_total"]
-    kernel = "resolve_kernel<false, false, 16> (resolution + the request's own row copies)"
+    kernel = "resolve_kernel<false, false, 16, false> (resolution + the request's own row copies)"
     achieved = bytes_link / (us_kernel * 1e-6) / 1e9
     call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
     peak = link["h2d_ceiling_gbs"] if link else None
@@ -664,7 +664,7 @@ def main():
                           "GBps_rows_read_written": round(
                               d["cold_rows"] * 2 * dcfg.row_bytes / d["us_cold"] / 1e3, 1)},
             "effective_GBps_call": round(dcall, 1), "frac_hbm_call": round(dcall / HBM_PEAK_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16>", "achieved": round(dach, 1),
+            "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16, false>", "achieved": round(dach, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("device_pool")},
         }
@@ -706,7 +706,7 @@ def main():
             "split_api": {"us_resolve_kernel": round(kr["us_resolve"] / n, 2),
                           "us_copy_kernel": round(kr["us_copy"] / n, 2)},
             "roofline": {"bound": "host_link",
-                         "kernel": "resolve_kernel<false, false, 16> (resolution + K and V row copies)",
+                         "kernel": "resolve_kernel<false, false, 16, false> (resolution + K and V row copies)",
                          "achieved": round(kach, 2), "peak": round(peak, 2) if peak else None,
                          "unit": "GB/s", "frac": round(kach / peak, 4) if peak else None,
                          "traffic": measured_traffic("kv_decode")},
