@@ -38,6 +38,11 @@ constexpr int kWaves = kThreads / kWave;
 #define HS_FUSE_UNROLL 8
 #endif
 constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused copy
+// Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
+// 1024 lanes exactly), LRU phases four (H = 4096). A lane slot past the end of
+// a pass still costs issue cycles, so the unroll follows the common sizes.
+constexpr int kKU = 2;
+constexpr int kHU = 4;
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
 
 // Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by
@@ -121,13 +126,21 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
   l.hitpos = o; o = align_up(o + 8 * hwords, 16);
   l.missw = o;  o = align_up(o + 8 * kwords, 16);
-  l.wtot = o;   o = align_up(o + 4 * 3 * kWaves + 16, 16);
+  l.wtot = o;   o = align_up(o + 4 * (2 * (kWaves + 1) + 1), 16);
   l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
   l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
   l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
   l.total = o;
   return l;
+}
+
+template <int N>
+__device__ __forceinline__ bool any_of(const bool (&v)[N]) {
+  bool r = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) r |= v[i];
+  return r;
 }
 
 // popcount of the bits of a 64-bit wave mask held by lanes below this one.
@@ -171,10 +184,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int32_t* s_tok = reinterpret_cast<int32_t*>(lds + lay.tok);
   uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
   uint64_t* missw = reinterpret_cast<uint64_t*>(lds + lay.missw);
+  // Cross-wave counts: pre_hit[w] / pre_miss[w] collect the totals of the
+  // waves before w, entry kWaves the grand total; s_pending the pending ids.
   int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
-  int32_t* wt_hit = wtot;
-  int32_t* wt_miss = wtot + kWaves;
-  int32_t* s_pending = wtot + 2 * kWaves;
+  int32_t* pre_hit = wtot;
+  int32_t* pre_miss = wtot + kWaves + 1;
+  int32_t* s_pending = wtot + 2 * (kWaves + 1);
   int16_t* s_lru = reinterpret_cast<int16_t*>(lds + lay.lru);
   int16_t* victim = reinterpret_cast<int16_t*>(lds + lay.victim);
   // Inactive lanes aim their CAS at a private word, so the CAS of every
@@ -222,16 +237,21 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   };
 
   // ---- stage: ids, the LRU row and the slot-token row -----------------------
-  // The first 4096 entries of each land in registers with all loads in flight
-  // at once; the hash table is cleared while they are outstanding.
-  int32_t vi[4];
+  // The first kKU * 1024 ids and kHU * 1024 LRU entries land in registers
+  // with all loads in flight at once; the hash table is cleared while they
+  // are outstanding. Longer rows follow in batches of four per lane.
+  int32_t vi[kKU];
   {
-    int32_t vt[4];
-    int16_t vl[4];
+    int32_t vt[kHU];
+    int16_t vl[kHU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
       vi[u] = x < K ? ids[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const int x = u * kThreads + tid;
       vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
@@ -240,32 +260,46 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
     u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
     for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
-    if (tid == 0) *s_pending = 0;
+    if (tid < 2 * (kWaves + 1) + 1) wtot[tid] = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
       if (x < K) s_topk[x] = vi[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const int x = u * kThreads + tid;
       if (x < H) {
         s_lru[x] = vl[u];
         if (a.stage_tokens) s_tok[x] = vt[u];
       }
     }
   }
-  const int span = K > H ? K : H;
-  for (int base = 4 * kThreads; base < span; base += 4 * kThreads) {
-    int32_t wi[4], wt[4];
-    int16_t wl[4];
+  for (int base = kKU * kThreads; base < K; base += 4 * kThreads) {
+    int32_t wi[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int x = base + u * kThreads + tid;
       wi[u] = x < K ? ids[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < K) s_topk[x] = wi[u];
+    }
+  }
+  for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
+    int32_t wt[4];
+    int16_t wl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
       wl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       wt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int x = base + u * kThreads + tid;
-      if (x < K) s_topk[x] = wi[u];
       if (x < H) {
         s_lru[x] = wl[u];
         if (a.stage_tokens) s_tok[x] = wt[u];
@@ -277,17 +311,33 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // ---- 1. classify ids; bind the newest token; insert pending ids ----------
   // SGLang page: the newest token goes to newest_slot (= H), every other id is
   // hashed. vLLM page: ids outside the pool resolve to -1 and are not misses.
-  for (int base = 0; base < K; base += 4 * kThreads) {
-    int32_t t[4], o[4];
-    uint32_t bk[4];
-    bool ins[4];
+  // Without a pool-row table an id is valid iff 0 <= t < lim, one unsigned
+  // compare: lim folds the sequence length, the row stride and the pool end.
+  uint32_t lim = 0;
+  int32_t newest_t = -1;   // never matches a valid id unless L-1 is one
+  int32_t row_newest = 0;
+  if constexpr (!kPaged) {
+    int64_t l64 = L < a.ctx_stride ? L : a.ctx_stride;
+    if constexpr (!kPoolRows) {
+      const int64_t room = a.pool_nrows - r * a.ctx_stride;
+      l64 = room < l64 ? room : l64;
+    }
+    l64 = l64 < 0 ? 0 : (l64 > INT32_MAX ? INT32_MAX : l64);
+    lim = static_cast<uint32_t>(l64);
+    if (L >= 1 && L - 1 < l64) newest_t = static_cast<int32_t>(L - 1);
+    row_newest = row_of(H);
+  }
+  for (int base = 0; base < K; base += kKU * kThreads) {
+    int32_t t[kKU], o[kKU];
+    uint32_t bk[kKU];
+    bool ins[kKU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int i = base + u * kThreads + tid;
       t[u] = base == 0 ? vi[u] : (i < K ? s_topk[i] : 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int i = base + u * kThreads + tid;
       if constexpr (kPaged) {
         // vLLM page, first phase: position -> global id through the source
@@ -318,33 +368,34 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         t[u] = static_cast<int32_t>(g);            // the key from here on
         if (ins[u]) s_topk[i] = t[u];
       } else {
-        bool valid = i < K && t[u] >= 0 && static_cast<int64_t>(t[u]) < L &&
-                     static_cast<int64_t>(t[u]) < a.ctx_stride;
-        if (valid) {
-          const int64_t pr = pool_of(t[u]);
-          valid = pr >= 0 && pr < a.pool_nrows;
+        bool valid = i < K && static_cast<uint32_t>(t[u]) < lim;
+        if constexpr (kPoolRows) {
+          if (valid) {
+            const int64_t pr = prow[t[u]];
+            valid = pr >= 0 && pr < a.pool_nrows;
+          }
         }
-        const bool newest = valid && static_cast<int64_t>(t[u]) == L - 1;
+        const bool newest = valid && t[u] == newest_t;
         ins[u] = valid && !newest;
-        o[u] = !valid ? -1 : (newest ? row_of(H) : kPending);
+        o[u] = !valid ? -1 : (newest ? row_newest : kPending);
       }
       bk[u] = bucket_of(t[u], bshift);
     }
     int npend = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) npend += __popcll(__ballot(ins[u]));
+    for (int u = 0; u < kKU; ++u) npend += __popcll(__ballot(ins[u]));
     // Each pending id takes the next entry of its home bucket with one LDS
     // atomicAdd on the bucket's count; a full bucket passes it on to the next
     // bucket (linear probing over buckets). A lookup stops at the first bucket
     // that is not full, which this order guarantees to be past the key; the
     // table is at most half full, so insertion terminates.
     const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
-    while (__ballot(ins[0] | ins[1] | ins[2] | ins[3]) != 0) {
-      uint32_t p[4];
+    while (__ballot(any_of(ins)) != 0) {
+      uint32_t p[kKU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
+      for (int u = 0; u < kKU; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kKU; ++u) {
         if (ins[u] && p[u] < 4) {
           hkey[4 * bk[u] + p[u]] = t[u];
           hidx[4 * bk[u] + p[u]] = static_cast<int16_t>(base + u * kThreads + tid);
@@ -355,7 +406,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int i = base + u * kThreads + tid;
       if (i < K) s_out[i] = o[u];
     }
@@ -383,10 +434,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int p = h0 + c0 + u * kWave + lane;
       sl[u] = (c0 + u * kWave < segH && p < H) ? s_lru[p] : -1;
     }
+    // The staging choice is uniform: branching once keeps all four token
+    // reads of a lane in flight together.
+    if (a.stage_tokens) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? s_tok[sl[u]] : -1;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? tokens[sl[u]] : -1;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool ok = sl[u] >= 0 && sl[u] < H;
-      key[u] = ok ? (a.stage_tokens ? s_tok[sl[u]] : tokens[sl[u]]) : -1;
       act[u] = key[u] >= 0;
       bk[u] = bucket_of(key[u], bshift);
       idx[u] = -1;
@@ -436,7 +494,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       }
     }
   }
-  if (lane == 0) wt_hit[wave] = run;
+  // Wave w adds its total to the prefix of every later wave and to the grand
+  // total: one LDS atomic per lane, no scan after the barrier.
+  if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
   __syncthreads();
 
   // ---- 3. victims, the new LRU order, miss words ----------------------------
@@ -444,65 +504,63 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // in miss order), then the hits -- every group in its old order. A
   // position's rank among hits is the hits of earlier waves, plus this wave's
   // earlier chunks, plus the hit lanes below it.
-  int hits = 0, hits_before = 0;
-  {
-    const int4* w4 = reinterpret_cast<const int4*>(wt_hit);
-#pragma unroll
-    for (int q = 0; q < kWaves / 4; ++q) {
-      const int4 v = w4[q];
-      const int t4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        hits += t4[k];
-        hits_before += (4 * q + k) < wave ? t4[k] : 0;
-      }
-    }
-  }
+  const int hits = pre_hit[kWaves];
+  const int hits_before = pre_hit[wave];
   const int E = H - hits;            // evictable slots
   const int M = pending_n - hits;    // misses (<= E because K <= H)
   run = hits_before;
+  int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
   for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += 4 * kWave) {
-    uint64_t wd[4];
+    // The chunk's four hit words arrive in one LDS read (lanes 0-3) and are
+    // broadcast with readlane, so no read waits on the one before it.
     int16_t sp[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = h0 + c0 + u * kWave;     // chunk start
       const bool in = c0 + u * kWave < segH && q < H;
-      wd[u] = in ? hitpos[q >> 6] : 0;
       sp[u] = (in && q + lane < H) ? s_lru[q + lane] : static_cast<int16_t>(0);
+    }
+    const uint64_t wl = (lane < 4 && c0 + lane * kWave < segH) ? hitpos[((h0 + c0) >> 6) + lane] : 0;
+    uint64_t wd[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = h0 + c0 + u * kWave;
+      const bool in = c0 + u * kWave < segH && q < H;
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(wl), u);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(wl >> 32), u);
+      wd[u] = in ? (static_cast<uint64_t>(hi) << 32 | lo) : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      if (c0 + u * kWave < segH && p < H) {
+      if (c0 + u * kWave < segH) {       // uniform
+        const bool h = (wd[u] >> lane) & 1ull;
         const int hr = run + rank_below(wd[u]);
-        int np;
-        if ((wd[u] >> lane) & 1ull) {
-          np = E + hr;
-        } else {
-          const int e = p - hr;
-          if (e < M) {
-            victim[e] = sp[u];
-            np = E - M + e;
-          } else {
-            np = e - M;
-          }
+        const int e = p - hr;              // rank among evictables
+        const bool vic = !h && e < M;
+        // hit: E + hr; victim: E - M + e; other evictable: e - M
+        const int hm = -static_cast<int>(h);
+        const int np = (hm & (E + hr)) | (~hm & (e - M + (vic ? E : 0)));
+        if (p < H) {
+          // Lanes that are not victims write their private sink instead,
+          // which keeps this step free of branches.
+          *(vic ? &victim[e] : sink16) = sp[u];
+          nlru[np] = sp[u];
         }
-        nlru[np] = sp[u];
       }
       run += __popcll(wd[u]);
     }
   }
   run = 0;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
-    int32_t so[4];
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+    int32_t so[kKU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int i = k0 + c0 + u * kWave + lane;
       so[u] = (c0 + u * kWave < segK && i < K) ? s_out[i] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int q = k0 + c0 + u * kWave;
       const uint64_t mm = __ballot(so[u] == kPending);
       if (c0 + u * kWave < segK && q < K) {
@@ -511,26 +569,14 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       }
     }
   }
-  if (lane == 0) wt_miss[wave] = run;
+  if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_miss[lane], run);
   __syncthreads();
 
   // ---- 4. misses in top-k order take victims; outputs; copy list -----------
   // Each wave finishes its own segment of top-k entries: the entries it does
   // not fill were final before the last barrier.
-  int m_total = 0, miss_before = 0;
-  {
-    const int4* w4 = reinterpret_cast<const int4*>(wt_miss);
-#pragma unroll
-    for (int q = 0; q < kWaves / 4; ++q) {
-      const int4 v = w4[q];
-      const int t4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        m_total += t4[k];
-        miss_before += (4 * q + k) < wave ? t4[k] : 0;
-      }
-    }
-  }
+  const int m_total = pre_miss[kWaves];
+  const int miss_before = pre_miss[wave];
   int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
   int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
@@ -539,11 +585,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
   int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
   run = miss_before;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += 4 * kWave) {
-    uint64_t wd[4];
-    int32_t so[4], t[4];
+  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+    uint64_t wd[kKU];
+    int32_t so[kKU], t[kKU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int q = k0 + c0 + u * kWave;
       const int i = q + lane;
       const bool in = c0 + u * kWave < segK && q < K;
@@ -551,15 +597,15 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       so[u] = (in && i < K) ? s_out[i] : 0;
       t[u] = (in && i < K) ? s_topk[i] : 0;
     }
-    int m[4], v[4];
+    int m[kKU], v[kKU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       m[u] = run + rank_below(wd[u]);
       run += __popcll(wd[u]);
       v[u] = (((wd[u] >> lane) & 1ull) && m[u] < M) ? victim[m[u]] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kKU; ++u) {
       const int i = k0 + c0 + u * kWave + lane;
       if (c0 + u * kWave >= segK || i >= K) continue;
       int32_t o = so[u];
