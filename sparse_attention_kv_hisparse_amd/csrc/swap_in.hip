@@ -35,7 +35,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 #ifndef HS_FUSE_UNROLL
-#define HS_FUSE_UNROLL 8
+#define HS_FUSE_UNROLL 12
 #endif
 constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused copy
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
@@ -237,22 +237,32 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   };
 
   // ---- stage: ids, the LRU row and the slot-token row -----------------------
-  // The first kKU * 1024 ids and kHU * 1024 LRU entries land in registers
-  // with all loads in flight at once; the hash table is cleared while they
-  // are outstanding. Longer rows follow in batches of four per lane.
+  // The first kKU * 1024 ids, the first 256 LRU positions of this wave's
+  // segment (kept in registers for the probe and the victim step, which work
+  // on the same positions) and kHU * 1024 slot tokens land with all loads in
+  // flight at once; the hash table is cleared while they are outstanding.
+  // Longer rows follow in batches of four per lane.
+  const int segH = static_cast<int>(wave_segment(H));
+  const int segK = static_cast<int>(wave_segment(K));
+  const int h0 = wave * segH;
+  const int k0 = wave * segK;
   int32_t vi[kKU];
+  int16_t vl[4];   // LRU entries at h0 + u*64 + lane
   {
     int32_t vt[kHU];
-    int16_t vl[kHU];
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
       vi[u] = x < K ? ids[x] : 0;
     }
 #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      vl[u] = (u * kWave < segH && p < H) ? lru[p] : static_cast<int16_t>(-1);
+    }
+#pragma unroll
     for (int u = 0; u < kHU; ++u) {
       const int x = u * kThreads + tid;
-      vl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
       vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
     }
     // Keys start empty (-1, never a token id) and bucket counts at 0.
@@ -267,11 +277,15 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       if (x < K) s_topk[x] = vi[u];
     }
 #pragma unroll
-    for (int u = 0; u < kHU; ++u) {
-      const int x = u * kThreads + tid;
-      if (x < H) {
-        s_lru[x] = vl[u];
-        if (a.stage_tokens) s_tok[x] = vt[u];
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      if (u * kWave < segH && p < H) s_lru[p] = vl[u];
+    }
+    if (a.stage_tokens) {
+#pragma unroll
+      for (int u = 0; u < kHU; ++u) {
+        const int x = u * kThreads + tid;
+        if (x < H) s_tok[x] = vt[u];
       }
     }
   }
@@ -288,21 +302,31 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       if (x < K) s_topk[x] = wi[u];
     }
   }
-  for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
-    int32_t wt[4];
+  for (int c0 = 4 * kWave; c0 < segH; c0 += 4 * kWave) {    // H > 4096
     int16_t wl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
-      wl[u] = x < H ? lru[x] : static_cast<int16_t>(0);
-      wt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
+      const int p = h0 + c0 + u * kWave + lane;
+      wl[u] = (c0 + u * kWave < segH && p < H) ? lru[p] : static_cast<int16_t>(0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
-      if (x < H) {
-        s_lru[x] = wl[u];
-        if (a.stage_tokens) s_tok[x] = wt[u];
+      const int p = h0 + c0 + u * kWave + lane;
+      if (c0 + u * kWave < segH && p < H) s_lru[p] = wl[u];
+    }
+  }
+  if (a.stage_tokens) {
+    for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
+      int32_t wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        wt[u] = x < H ? tokens[x] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        if (x < H) s_tok[x] = wt[u];
       }
     }
   }
@@ -420,10 +444,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // wins (a second slot with the same token -- corrupt state -- stays
   // evictable instead of serving the entry twice).
   const int pending_n = *s_pending;
-  const int segH = static_cast<int>(wave_segment(H));
-  const int segK = static_cast<int>(wave_segment(K));
-  const int h0 = wave * segH;
-  const int k0 = wave * segK;
   int run = 0;
   for (int c0 = 0; c0 < segH; c0 += 4 * kWave) {
     int32_t sl[4], key[4], idx[4];
@@ -432,7 +452,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      sl[u] = (c0 + u * kWave < segH && p < H) ? s_lru[p] : -1;
+      sl[u] = c0 == 0 ? vl[u] : ((c0 + u * kWave < segH && p < H) ? s_lru[p] : -1);
     }
     // The staging choice is uniform: branching once keeps all four token
     // reads of a lane in flight together.
@@ -518,7 +538,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     for (int u = 0; u < 4; ++u) {
       const int q = h0 + c0 + u * kWave;     // chunk start
       const bool in = c0 + u * kWave < segH && q < H;
-      sp[u] = (in && q + lane < H) ? s_lru[q + lane] : static_cast<int16_t>(0);
+      sp[u] = c0 == 0 ? vl[u] : ((in && q + lane < H) ? s_lru[q + lane] : static_cast<int16_t>(0));
     }
     const uint64_t wl = (lane < 4 && c0 + lane * kWave < segH) ? hitpos[((h0 + c0) >> 6) + lane] : 0;
     uint64_t wd[4];
@@ -635,7 +655,14 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     }
   }
   // The new LRU order, built in LDS by phase 3, goes out in one coalesced pass.
-  for (int p = tid; p < H; p += kThreads) lru[p] = nlru[p];
+  if ((H & 3) == 0 && (reinterpret_cast<uintptr_t>(lru) & 7) == 0) {
+    // four slots per 8-byte store
+    const uint64_t* n8 = reinterpret_cast<const uint64_t*>(nlru);
+    uint64_t* l8 = reinterpret_cast<uint64_t*>(lru);
+    for (int q = tid; q < H / 4; q += kThreads) l8[q] = n8[q];
+  } else {
+    for (int p = tid; p < H; p += kThreads) lru[p] = nlru[p];
+  }
   if (tid == 0) {
     a.count[b] = m_total;
     if (a.miss_counts) a.miss_counts[b] = m_total;
