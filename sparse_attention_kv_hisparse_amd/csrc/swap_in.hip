@@ -473,11 +473,16 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     // query. Buckets fill in entry order, so a bucket whose last key is empty
     // is not full and ends a miss. Ends when no lane of the wave is still
     // searching; the top-k index of each found key is read once afterwards.
-    int pos[4] = {-1, -1, -1, -1};
+    // The bucket's four top-k indices (8 bytes) are read beside its keys, so
+    // a found key's index needs no further LDS round trip.
     while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
       u32x4 kv[4];
+      uint64_t iv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
+      for (int u = 0; u < 4; ++u) {
+        kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
+        iv[u] = reinterpret_cast<const uint64_t*>(hidx)[bk[u]];
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int32_t kk = key[u];
@@ -486,17 +491,14 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         const bool m2 = static_cast<int32_t>(kv[u].z) == kk;
         const bool m3 = static_cast<int32_t>(kv[u].w) == kk;
         const bool found = m0 | m1 | m2 | m3;
-        const int j = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : 3));
+        const uint32_t j = m0 ? 0u : (m1 ? 1u : (m2 ? 2u : 3u));
         const bool open = static_cast<int32_t>(kv[u].w) == -1;
-        pos[u] = (act[u] && found) ? static_cast<int>(4 * bk[u]) + j : pos[u];
+        const int ii = static_cast<int16_t>(static_cast<uint32_t>(iv[u] >> (16 * j)) & 0xffffu);
+        const int take = -static_cast<int>(act[u] && found);   // all ones or zero
+        idx[u] = (ii & take) | (idx[u] & ~take);
         act[u] = act[u] && !found && !open;
         bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
       }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int16_t ii = hidx[pos[u] >= 0 ? pos[u] : 0];
-      idx[u] = pos[u] >= 0 ? static_cast<int>(ii) : -1;
     }
     int32_t prev[4];
 #pragma unroll
