@@ -73,7 +73,10 @@ def _small(**kw):
     dict(row_bytes=4), dict(row_bytes=132),     # 4-byte path
     dict(row_bytes=1152, pool_kind="device"),
     dict(B=1, H=2048, K=2048, ctx=4096),        # one request, all K = H
-], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single"])
+    dict(H=16384, K=2048, ctx=40000, B=2, steps=3),   # slot tokens too big to stage in LDS
+    dict(H=16384, K=2048, ctx=40000, B=2, steps=3, pool_kind="device"),
+], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single",
+        "unstaged_host", "unstaged_dev"])
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
