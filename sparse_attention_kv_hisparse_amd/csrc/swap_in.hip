@@ -149,9 +149,9 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
 }
 
-// Resolve request b (one workgroup). Leaves the miss list in LDS (msrc/mdst,
-// reusing the hash area) and returns the miss count; all state and outputs
-// are written to global memory.
+// Resolve request b (one workgroup): outputs, state updates and the miss list
+// go to global memory; with kCopyW != 0 the workgroup then copies its own
+// missed rows from a copy of the list kept in LDS (phase 5).
 // kSlotRows / kPoolRows: whether the slot-row and pool-row tables are given.
 // Without them no global load follows the first global store, so no wait on
 // outstanding stores (vmcnt counts both) ever stalls a phase.
