@@ -791,6 +791,7 @@ struct Plan {
   const void* resolve_fn;   // resolution only
   const void* fused_fn;     // resolution + the request's own copies, or null
   LdsLayout lay;
+  bool host_pool;           // the pool is pinned host memory
   int W;
   int64_t C;
   int num_cus;
@@ -993,6 +994,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   pl->resolve_fn = resolve_fn;
   pl->fused_fn = fused_fn;
   pl->lay = lay;
+  pl->host_pool = attr.type == hipMemoryTypeHost;
   pl->W = W;
   pl->C = C;
   pl->num_cus = di.num_cus;
@@ -1026,7 +1028,7 @@ int launch_copy(Plan& pl, hipStream_t stream) {
   l.layers = 1;
   l.cdiv = pl.s.cdiv;
   l.ldiv = make_fastdiv(1);
-  return launch_swap_copy(l, pl.W, pl.num_cus, stream);
+  return launch_swap_copy(l, pl.W, pl.num_cus, stream, pl.host_pool);
 }
 
 }  // namespace
