@@ -41,10 +41,15 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 // ---------------------------------------------------------------------------
 // Copy engine: rows are moved as independent 16-byte (or 4-byte) chunks, one
 // per lane, with consecutive lanes on consecutive chunks of a row so a wave's
-// accesses coalesce. Loads and stores are nontemporal: pool rows are read
-// once and hot rows are not re-read by the copy. Measured on gfx950 with cold
-// caches, nontemporal loads beat cached ones by ~30% on scattered 656-byte
-// rows (cached loads allocate lines that then have to be evicted).
+// accesses coalesce. Loads are nontemporal: pool rows are read once, and on
+// gfx950 with cold caches nontemporal loads beat cached ones by ~30% on
+// scattered 656-byte rows (cached loads allocate lines that then have to be
+// evicted). Stores are ordinary write-back stores: a row that ends inside a
+// 128-byte line leaves a partial line, which in L2 can merge with the
+// neighbouring row's write (or be written back as one unit) instead of
+// reaching HBM as a partial write. Measured against nontemporal stores on the
+// device-pool decode step: 33.5 -> 29.5 us per copy launch, with every other
+// copy (host pool, all-layer, scatter) the same or faster.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
@@ -58,9 +63,7 @@ struct Chunk<16> {
   static __device__ __forceinline__ T load(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   }
-  static __device__ __forceinline__ void store(char* p, T v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  }
+  static __device__ __forceinline__ void store(char* p, T v) { *reinterpret_cast<u32x4*>(p) = v; }
 };
 
 template <>
@@ -69,9 +72,7 @@ struct Chunk<4> {
   static __device__ __forceinline__ T load(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   }
-  static __device__ __forceinline__ void store(char* p, T v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-  }
+  static __device__ __forceinline__ void store(char* p, T v) { *reinterpret_cast<uint32_t*>(p) = v; }
 };
 
 // Chunks a row of `row_bytes` splits into at width W.
