@@ -570,8 +570,9 @@ def cpu_baseline(cfg, warmup, steps, min_seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every GPU box here has "
-              f"one GPU and this path has no multi-GPU leg.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): requests shard across "
+              f"GPUs with no exchange between them, so there is no multi-GPU leg to time.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import sparse_attention_kv_hisparse_amd as hs
