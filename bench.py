@@ -406,10 +406,10 @@ def host_link_ceiling(torch, hs):
     dp = torch.tensor([dev.data_ptr()], dtype=torch.int64, device="cuda")
     res["zero_copy_h2d_gbs"] = best(lambda: hs.transfer_rows_all_layer(
         src_layer_ptrs=hp, dst_layer_ptrs=dp, src_idx=idx, dst_idx=idx, row_bytes=rb,
-        src_nrows=rows, dst_nrows=rows))
+        src_nrows=rows, dst_nrows=rows, host_link=True))
     res["zero_copy_d2h_gbs"] = best(lambda: hs.transfer_rows_all_layer(
         src_layer_ptrs=dp, dst_layer_ptrs=hp, src_idx=idx, dst_idx=idx, row_bytes=rb,
-        src_nrows=rows, dst_nrows=rows))
+        src_nrows=rows, dst_nrows=rows, host_link=True))
     res["h2d_ceiling_gbs"] = max(res["memcpy_h2d_gbs"], res["zero_copy_h2d_gbs"])
     res["d2h_ceiling_gbs"] = max(res["memcpy_d2h_gbs"], res["zero_copy_d2h_gbs"])
     del host, dev
@@ -431,7 +431,7 @@ def calibrate(torch, hs):
         hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=idx, dst_idx=idx,
                                    row_bytes=rb, src_nrows=n // rb, dst_nrows=n // rb)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "transfer_kernel<16>", "bytes_read_per_launch": n,
+    print(json.dumps({"calibration": "transfer_kernel<16, 4>", "bytes_read_per_launch": n,
                       "bytes_written_per_launch": n, "launches": 3}), flush=True)
 
 
@@ -479,7 +479,8 @@ def copy_ceilings(torch, hs):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
             hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=src, dst_idx=dst,
-                                       row_bytes=rb, src_nrows=pool.shape[0], dst_nrows=hot.shape[0])
+                                       row_bytes=rb, src_nrows=pool.shape[0], dst_nrows=hot.shape[0],
+                                       host_link=kind == "host")
             e1.record(s)
             torch.cuda.synchronize()
             if rep:
@@ -499,7 +500,8 @@ def copy_ceilings(torch, hs):
 def run_all_layer(torch, hs, reps=5):
     """The fused all-layer transfer at full size: 61 layers x 262,144 rows x
     656 B, 8192 index pairs, one call per repetition, per direction (offload =
-    HBM -> pinned host, load = pinned host -> HBM). A 512 MiB write between
+    HBM -> pinned host, load = pinned host -> HBM), with the host-link launch
+    shape (one side is host memory in both directions). A 512 MiB write between
     repetitions evicts L2 and MALL. Returns per-direction µs (median, best)."""
     from workloads import gen
     cfg = gen.ALL_LAYER
@@ -522,7 +524,7 @@ def run_all_layer(torch, hs, reps=5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
             hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=si, dst_idx=di,
-                                       row_bytes=rb, src_nrows=rows, dst_nrows=rows)
+                                       row_bytes=rb, src_nrows=rows, dst_nrows=rows, host_link=True)
             e1.record(s)
             torch.cuda.synchronize()
             if rep:

@@ -282,11 +282,18 @@ size_t hs_swap_in_workspace_layout(int32_t B, int32_t K, size_t* count_offset, s
  * Pairs with an index outside [0, src_nrows) / [0, dst_nrows) are skipped.
  * dst indices must be unique and source and destination rows must not overlap.
  * row_bytes > 0, multiple of 4; n == 0 or num_layers == 0 returns HS_OK.
+ * flags: 0, or HS_TRANSFER_HOST_LINK when one side is pinned host memory (the
+ * offload and load directions). The library cannot see where the layer bases
+ * point; with the flag the launch uses one workgroup per two CUs, each lane
+ * keeping 8 chunks in flight, which moves more over the host link than the
+ * HBM-sized launch and leaves the other CUs to concurrent work. The bytes
+ * written are the same either way. Any other bit set: HS_EINVAL.
  */
+#define HS_TRANSFER_HOST_LINK 1u
 int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
                             const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
                             int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
-                            int64_t dst_nrows, hipStream_t stream);
+                            int64_t dst_nrows, uint32_t flags, hipStream_t stream);
 
 /*
  * transfer_kv_all_layer -- the non-MLA form of transfer_rows_all_layer.
@@ -298,14 +305,14 @@ int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_
  * Four device uint64 [num_layers] arrays of layer base addresses; K and V
  * layers have the same row counts (src_nrows, dst_nrows) and row_bytes.
  * Everything else (alignment, directions, skipped pairs, index width,
- * uniqueness, errors) is as for transfer_rows_all_layer; all 2 * num_layers
- * streams move in one launch.
+ * uniqueness, flags, errors) is as for transfer_rows_all_layer; all
+ * 2 * num_layers streams move in one launch.
  */
 int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs, const uint64_t* v_src_layer_ptrs,
                           const uint64_t* k_dst_layer_ptrs, const uint64_t* v_dst_layer_ptrs,
                           const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
                           int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
-                          int64_t dst_nrows, hipStream_t stream);
+                          int64_t dst_nrows, uint32_t flags, hipStream_t stream);
 
 /*
  * store_kv_scatter -- write rows into a cache at given row indices.

@@ -176,10 +176,15 @@ def hisparse_gather_compact_layers(*, workspace: torch.Tensor, B: int, K: int,
         _stream(stream)))
 
 
+HOST_LINK = 1   # HS_TRANSFER_HOST_LINK
+
+
 def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: torch.Tensor,
                             src_idx: torch.Tensor, dst_idx: torch.Tensor, row_bytes: int,
-                            src_nrows: int, dst_nrows: int, stream=None) -> None:
-    """All-layer indexed row copy; layer pointer arrays are device uint64 (torch int64) [L]."""
+                            src_nrows: int, dst_nrows: int, host_link: bool = False,
+                            stream=None) -> None:
+    """All-layer indexed row copy; layer pointer arrays are device uint64 (torch int64) [L].
+    ``host_link``: one side is pinned host memory (launch shaped for the host link)."""
     L = src_layer_ptrs.numel()
     if dst_layer_ptrs.numel() != L or src_idx.numel() != dst_idx.numel():
         raise ValueError("pointer arrays / index arrays must have equal lengths")
@@ -187,15 +192,17 @@ def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: tor
         _dev(src_layer_ptrs, torch.int64, "src_layer_ptrs"),
         _dev(dst_layer_ptrs, torch.int64, "dst_layer_ptrs"),
         _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
-        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, _stream(stream)))
+        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, HOST_LINK if host_link else 0,
+        _stream(stream)))
 
 
 def transfer_kv_all_layer(*, k_src_layer_ptrs: torch.Tensor, v_src_layer_ptrs: torch.Tensor,
                           k_dst_layer_ptrs: torch.Tensor, v_dst_layer_ptrs: torch.Tensor,
                           src_idx: torch.Tensor, dst_idx: torch.Tensor, row_bytes: int,
-                          src_nrows: int, dst_nrows: int, stream=None) -> None:
+                          src_nrows: int, dst_nrows: int, host_link: bool = False,
+                          stream=None) -> None:
     """K+V all-layer indexed row copy; the four layer pointer arrays are device
-    uint64 (torch int64) [L]."""
+    uint64 (torch int64) [L]. ``host_link`` as for transfer_rows_all_layer."""
     L = k_src_layer_ptrs.numel()
     if not (v_src_layer_ptrs.numel() == k_dst_layer_ptrs.numel() == v_dst_layer_ptrs.numel() == L):
         raise ValueError("layer pointer arrays must have equal lengths")
@@ -207,7 +214,8 @@ def transfer_kv_all_layer(*, k_src_layer_ptrs: torch.Tensor, v_src_layer_ptrs: t
         _dev(k_dst_layer_ptrs, torch.int64, "k_dst_layer_ptrs"),
         _dev(v_dst_layer_ptrs, torch.int64, "v_dst_layer_ptrs"),
         _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
-        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, _stream(stream)))
+        src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, HOST_LINK if host_link else 0,
+        _stream(stream)))
 
 
 def store_kv_cache(*, k_src: torch.Tensor, v_src: torch.Tensor, k_dst: torch.Tensor,

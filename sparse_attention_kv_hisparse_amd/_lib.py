@@ -90,11 +90,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     szp = ctypes.POINTER(ctypes.c_size_t)
     lib.hs_swap_in_workspace_layout.argtypes = [i32, i32, szp, szp, szp]
     lib.hs_swap_in_workspace_layout.restype = sz
-    lib.transfer_rows_all_layer.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
+    u32 = ctypes.c_uint32
+    lib.transfer_rows_all_layer.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, u32, vp]
     lib.transfer_rows_all_layer.restype = ctypes.c_int
     lib.store_kv_scatter.argtypes = [vp, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.store_kv_scatter.restype = ctypes.c_int
-    lib.transfer_kv_all_layer.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
+    lib.transfer_kv_all_layer.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, u32, vp]
     lib.transfer_kv_all_layer.restype = ctypes.c_int
     lib.store_kv_cache.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.store_kv_cache.restype = ctypes.c_int

@@ -21,7 +21,8 @@ namespace hs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;          // chunks in flight per lane, HBM-sized launches
+constexpr int kHostLinkUnroll = 8;  // ... and with HS_TRANSFER_HOST_LINK
 constexpr int kMaxStagedLayers = 256;
 
 // Layer bases: streams [0, lk) come from the K arrays, [lk, num_layers) from
@@ -34,7 +35,7 @@ struct LayerPtrs {
   int32_t lk;
 };
 
-template <int W>
+template <int W, int U>
 __global__ __launch_bounds__(kThreads) void transfer_kernel(
     LayerPtrs lp, const int64_t* __restrict__ src_idx, const int64_t* __restrict__ dst_idx,
     uint32_t total, int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
@@ -52,12 +53,12 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
     }
     __syncthreads();
   }
-  const uint32_t step = gridDim.x * kThreads * kUnroll;
-  for (uint32_t j0 = blockIdx.x * kThreads * kUnroll + threadIdx.x; j0 < total; j0 += step) {
-    typename C::T v[kUnroll];
-    char* d[kUnroll];
+  const uint32_t step = gridDim.x * kThreads * U;
+  for (uint32_t j0 = blockIdx.x * kThreads * U + threadIdx.x; j0 < total; j0 += step) {
+    typename C::T v[U];
+    char* d[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t j = j0 + u * kThreads;
       d[u] = nullptr;
       if (j < total) {
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       if (d[u]) C::store(d[u], v[u]);
   }
 }
@@ -178,7 +179,8 @@ namespace {
 // of V when lp.src_v is set.
 int launch_transfer(const LayerPtrs& lp, const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
                     int32_t num_layers, int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
-                    hipStream_t stream) {
+                    uint32_t flags, hipStream_t stream) {
+  if (flags & ~HS_TRANSFER_HOST_LINK) return set_error(HS_EINVAL, "unknown flags 0x%x", flags);
   if (n < 0 || num_layers < 0) return set_error(HS_EINVAL, "n and num_layers must be >= 0");
   if (n == 0 || num_layers == 0) return HS_OK;
   if (!lp.src_k || !lp.dst_k || !src_idx || !dst_idx || (lp.src_v && !lp.dst_v))
@@ -189,6 +191,7 @@ int launch_transfer(const LayerPtrs& lp, const int64_t* src_idx, const int64_t* 
   if (src_nrows < 0 || dst_nrows < 0) return set_error(HS_EINVAL, "row counts must be >= 0");
   if (num_layers > (1 << 24)) return set_error(HS_ERANGE, "too many layers");
   const int32_t streams = lp.src_v ? 2 * num_layers : num_layers;
+  const bool host_link = (flags & HS_TRANSFER_HOST_LINK) != 0;
   // Layer base addresses live on the device; rows are 16-byte chunks when
   // row_bytes allows (a base that is only 4-byte aligned is moved as dwords
   // by the kernel).
@@ -206,15 +209,33 @@ int launch_transfer(const LayerPtrs& lp, const int64_t* src_idx, const int64_t* 
   for (int64_t p0 = 0; p0 < n; p0 += max_pairs) {
     const int64_t np = (n - p0) < max_pairs ? (n - p0) : max_pairs;
     const uint32_t total = static_cast<uint32_t>(np * per_pair);
-    const unsigned grid = copy_grid(total, di.num_cus);
-    if (W == 16)
-      hipLaunchKernelGGL(transfer_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, lp,
-                         src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
-                         dst_nrows, cdiv, ldiv);
-    else
-      hipLaunchKernelGGL(transfer_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, lp,
-                         src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
-                         dst_nrows, cdiv, ldiv);
+    if (host_link) {
+      // The host link is full with far fewer requesters than HBM needs:
+      // one workgroup per two CUs, 8 chunks in flight per lane (all-layer
+      // load of 656-byte rows: 44.7 -> 47.7 GB/s against the HBM-sized
+      // launch; offload 51.9 -> 51.7).
+      const uint64_t need = (total + kThreads * kHostLinkUnroll - 1) / (kThreads * kHostLinkUnroll);
+      const uint64_t cap = di.num_cus > 1 ? static_cast<uint64_t>(di.num_cus) / 2 : 1;
+      const unsigned grid = static_cast<unsigned>(need < cap ? (need > 0 ? need : 1) : cap);
+      if (W == 16)
+        hipLaunchKernelGGL((transfer_kernel<16, kHostLinkUnroll>), dim3(grid), dim3(kThreads), 0,
+                           stream, lp, src_idx + p0, dst_idx + p0, total, streams, row_bytes,
+                           src_nrows, dst_nrows, cdiv, ldiv);
+      else
+        hipLaunchKernelGGL((transfer_kernel<4, kHostLinkUnroll>), dim3(grid), dim3(kThreads), 0,
+                           stream, lp, src_idx + p0, dst_idx + p0, total, streams, row_bytes,
+                           src_nrows, dst_nrows, cdiv, ldiv);
+    } else {
+      const unsigned grid = copy_grid(total, di.num_cus);
+      if (W == 16)
+        hipLaunchKernelGGL((transfer_kernel<16, kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                           lp, src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
+                           dst_nrows, cdiv, ldiv);
+      else
+        hipLaunchKernelGGL((transfer_kernel<4, kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                           lp, src_idx + p0, dst_idx + p0, total, streams, row_bytes, src_nrows,
+                           dst_nrows, cdiv, ldiv);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(HS_ELAUNCH, "transfer launch: %s", hipGetErrorString(e));
   }
@@ -272,9 +293,10 @@ int launch_scatter(const ScatterSide& k, const ScatterSide* v, int64_t dst_nrows
 extern "C" int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_layer_ptrs,
                                        const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
                                        int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
-                                       int64_t dst_nrows, hipStream_t stream) {
+                                       int64_t dst_nrows, uint32_t flags, hipStream_t stream) {
   const LayerPtrs lp{src_layer_ptrs, dst_layer_ptrs, nullptr, nullptr, num_layers};
-  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows, stream);
+  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows,
+                         flags, stream);
 }
 
 extern "C" int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs,
@@ -283,14 +305,16 @@ extern "C" int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs,
                                      const uint64_t* v_dst_layer_ptrs, const int64_t* src_idx,
                                      const int64_t* dst_idx, int64_t n, int32_t num_layers,
                                      int64_t row_bytes, int64_t src_nrows, int64_t dst_nrows,
-                                     hipStream_t stream) {
+                                     uint32_t flags, hipStream_t stream) {
+  if (flags & ~HS_TRANSFER_HOST_LINK) return set_error(HS_EINVAL, "unknown flags 0x%x", flags);
   if (!v_src_layer_ptrs || !v_dst_layer_ptrs) {
     if (n == 0 || num_layers == 0) return HS_OK;
     return set_error(HS_EINVAL, "a required pointer is NULL");
   }
   const LayerPtrs lp{k_src_layer_ptrs, k_dst_layer_ptrs, v_src_layer_ptrs, v_dst_layer_ptrs,
                      num_layers};
-  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows, stream);
+  return launch_transfer(lp, src_idx, dst_idx, n, num_layers, row_bytes, src_nrows, dst_nrows,
+                         flags, stream);
 }
 
 extern "C" int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,

@@ -113,12 +113,17 @@ def test_split_calls_validate_like_swap_in(lib, name):
 
 def test_transfer_rejects(lib):
     f = 0x100000
-    assert lib.transfer_rows_all_layer(f, f, f, f, -1, 3, 16, 10, 10, None) == -1
-    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 6, 10, 10, None) == -1
-    assert lib.transfer_rows_all_layer(None, f, f, f, 5, 3, 16, 10, 10, None) == -1
-    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 16, -1, 10, None) == -1
-    assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, None) == 0
-    assert lib.transfer_rows_all_layer(None, None, None, None, 4, 0, 16, 10, 10, None) == 0
+    assert lib.transfer_rows_all_layer(f, f, f, f, -1, 3, 16, 10, 10, 0, None) == -1
+    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 6, 10, 10, 0, None) == -1
+    assert lib.transfer_rows_all_layer(None, f, f, f, 5, 3, 16, 10, 10, 0, None) == -1
+    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 16, -1, 10, 0, None) == -1
+    assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, 0, None) == 0
+    assert lib.transfer_rows_all_layer(None, None, None, None, 4, 0, 16, 10, 10, 0, None) == 0
+    # flags: only HS_TRANSFER_HOST_LINK (1) is defined
+    assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, 1, None) == 0
+    assert lib.transfer_rows_all_layer(f, f, f, f, 5, 3, 16, 10, 10, 2, None) == -1
+    assert b"flags" in lib.hisparse_last_error()
+    assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, 0x80000000, None) == -1
 
 
 def test_scatter_rejects(lib):
@@ -179,12 +184,13 @@ def test_gather_layers_rejects(lib):
 def test_kv_entries_reject(lib):
     f = 0x100000
     t = lib.transfer_kv_all_layer
-    assert t(f, f, f, f, f, f, 0, 3, 16, 10, 10, None) == 0               # empty
-    assert t(f, f, f, f, f, f, 5, 0, 16, 10, 10, None) == 0               # no layers
-    assert t(f, None, f, f, f, f, 5, 3, 16, 10, 10, None) == -1           # V arrays missing
-    assert t(f, f, f, None, f, f, 5, 3, 16, 10, 10, None) == -1
-    assert t(f, f, f, f, f, f, 5, 3, 14, 10, 10, None) == -1              # row_bytes % 4
-    assert t(f, f, f, f, f, f, -1, 3, 16, 10, 10, None) == -1
+    assert t(f, f, f, f, f, f, 0, 3, 16, 10, 10, 0, None) == 0            # empty
+    assert t(f, f, f, f, f, f, 5, 0, 16, 10, 10, 1, None) == 0            # no layers
+    assert t(f, None, f, f, f, f, 5, 3, 16, 10, 10, 0, None) == -1        # V arrays missing
+    assert t(f, f, f, None, f, f, 5, 3, 16, 10, 10, 0, None) == -1
+    assert t(f, f, f, f, f, f, 5, 3, 14, 10, 10, 0, None) == -1           # row_bytes % 4
+    assert t(f, f, f, f, f, f, -1, 3, 16, 10, 10, 0, None) == -1
+    assert t(f, f, f, f, f, f, 5, 3, 16, 10, 10, 4, None) == -1           # unknown flag
     s = lib.store_kv_cache
     assert s(None, 16, None, 16, None, 16, None, 16, 10, None, 0, 16, None) == 0
     assert s(f, 16, f, 8, f, 16, f, 16, 10, f, 3, 16, None) == -1         # v src stride < rb

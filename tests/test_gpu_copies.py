@@ -43,6 +43,7 @@ def _np(t):
     return t.cpu().numpy() if t.is_cuda else t.numpy()
 
 
+@pytest.mark.parametrize("host_link", [False, True], ids=["hbm_launch", "host_link_launch"])
 @pytest.mark.parametrize("L,rows,rb,n,src_kind,dst_kind", [
     (1, 64, 656, 17, "device", "device"),
     (3, 500, 656, 300, "host", "device"),
@@ -50,8 +51,9 @@ def _np(t):
     (2, 200, 132, 150, "host", "device"),       # 4-byte path
     (7, 100, 4, 100, "device", "device"),
     (61, 300, 1152, 257, "device", "host"),
+    (4, 40000, 656, 30000, "host", "device"),   # more items than one host-link launch round
 ])
-def test_transfer_parity(L, rows, rb, n, src_kind, dst_kind):
+def test_transfer_parity(L, rows, rb, n, src_kind, dst_kind, host_link):
     import sparse_attention_kv_hisparse_amd as hs
     rng = np.random.default_rng(L * 1000 + n)
     _, src_l, src_p = _layers(L, rows, rb, src_kind, 1 + L)
@@ -64,7 +66,7 @@ def test_transfer_parity(L, rows, rb, n, src_kind, dst_kind):
     skipped = oracle.transfer_rows_all_layer(want_src, want_dst, si, di)
     hs.transfer_rows_all_layer(src_layer_ptrs=src_p, dst_layer_ptrs=dst_p,
                                src_idx=torch.as_tensor(si).cuda(), dst_idx=torch.as_tensor(di).cuda(),
-                               row_bytes=rb, src_nrows=rows, dst_nrows=rows)
+                               row_bytes=rb, src_nrows=rows, dst_nrows=rows, host_link=host_link)
     torch.cuda.synchronize()
     assert skipped == len(si[::37])
     for l in range(L):
@@ -90,7 +92,7 @@ def test_transfer_all_layer_full_size(direction):
     before = {l: _np(dst_l[l]).copy() for l in sample}
     hs.transfer_rows_all_layer(src_layer_ptrs=src_p, dst_layer_ptrs=dst_p,
                                src_idx=torch.as_tensor(si).cuda(), dst_idx=torch.as_tensor(di).cuda(),
-                               row_bytes=rb, src_nrows=rows, dst_nrows=rows)
+                               row_bytes=rb, src_nrows=rows, dst_nrows=rows, host_link=True)
     torch.cuda.synchronize()
     _log(f"  all-layer {direction}: copied, checking")
     sit, dit = torch.as_tensor(si), torch.as_tensor(di)

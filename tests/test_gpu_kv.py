@@ -98,7 +98,8 @@ def _layers(L, rows, rb, where, seed):
     (2, 200, 132, 150, "device", "device"),       # 4-byte path
     (150, 40, 64, 30, "host", "device"),          # 300 streams: more than are staged in LDS
 ])
-def test_transfer_kv_all_layer(L, rows, rb, n, src_kind, dst_kind):
+@pytest.mark.parametrize("host_link", [False, True], ids=["hbm_launch", "host_link_launch"])
+def test_transfer_kv_all_layer(L, rows, rb, n, src_kind, dst_kind, host_link):
     import sparse_attention_kv_hisparse_amd as hs
     _log(f"  transfer_kv L={L} rows={rows} rb={rb} n={n} {src_kind}->{dst_kind}")
     ks, ksp = _layers(L, rows, rb, src_kind, 1)
@@ -114,7 +115,7 @@ def test_transfer_kv_all_layer(L, rows, rb, n, src_kind, dst_kind):
     hs.transfer_kv_all_layer(k_src_layer_ptrs=ksp, v_src_layer_ptrs=vsp, k_dst_layer_ptrs=kdp,
                              v_dst_layer_ptrs=vdp, src_idx=torch.as_tensor(si).cuda(),
                              dst_idx=torch.as_tensor(di).cuda(), row_bytes=rb, src_nrows=rows,
-                             dst_nrows=rows)
+                             dst_nrows=rows, host_link=host_link)
     torch.cuda.synchronize()
     for l in range(L):
         assert np.array_equal(_np(kd[l]), want_k[l]), f"K layer {l}"
