@@ -97,11 +97,15 @@ struct SwapArgs {
   uint32_t T;         // hash entries, power of two >= 2K
   uint32_t shift;     // 32 - log2(T)
   int32_t stage_tokens;
+  int32_t hbt_n;      // paged: hot block table entries staged in LDS (0 = read from HBM)
+  int32_t sbt_n;      // paged: source block table entries staged in LDS (0 = read from HBM)
   FastDiv cdiv;       // chunks per row
+  FastDiv hbs_div, sbs_div, rbs_div;   // paged: the three block sizes
 };
 
 struct LdsLayout {
-  uint32_t hash, hidx, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, total;
+  uint32_t hash, hidx, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, hbt,
+      sbt, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
@@ -112,7 +116,8 @@ __host__ __device__ inline uint32_t wave_segment(int32_t n) {
   return align_up((static_cast<uint32_t>(n) + kWaves - 1) / kWaves, 64);
 }
 
-__host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T, bool stage_tokens) {
+__host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T, bool stage_tokens,
+                                                uint32_t hbt_n, uint32_t sbt_n) {
   const uint32_t hwords = kWaves * wave_segment(H) / 64;
   const uint32_t kwords = kWaves * wave_segment(K) / 64;
   LdsLayout l;
@@ -131,6 +136,8 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
   l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
   l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
+  l.hbt = o;    o = align_up(o + 4 * hbt_n, 16);                 // paged: hot block table row
+  l.sbt = o;    o = align_up(o + 4 * sbt_n, 16);                 // paged: source block table row
   l.total = o;
   return l;
 }
@@ -222,10 +229,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   const int32_t* srows = kSlotRows ? a.slot_rows + r * a.S_r : nullptr;
   const int64_t* prow = kPoolRows ? a.pool_rows + r * a.ctx_stride : nullptr;
   const int64_t hot_base = r * a.S_r;
+  const int32_t* s_hbt = reinterpret_cast<const int32_t*>(lds + lay.hbt);
   auto row_of = [&](int32_t s) -> int32_t {
     if constexpr (kPaged) {
-      const int32_t blk = a.hbt[r * a.hbt_stride + s / a.hbs];
-      return blk * a.hbs + s % a.hbs;
+      const int32_t q = static_cast<int32_t>(fdiv(static_cast<uint32_t>(s), a.hbs_div));
+      const int32_t blk = a.hbt_n ? s_hbt[q] : a.hbt[r * a.hbt_stride + q];
+      return blk * a.hbs + (s - q * a.hbs);
     }
     if constexpr (kSlotRows) return srows[s];
     return static_cast<int32_t>(hot_base + s);
@@ -271,6 +280,16 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
     for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
     if (tid < 2 * (kWaves + 1) + 1) wtot[tid] = 0;
+    if constexpr (kPaged) {
+      // The request's hot block table row: every slot -> row translation in
+      // the probe and the assign step then stays in LDS.
+      int32_t* hb = reinterpret_cast<int32_t*>(lds + lay.hbt);
+      for (int i = tid; i < a.hbt_n; i += kThreads) hb[i] = a.hbt[r * a.hbt_stride + i];
+      // ... and the source block table row, so classifying an id needs no
+      // dependent HBM read.
+      int32_t* sb = reinterpret_cast<int32_t*>(lds + lay.sbt);
+      for (int i = tid; i < a.sbt_n; i += kThreads) sb[i] = a.sbt[r * a.sbt_stride + i];
+    }
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
@@ -371,18 +390,22 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         int64_t g = -1, res = -1;
         if (i < K) {
           g = tt;
+          // Block and offset by multiply-shift division (tt < 2^31).
+          const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
+          const int32_t rq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.rbs_div));
           if (a.sbt) {
             g = -1;
-            if (tt >= 0 && tt / a.sbs < a.sbt_nblocks) {
-              const int32_t pb = a.sbt[r * a.sbt_stride + tt / a.sbs];
-              if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + tt % a.sbs;
+            if (tt >= 0 && sq < a.sbt_nblocks) {
+              const int32_t pb = a.sbt_n ? reinterpret_cast<const int32_t*>(lds + lay.sbt)[sq]
+                                         : a.sbt[r * a.sbt_stride + sq];
+              if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
             }
           }
           if (g >= a.pool_nrows) g = -1;
-          if (a.rbt && tt >= 0 && tt / a.rbs < a.rbt_nblocks) {
-            const int32_t pb = a.rbt[r * a.rbt_stride + tt / a.rbs];
+          if (a.rbt && tt >= 0 && rq < a.rbt_nblocks) {
+            const int32_t pb = a.rbt[r * a.rbt_stride + rq];
             if (pb != a.r_null && pb >= 0) {
-              res = static_cast<int64_t>(pb) * a.rbs + tt % a.rbs;
+              res = static_cast<int64_t>(pb) * a.rbs + (tt - rq * a.rbs);
               if (res > INT32_MAX) res = -1;
             }
           }
@@ -650,10 +673,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         }
       }
       out[i] = o;
-      if (kPaged && a.att)   // vLLM page, store_hot_index
+      if (kPaged && a.att) {  // vLLM page, store_hot_index
+        const int32_t ob = static_cast<int32_t>(fdiv(static_cast<uint32_t>(o < 0 ? 0 : o), a.hbs_div));
         a.att[static_cast<int64_t>(b) * a.att_stride + i] =
-            o < 0 ? -1
-                  : static_cast<int32_t>((o / a.hbs) * a.att_block_stride + o % a.hbs);
+            o < 0 ? -1 : static_cast<int32_t>(ob * a.att_block_stride + (o - ob * a.hbs));
+      }
     }
   }
   // The new LRU order, built in LDS by phase 3, goes out in one coalesced pass.
@@ -715,7 +739,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0);
+  const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0, static_cast<uint32_t>(a.hbt_n),
+                                   static_cast<uint32_t>(a.sbt_n));
   resolve<kSlotRows, kPoolRows, kCopyW, kPaged>(a, blockIdx.x, lds, lay);
 }
 
@@ -870,13 +895,22 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // staging (tokens gathered from HBM). Shorter probe chains matter most: a
   // wave's probe loop runs as long as its longest chain.
   const uint32_t k2 = 2u * static_cast<uint32_t>(a->K) < 64u ? 64u : 2u * static_cast<uint32_t>(a->K);
+  // Paged: the request's hot block table row (one entry per block of slots)
+  // and source block table row go to LDS when they are small; larger rows
+  // are read from HBM.
+  uint32_t hbt_n = 0, sbt_n = 0;
+  if (pg) {
+    const int64_t nb = (static_cast<int64_t>(a->H) + pa->hot_block_size - 1) / pa->hot_block_size;
+    if (nb <= 2048) hbt_n = static_cast<uint32_t>(nb);
+    if (pa->src_block_table && pa->src_num_blocks <= 2048) sbt_n = static_cast<uint32_t>(pa->src_num_blocks);
+  }
   const uint32_t plans_T[4] = {pow2_at_least(2 * k2), pow2_at_least(k2), pow2_at_least(2 * k2),
                                pow2_at_least(k2)};
   const bool plans_stage[4] = {true, true, false, false};
   int plan = -1;
   LdsLayout lay{};
   for (int i = 0; i < 4 && plan < 0; ++i) {
-    lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i]);
+    lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i], hbt_n, sbt_n);
     if (static_cast<int>(lay.total) <= di.max_lds) plan = i;
   }
   if (plan < 0)
@@ -989,6 +1023,11 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.T = T;
   s.shift = 32 - log2T;
   s.stage_tokens = stage ? 1 : 0;
+  s.hbt_n = static_cast<int32_t>(hbt_n);
+  s.sbt_n = static_cast<int32_t>(sbt_n);
+  s.hbs_div = make_fastdiv(static_cast<uint32_t>(s.hbs));
+  s.sbs_div = make_fastdiv(static_cast<uint32_t>(s.sbs));
+  s.rbs_div = make_fastdiv(static_cast<uint32_t>(s.rbs));
   s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
 
   pl->resolve_fn = resolve_fn;
