@@ -477,6 +477,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int p = h0 + c0 + u * kWave + lane;
       sl[u] = c0 == 0 ? vl[u] : ((c0 + u * kWave < segH && p < H) ? s_lru[p] : -1);
     }
+    // Each slot's hot row, worked out beside the token read (with paged
+    // addressing it is an LDS table read of its own, kept off the CAS's path).
+    int32_t rw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rw[u] = row_of((sl[u] >= 0 && sl[u] < H) ? sl[u] : 0);
     // The staging choice is uniform: branching once keeps all four token
     // reads of a lane in flight together.
     if (a.stage_tokens) {
@@ -526,8 +531,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     int32_t prev[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending,
-                          idx[u] >= 0 ? row_of(sl[u]) : 0);
+      prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending, idx[u] >= 0 ? rw[u] : 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool hit = idx[u] >= 0 && prev[u] == kPending;
