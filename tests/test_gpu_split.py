@@ -24,7 +24,10 @@ def _lib():
     gen.SwapConfig("split", B=5, H=300, K=120, ctx=2000, row_bytes=656, steps=6, rho=0.6,
                    dist="uniform", pool_kind="host", seed=31),
     gen.DEVPOOL.with_(B=8, steps=4),
-], ids=["host", "device"])
+    # more requests than CUs: the host-pool copy's one-workgroup-per-CU grid
+    gen.SwapConfig("split_many", B=400, H=64, K=30, ctx=300, row_bytes=656, steps=4, rho=0.5,
+                   dist="uniform", pool_kind="host", seed=32),
+], ids=["host", "device", "host_many_requests"])
 def test_resolve_then_gather_matches_oracle(cfg):
     import sparse_attention_kv_hisparse_amd as hs
     pool = wdev.make_pool(cfg)

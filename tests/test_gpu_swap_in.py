@@ -75,8 +75,10 @@ def _small(**kw):
     dict(B=1, H=2048, K=2048, ctx=4096),        # one request, all K = H
     dict(H=16384, K=2048, ctx=40000, B=2, steps=3),   # slot tokens too big to stage in LDS
     dict(H=16384, K=2048, ctx=40000, B=2, steps=3, pool_kind="device"),
+    dict(B=600, H=96, K=40, ctx=400, steps=4),        # more requests than CUs (fused copy)
+    dict(B=600, H=96, K=40, ctx=400, steps=4, pool_kind="device"),
 ], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single",
-        "unstaged_host", "unstaged_dev"])
+        "unstaged_host", "unstaged_dev", "many_host", "many_dev"])
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
