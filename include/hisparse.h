@@ -155,6 +155,12 @@ typedef struct hs_swap_in_args {
   /* vLLM-style paged addressing (host pointer to a struct whose tables are
    * device arrays), or NULL for the addressing described above. */
   const hs_paged_addressing* paged;
+
+  /* Running counters (vLLM hisparse_kernels.cu, stats), or NULL: device
+   * uint64 [2], in/out. Every real batch row adds its hits (step 2) to
+   * stats[0] and its misses (step 3) to stats[1] with device atomics, so calls
+   * accumulate; the caller zeroes them when it wants a fresh count. */
+  uint64_t* stats;
 } hs_swap_in_args;
 
 /* Bytes of device workspace hisparse_swap_in needs for B rows of K ids
@@ -179,7 +185,7 @@ size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K);
  *      pool_row(r, t) to hot row Row(r, v).
  *   4. lru[r] becomes: remaining evictables, then the filled slots in miss order,
  *      then the hits, each group in its previous order.
- *   5. miss_counts[b] = number of misses.
+ *   5. miss_counts[b] = number of misses; stats[0] += hits, stats[1] += misses.
  *
  * Preconditions the caller guarantees (not checked on the device): valid ids
  * are unique within a batch row; real rows name distinct state rows; lru rows

@@ -89,6 +89,7 @@ class _SwapArgs(ctypes.Structure):
         ("list_src", ctypes.c_void_p), ("list_dst", ctypes.c_void_p),
         ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
         ("paged", ctypes.POINTER(_Paged)),
+        ("stats", ctypes.c_void_p),
     ]
 
 
@@ -173,7 +174,7 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
             pool_rows: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None,
             miss_counts: Optional[np.ndarray] = None, plan: bool = False,
             pool_v: Optional[np.ndarray] = None, hot_v: Optional[np.ndarray] = None,
-            paged: Optional[dict] = None):
+            paged: Optional[dict] = None, stats: Optional[np.ndarray] = None):
     """One swap-in call on host state; returns ``(out_rows int32[B,K], miss_counts int32[B])``,
     and with ``plan=True`` a third item: the plan index-sharing layers replay,
     ``{"miss_mask": int32[B,K], "count": int32[B], "src": int64[B,K], "dst": int32[B,K]}``
@@ -187,6 +188,7 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
     ``src_block_table`` int32 [R, n] + ``src_block_size``, ``resident_block_table`` int32
     [R, n] + ``resident_block_size`` + ``resident_null_block``, ``attention_indices`` int32
     [B, K] (output) + ``attention_block_stride``; ``seq_lens`` and ``ctx_stride`` are unused.
+    ``stats`` (uint64[2], in/out): every real row adds its hits and its misses.
     """
     assert (pool_v is None) == (hot_v is None)
     if pool_v is not None:
@@ -240,7 +242,8 @@ def swap_in(*, topk: np.ndarray, req_rows: np.ndarray, seq_lens: np.ndarray,
         list_count=p and _ptr(p["count"], np.int32, True),
         list_src=p and _ptr(p["src"], np.int64, True), list_dst=p and _ptr(p["dst"], np.int32, True),
         pool_v=_ptr(pool_v, np.uint8), hot_v=_ptr(hot_v, np.uint8, True),
-        paged=ctypes.pointer(pg) if pg is not None else None)
+        paged=ctypes.pointer(pg) if pg is not None else None,
+        stats=None if stats is None else _ptr(stats, np.uint64, True))
     rc = _load().oracle_swap_in(ctypes.byref(a))
     if rc != ORACLE_OK:
         raise OracleError(rc)

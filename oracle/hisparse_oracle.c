@@ -283,6 +283,10 @@ int oracle_swap_in(const oracle_swap_in_args *a) {
     memcpy(lru, new_lru, sizeof(int16_t) * (size_t)H);
 
     if (a->miss_counts) a->miss_counts[b] = M;
+    if (a->stats) {
+      a->stats[0] += (uint64_t)nh;
+      a->stats[1] += (uint64_t)M;
+    }
     store_attention(a, b, out);
   }
 

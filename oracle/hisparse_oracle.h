@@ -99,6 +99,9 @@ typedef struct {
   const uint8_t *pool_v;    /* [pool_nrows, row_bytes] or NULL */
   uint8_t *hot_v;           /* [hot_nrows, row_bytes], NULL when pool_v is */
   const oracle_paged *paged; /* NULL: SGLang-style addressing (above) */
+  /* Optional running counters ([VLLM] stats): every real row adds its hits
+   * (step 2) to stats[0] and its misses (step 3) to stats[1]. */
+  uint64_t *stats;          /* [2] in/out, or NULL */
 } oracle_swap_in_args;
 
 /* One decode-step swap-in call. Returns ORACLE_OK or a negative code when a

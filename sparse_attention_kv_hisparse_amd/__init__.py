@@ -60,8 +60,8 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                      pool_rows: Optional[torch.Tensor] = None,
                      miss_mask: Optional[torch.Tensor] = None,
                      pool_v: Optional[torch.Tensor] = None, hot_v: Optional[torch.Tensor] = None,
-                     paged: Optional[dict] = None, stream=None,
-                     _entry: str = "hisparse_swap_in") -> None:
+                     paged: Optional[dict] = None, stats: Optional[torch.Tensor] = None,
+                     stream=None, _entry: str = "hisparse_swap_in") -> None:
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
@@ -76,6 +76,8 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
     ``resident_block_table`` int32 [R, n] + ``resident_block_size`` + ``resident_null_block``,
     ``attention_indices`` int32 [B, >=K] output + ``attention_block_stride``. seq_lens may
     then be None and ctx_stride is unused.
+    stats: int64 or uint64 device tensor of 2 elements (optional, in/out): the hits and
+    misses of every real row are added to stats[0] and stats[1].
     """
     if (pool_v is None) != (hot_v is None):
         raise ValueError("pool_v and hot_v go together")
@@ -144,6 +146,10 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         paged=ctypes.pointer(pg) if pg is not None else None)
     if miss_mask is not None and (tuple(miss_mask.shape) != (B, K) or not miss_mask.is_contiguous()):
         raise ValueError("miss_mask must be a contiguous [B, K] int32 tensor")
+    if stats is not None:
+        if stats.dtype not in (torch.int64, torch.uint64) or stats.numel() != 2 or not stats.is_contiguous():
+            raise ValueError("stats must be a contiguous 2-element int64 or uint64 tensor")
+        a.stats = _dev(stats, stats.dtype, "stats")
     ws = _dev(workspace, torch.uint8, "workspace")
     check(_entry, getattr(load(), _entry)(ctypes.byref(a), ws, workspace.numel(), _stream(stream)))
 

@@ -59,6 +59,7 @@ class SwapInArgs(ctypes.Structure):
         ("miss_mask", ctypes.c_void_p),
         ("pool_v", ctypes.c_void_p), ("hot_v", ctypes.c_void_p),
         ("paged", ctypes.POINTER(PagedAddressing)),
+        ("stats", ctypes.c_void_p),
     ]
 
 

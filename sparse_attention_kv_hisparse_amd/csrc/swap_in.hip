@@ -74,6 +74,7 @@ struct SwapArgs {
   int32_t* out_rows;
   int32_t* miss_counts;
   int32_t* miss_mask; // [B, K] or null: 1 where the entry missed and got a slot
+  unsigned long long* stats;  // [2] or null: hits and misses, accumulated
   const char* pool_v; // non-MLA caches: V pool / V hot buffer, or null
   char* hot_v;
   // vLLM-style paged addressing (kPaged instantiations only): hot block
@@ -696,6 +697,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   if (tid == 0) {
     a.count[b] = m_total;
     if (a.miss_counts) a.miss_counts[b] = m_total;
+    if (a.stats) {   // vLLM hisparse_kernels.cu, stats: hits, misses
+      atomicAdd(&a.stats[0], static_cast<unsigned long long>(hits));
+      atomicAdd(&a.stats[1], static_cast<unsigned long long>(m_total));
+    }
   }
 
   // ---- 5. (host pools) the request's own row copies -------------------------
@@ -1016,6 +1021,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.out_rows = a->out_rows;
   s.miss_counts = a->miss_counts;
   s.miss_mask = a->miss_mask;
+  s.stats = reinterpret_cast<unsigned long long*>(a->stats);
   s.count = reinterpret_cast<int32_t*>(ws + wl.count);
   s.src = reinterpret_cast<int64_t*>(ws + wl.src);
   s.dst = reinterpret_cast<int32_t*>(ws + wl.dst);

@@ -1,9 +1,9 @@
 """Side-by-side runs of the HIP swap-in and the CPU oracle on identical inputs.
 
 After every call the GPU's outputs and state are downloaded and compared with
-the oracle's bit for bit: out_rows, miss_counts, slot_tokens, lru, the rows the
-call may have written, and the whole hot buffer on the steps listed in
-``full_hot_steps``.
+the oracle's bit for bit: out_rows, miss_counts, slot_tokens, lru, the running
+hit / miss counters, the rows the call may have written, and the whole hot
+buffer on the steps listed in ``full_hot_steps``.
 """
 
 from __future__ import annotations
@@ -62,6 +62,9 @@ class ParityRun:
         self.pool_rows_t = None if pool_rows is None else torch.as_tensor(pool_rows).cuda()
         self.o_tokens, self.o_lru = gen.initial_state(self.R, cfg.H, cfg.S_r)
         self.o_hot = np.zeros(tuple(self.st.hot.shape), dtype=np.uint8)
+        # running hit / miss counters, accumulated over the run on both sides
+        self.stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.o_stats = np.zeros(2, dtype=np.uint64)
         self.calls = 0
 
     def _newest_loc(self, seq: np.ndarray) -> np.ndarray:
@@ -108,17 +111,19 @@ class ParityRun:
             pool=self.pool_t, hot=self.st.hot, out_rows=self.st.out, ctx_stride=cfg.ctx,
             workspace=self.st.ws, miss_counts=self.st.counts,
             num_real=None if num_real < 0 else torch.tensor([num_real], dtype=torch.int32).cuda(),
-            slot_rows=self.slot_rows_t, pool_rows=self.pool_rows_t)
+            slot_rows=self.slot_rows_t, pool_rows=self.pool_rows_t, stats=self.stats)
         o_out, o_cnt = oracle.swap_in(
             topk=topk, req_rows=self.req_rows, seq_lens=seq, slot_tokens=self.o_tokens,
             lru=self.o_lru, pool=self.pool_np, hot=self.o_hot, ctx_stride=cfg.ctx,
-            num_real=num_real, slot_rows=self.slot_rows, pool_rows=self.pool_rows)
+            num_real=num_real, slot_rows=self.slot_rows, pool_rows=self.pool_rows,
+            stats=self.o_stats)
         torch.cuda.synchronize()
         tag = f"{cfg.name} call {self.calls}"
         assert_equal(f"{tag} out_rows", self.st.out.cpu().numpy(), o_out)
         assert_equal(f"{tag} miss_counts", self.st.counts.cpu().numpy(), o_cnt)
         assert_equal(f"{tag} slot_tokens", self.st.slot_tokens.cpu().numpy(), self.o_tokens)
         assert_equal(f"{tag} lru", self.st.lru.cpu().numpy(), self.o_lru)
+        assert_equal(f"{tag} stats", self.stats.cpu().numpy().astype(np.uint64), self.o_stats)
         if full_hot:
             assert_equal(f"{tag} hot buffer", self.st.hot.cpu().numpy(), self.o_hot)
         else:

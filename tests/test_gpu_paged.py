@@ -66,6 +66,8 @@ def test_paged_swap_in_matches_oracle(case):
     o_lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
     o_hot = np.zeros((hot_nrows, rb), np.uint8)
     o_hot_v = np.zeros_like(o_hot) if kv else None
+    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    o_stats = np.zeros(2, np.uint64)
     for call in range(8):
         if call % 4 == 3:
             rows = rng.integers(-1, R + 1, 40).astype(np.int64)
@@ -83,7 +85,7 @@ def test_paged_swap_in_matches_oracle(case):
                   seq_lens=None, slot_tokens=keys, lru=lru, pool=pool, hot=hot, out_rows=out,
                   ctx_stride=0, workspace=ws, miss_counts=counts,
                   num_real=torch.tensor([nreal if nreal >= 0 else B], dtype=torch.int32, device="cuda"),
-                  paged=paged_dev)
+                  paged=paged_dev, stats=stats)
         if kv:
             kw.update(pool_v=pool_v, hot_v=hot_v)
         if split:
@@ -95,8 +97,9 @@ def test_paged_swap_in_matches_oracle(case):
         pg = dict(paged_np, attention_indices=o_att, attention_block_stride=40)
         o_out, o_cnt = oracle.swap_in(topk=topk, req_rows=req, seq_lens=None, slot_tokens=o_keys,
                                       lru=o_lru, pool=pool_np, hot=o_hot, ctx_stride=0, num_real=nreal,
-                                      paged=pg, pool_v=pool_v_np, hot_v=o_hot_v)
+                                      paged=pg, pool_v=pool_v_np, hot_v=o_hot_v, stats=o_stats)
         torch.cuda.synchronize()
+        assert np.array_equal(_np(stats).astype(np.uint64), o_stats), f"call {call}: stats"
         assert np.array_equal(_np(out), o_out), f"call {call}: out_rows"
         assert np.array_equal(_np(counts), o_cnt), f"call {call}: miss_counts"
         assert np.array_equal(_np(att)[:, :K], o_att[:, :K]), f"call {call}: attention_indices"

@@ -38,12 +38,15 @@ def test_resolve_then_gather_matches_oracle(cfg):
     o_tok, o_lru = gen.initial_state(cfg)
     o_hot = np.zeros((cfg.R * cfg.S_r, cfg.row_bytes), np.uint8)
     rows = np.arange(cfg.B, dtype=np.int64)
+    # uint64 counters: only the resolve adds to them, the gather leaves them alone
+    stats = torch.zeros(2, dtype=torch.uint64).cuda()
+    o_stats = np.zeros(2, np.uint64)
     for t, topk in enumerate(gen.topk_trace(cfg)):
         seq = gen.seq_lens(cfg, t)
         kw = dict(topk=torch.as_tensor(topk).cuda(), req_rows=torch.as_tensor(rows).cuda(),
                   seq_lens=torch.as_tensor(seq).cuda(), slot_tokens=st.slot_tokens, lru=st.lru,
                   pool=pool, hot=st.hot, out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
-                  miss_counts=st.counts)
+                  miss_counts=st.counts, stats=stats)
         hs.hisparse_resolve(**kw)
         torch.cuda.synchronize()
         ws = st.ws.cpu().numpy()
@@ -53,8 +56,10 @@ def test_resolve_then_gather_matches_oracle(cfg):
         tok_before = o_tok.copy()
         hs.hisparse_gather_compact(**kw)
         o_out, o_cnt = oracle.swap_in(topk=topk, req_rows=rows, seq_lens=seq, slot_tokens=o_tok,
-                                      lru=o_lru, pool=pool_np, hot=o_hot, ctx_stride=cfg.ctx)
+                                      lru=o_lru, pool=pool_np, hot=o_hot, ctx_stride=cfg.ctx,
+                                      stats=o_stats)
         torch.cuda.synchronize()
+        assert np.array_equal(stats.view(torch.int64).cpu().numpy().astype(np.uint64), o_stats)
         assert np.array_equal(st.out.cpu().numpy(), o_out)
         assert np.array_equal(st.counts.cpu().numpy(), o_cnt)
         assert np.array_equal(st.slot_tokens.cpu().numpy(), o_tok)

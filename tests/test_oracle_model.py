@@ -10,7 +10,9 @@
   same compacted array) give the oracle's order.
 * Every comparison with the model also covers the plan the oracle publishes
   for index-sharing layers: the miss mask and the compact copy list in miss
-  order.
+  order, and the running hit / miss counters against their definition (a
+  pending id is a hit when its token sits in one of the row's LRU slots before
+  the call).
 """
 
 import itertools
@@ -28,6 +30,30 @@ def _pool(n, rb):
     return rng.integers(0, 256, size=(n, rb), dtype=np.uint8)
 
 
+def _expected_stats(c, st, *, R, H, ctx_stride, pool_rows, pool_nrows):
+    """(hits, misses) of one call from the definition, on the state before it:
+    over the real rows, a pending id (valid, not the newest token) is a hit when
+    its token sits in one of the row's H LRU slots, else a miss."""
+    hits = misses = 0
+    nreal = c.get("num_real", -1)
+    for b, r in enumerate(c["req_rows"].tolist()):
+        if (nreal >= 0 and b >= nreal) or not 0 <= r < R:
+            continue
+        L = int(c["seq_lens"][b])
+        resident = set(st[r, :H].tolist()) - {-1}
+        for t in set(c["topk"][b].tolist()):
+            if t < 0 or t >= L or t >= ctx_stride or t == L - 1:
+                continue
+            pr = int(pool_rows[r, t]) if pool_rows is not None else r * ctx_stride + t
+            if not 0 <= pr < pool_nrows:
+                continue
+            if t in resident:
+                hits += 1
+            else:
+                misses += 1
+    return hits, misses
+
+
 def _run_both(calls, *, R, H, S_r, ctx_stride, rb=8, slot_rows=None, pool_rows=None,
               hot_nrows=None, pool_nrows=None, kv=False):
     pool = _pool(pool_nrows or R * ctx_stride, rb)
@@ -39,12 +65,18 @@ def _run_both(calls, *, R, H, S_r, ctx_stride, rb=8, slot_rows=None, pool_rows=N
     pool_v = (255 - pool) if kv else None
     hv_o = np.zeros_like(hot_o) if kv else None
     hv_m = np.zeros_like(hot_o) if kv else None
+    stats = np.zeros(2, np.uint64)
+    want = np.zeros(2, np.int64)
     for c in calls:
         kw = dict(topk=c["topk"], req_rows=c["req_rows"], seq_lens=c["seq_lens"],
                   ctx_stride=ctx_stride, num_real=c.get("num_real", -1), slot_rows=slot_rows,
                   pool_rows=pool_rows, pool=pool)
+        want += _expected_stats(c, st_o, R=R, H=H, ctx_stride=ctx_stride, pool_rows=pool_rows,
+                                pool_nrows=pool.shape[0])
         out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True,
-                                              pool_v=pool_v, hot_v=hv_o, **kw)
+                                              pool_v=pool_v, hot_v=hv_o, stats=stats, **kw)
+        # running counters: hits and misses from the definition, accumulated
+        assert stats.tolist() == want.tolist()
         out_m, cnt_m, plan_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, plan=True,
                                                  pool_v=pool_v, hot_v=hv_m, **kw)
         if kv:

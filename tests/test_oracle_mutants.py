@@ -60,6 +60,8 @@ MUTANTS = {
                             "if (slot_keys[s] == g) { slot_keys[s] = -1;"),
     "attention_offset_wrong": ("                               o % p->hot_block_size);",
                                "                               o % p->attention_block_stride);"),
+    "stats_hits_are_evictables": ("a->stats[0] += (uint64_t)nh;", "a->stats[0] += (uint64_t)ne;"),
+    "stats_misses_not_added": ("a->stats[1] += (uint64_t)M;", ""),
     "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
                                       "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }

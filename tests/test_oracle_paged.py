@@ -119,8 +119,11 @@ def test_paged_matches_model(seed):
         nreal = int(rng.integers(1, B + 1)) if rng.random() < 0.3 else -1
         kw = dict(topk=topk, req_rows=req, seq_lens=None, pool=pool, ctx_stride=0, num_real=nreal,
                   paged=paged)
-        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True, **kw)
+        stats = np.zeros(2, np.uint64)
+        out_o, cnt_o, plan_o = oracle.swap_in(slot_tokens=st_o, lru=lru_o, hot=hot_o, plan=True,
+                                              stats=stats, **kw)
         out_m, cnt_m, plan_m = lru_model_swap_in(slot_tokens=st_m, lru=lru_m, hot=hot_m, plan=True, **kw)
+        assert int(stats[1]) == int(cnt_m.sum())   # misses, from the model's counts
         assert out_o.tolist() == out_m.tolist(), call
         assert cnt_o.tolist() == cnt_m.tolist()
         assert st_o.tolist() == st_m.tolist()
