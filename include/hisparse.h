@@ -159,7 +159,8 @@ typedef struct hs_swap_in_args {
   /* Running counters (vLLM hisparse_kernels.cu, stats), or NULL: device
    * uint64 [2], in/out. Every real batch row adds its hits (step 2) to
    * stats[0] and its misses (step 3) to stats[1] with device atomics, so calls
-   * accumulate; the caller zeroes them when it wants a fresh count. */
+   * accumulate; the caller zeroes them when it wants a fresh count. Must be
+   * 8-byte aligned (HS_EINVAL otherwise). */
   uint64_t* stats;
 } hs_swap_in_args;
 

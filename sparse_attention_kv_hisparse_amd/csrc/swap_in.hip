@@ -884,6 +884,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     return set_error(HS_EINVAL, "pool_v and hot_v are given together or not at all");
   if (a->pool_v && (!aligned(a->pool_v, 4) || !aligned(a->hot_v, 4)))
     return set_error(HS_EINVAL, "pool_v and hot_v must be 4-byte aligned");
+  if (a->stats && !aligned(a->stats, 8)) return set_error(HS_EINVAL, "stats must be 8-byte aligned");
   const bool kv = a->pool_v != nullptr;
   const int W = (aligned(a->pool, 16) && aligned(a->hot, 16) && (a->row_bytes & 15) == 0 &&
                  (!kv || (aligned(a->pool_v, 16) && aligned(a->hot_v, 16))))

@@ -62,6 +62,7 @@ def _args(**kw):
     (dict(hot_nrows=17), -1),             # flat regions need R*S_r rows
     (dict(pool=0x100002), -1),            # not 4-byte aligned
     (dict(row_bytes=1 << 21), -2),
+    (dict(stats=0x100004), -1),           # counters not 8-byte aligned
 ])
 def test_swap_in_rejects_bad_arguments(lib, kw, status):
     a = _args(**kw)
