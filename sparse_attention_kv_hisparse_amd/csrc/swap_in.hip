@@ -38,6 +38,13 @@ constexpr int kWaves = kThreads / kWave;
 #define HS_FUSE_UNROLL 12
 #endif
 constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused copy
+#ifndef HS_EARLY_CHUNKS
+#define HS_EARLY_CHUNKS 1
+#endif
+constexpr int kEarlyChunks = HS_EARLY_CHUNKS;  // fused copy: chunks per lane loaded before the victims
+// s_waitcnt immediate for vmcnt(0) alone: vmcnt bits [3:0] and [15:14] zero,
+// expcnt [6:4] and lgkmcnt [11:8] at their no-wait maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
 // 1024 lanes exactly), LRU phases four (H = 4096). A lane slot past the end of
 // a pass still costs issue cycles, so the unroll follows the common sizes.
@@ -549,7 +556,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
   __syncthreads();
 
-  // ---- 3. victims, the new LRU order, miss words ----------------------------
+  // ---- 3. miss words, (host pools) early row loads, victims, new LRU order ---
   // New order: stale evictables, then the M victims (they receive the misses,
   // in miss order), then the hits -- every group in its old order. A
   // position's rank among hits is the hits of earlier waves, plus this wave's
@@ -558,6 +565,88 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   const int hits_before = pre_hit[wave];
   const int E = H - hits;            // evictable slots
   const int M = pending_n - hits;    // misses (<= E because K <= H)
+  // The fused copy's list (pool row, hot row) in miss order, kept in the key
+  // and index arrays, which are free since the probe phase (6T >= 12K bytes).
+  int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
+  int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
+  // An id still pending after the probe is a miss: each wave records its
+  // segment's miss words and adds its miss total to the later waves' prefixes.
+  auto miss_words = [&]() {
+    int mrun = 0;
+    for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+      int32_t so[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int i = k0 + c0 + u * kWave + lane;
+        so[u] = (c0 + u * kWave < segK && i < K) ? s_out[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int q = k0 + c0 + u * kWave;
+        const uint64_t mm = __ballot(so[u] == kPending);
+        if (c0 + u * kWave < segK && q < K) {
+          if (lane == 0) missw[q >> 6] = mm;
+          mrun += __popcll(mm);
+        }
+      }
+    }
+    if (lane > wave && lane <= kWaves && mrun) atomicAdd(&pre_miss[lane], mrun);
+  };
+  // Host pools: the pool row of every miss is known now; only its hot row
+  // waits for the victims. The first kEarlyChunks chunks of every lane are
+  // loaded here, in the fused copy's order, so the host link is already busy
+  // while the victims and outputs are worked out. One per lane: with a whole
+  // round (kFuseUnroll per lane) outstanding the link moved less and the
+  // call got no faster; one per lane saves ~2% on the DeepSeek-V3.2-like step.
+  constexpr bool kEarlyCopy = kEarlyChunks > 0 && kCopyW != 0 && !kSlotRows && !kPoolRows;
+  const bool early = kEarlyCopy && (!kPaged || a.hbt_n != 0);   // uniform
+  typedef Chunk<kCopyW == 0 ? 4 : kCopyW> CE;
+  [[maybe_unused]] typename CE::T ev[kEarlyChunks > 0 ? kEarlyChunks : 1];
+  if constexpr (kEarlyCopy) {
+    if (early) {
+      miss_words();
+      __syncthreads();
+      int mrun = pre_miss[wave];
+      for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+        uint64_t wd[kKU];
+        int32_t t[kKU];
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          const int q = k0 + c0 + u * kWave;
+          const int i = q + lane;
+          const bool in = c0 + u * kWave < segK && q < K;
+          wd[u] = in ? missw[q >> 6] : 0;
+          t[u] = (in && i < K) ? s_topk[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          if ((wd[u] >> lane) & 1ull) l_src[mrun + rank_below(wd[u])] = pool_of(t[u]);
+          mrun += __popcll(wd[u]);
+        }
+      }
+      __syncthreads();
+      // Every earlier global load returned long ago; saying so keeps the
+      // compiler from waiting for them later, which (the counter retires in
+      // order) would mean waiting for these loads as well.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      const uint32_t C = a.cdiv.d;
+      const bool kv = a.pool_v != nullptr;
+      const uint32_t total = static_cast<uint32_t>(pre_miss[kWaves]) * (kv ? 2u : 1u) * C;
+#pragma unroll
+      for (int u = 0; u < kEarlyChunks; ++u) {
+        const uint32_t j = tid + u * kThreads;
+        ev[u] = typename CE::T{};
+        if (j < total) {
+          const uint32_t q = fdiv(j, a.cdiv);     // (miss, K/V) row
+          const uint32_t c = j - q * C;
+          const int64_t sr = l_src[kv ? q >> 1 : q];
+          if (sr >= 0 && sr < a.pool_nrows)
+            ev[u] = CE::load(((kv && (q & 1)) ? a.pool_v : a.pool) + sr * a.row_bytes +
+                             static_cast<int64_t>(c) * kCopyW);
+        }
+      }
+    }
+  }
   run = hits_before;
   int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
   for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += 4 * kWave) {
@@ -601,25 +690,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       run += __popcll(wd[u]);
     }
   }
-  run = 0;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
-    int32_t so[kKU];
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int i = k0 + c0 + u * kWave + lane;
-      so[u] = (c0 + u * kWave < segK && i < K) ? s_out[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int q = k0 + c0 + u * kWave;
-      const uint64_t mm = __ballot(so[u] == kPending);
-      if (c0 + u * kWave < segK && q < K) {
-        if (lane == 0) missw[q >> 6] = mm;
-        run += __popcll(mm);
-      }
-    }
-  }
-  if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_miss[lane], run);
+  if (!early) miss_words();
   __syncthreads();
 
   // ---- 4. misses in top-k order take victims; outputs; copy list -----------
@@ -630,10 +701,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int64_t* ws_src = a.src + static_cast<int64_t>(b) * K;
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
   int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
-  // With the copy fused in, the list is also kept in LDS (in the key and
-  // index arrays, free since the probe phase: 6T >= 12K bytes).
-  int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
-  int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
   run = miss_before;
   for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
     uint64_t wd[kKU];
@@ -673,7 +740,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         ws_src[m[u]] = pr;
         ws_dst[m[u]] = o;
         if constexpr (kCopyW != 0) {
-          l_src[m[u]] = pr;
+          if (!early) l_src[m[u]] = pr;
           l_dst[m[u]] = o;
         }
       }
@@ -714,7 +781,28 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     const uint32_t C = a.cdiv.d;
     const bool kv = a.pool_v != nullptr;    // uniform: a V row per miss too
     const uint32_t total = static_cast<uint32_t>(m_total) * (kv ? 2u : 1u) * C;
-    for (uint32_t j0 = tid; j0 < total; j0 += kThreads * kFuseUnroll) {
+    uint32_t j_first = tid;
+    if constexpr (kEarlyCopy) {
+      if (early) {   // the chunks loaded in phase 3 go to their hot rows now
+#pragma unroll
+        for (int u = 0; u < kEarlyChunks; ++u) {
+          const uint32_t j = tid + u * kThreads;
+          if (j < total) {
+            const uint32_t q = fdiv(j, a.cdiv);
+            const uint32_t c = j - q * C;
+            const uint32_t mm = kv ? q >> 1 : q;
+            const int64_t sr = l_src[mm];
+            const int32_t hr = l_dst[mm];
+            if (sr >= 0 && sr < a.pool_nrows && hr >= 0 && hr < a.hot_nrows)
+              CW::store(((kv && (q & 1)) ? a.hot_v : a.hot) + static_cast<int64_t>(hr) * a.row_bytes +
+                            static_cast<int64_t>(c) * kCopyW,
+                        ev[u]);
+          }
+        }
+        j_first += kEarlyChunks * kThreads;
+      }
+    }
+    for (uint32_t j0 = j_first; j0 < total; j0 += kThreads * kFuseUnroll) {
       typename CW::T cv[kFuseUnroll];
       char* cd[kFuseUnroll];
 #pragma unroll
