@@ -110,28 +110,44 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterSide k, Scatte
   typedef Chunk<W> C;
   const uint32_t step = gridDim.x * kThreads * kUnroll;
   for (uint32_t j0 = blockIdx.x * kThreads * kUnroll + threadIdx.x; j0 < total; j0 += step) {
+    // A round: every load of the round in flight at once, then the stores,
+    // with no branch in front of them (a lane with nothing to store writes its
+    // sink slot). The wait on entry tells the compiler the previous round is
+    // done; without it, and with the stores behind branches, it waits for
+    // every earlier access before each load and store, one row at a time.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     typename C::T val[kUnroll];
-    char* d[kUnroll];
+    int64_t to[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t j = j0 + u * kThreads;
-      d[u] = nullptr;
-      if (j < total) {
-        const uint32_t q = fdiv(j, cdiv);
-        const uint32_t c = j - q * cdiv.d;
-        const uint32_t row = kv ? q >> 1 : q;
-        const ScatterSide& sd = (kv && (q & 1)) ? v : k;
-        // The source row is always in range (row < n): its load does not wait
-        // for loc, so the two loads are in flight together.
-        const int64_t off = static_cast<int64_t>(c) * W;
-        val[u] = C::load(sd.src + static_cast<int64_t>(row) * sd.src_stride + off);
-        const int64_t to = loc[row];
-        if (to >= 0 && to < dst_nrows) d[u] = sd.dst + to * sd.dst_stride + off;
-      }
+      const uint32_t jj = j < total ? j : j0;
+      const uint32_t q = fdiv(jj, cdiv);
+      const uint32_t c = jj - q * cdiv.d;
+      const uint32_t row = kv ? q >> 1 : q;
+      // Field by field: a per-lane choice of a whole argument struct would be
+      // read from the argument segment with vector loads.
+      const bool isv = kv && (q & 1);
+      const char* sbase = isv ? v.src : k.src;
+      const int64_t sstride = isv ? v.src_stride : k.src_stride;
+      // The source row is always in range (row < n): its load does not wait
+      // for loc, so the two loads are in flight together.
+      val[u] = C::load(sbase + static_cast<int64_t>(row) * sstride + static_cast<int64_t>(c) * W);
+      to[u] = loc[row];
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (d[u]) C::store(d[u], val[u]);
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t j = j0 + u * kThreads;
+      const uint32_t jj = j < total ? j : j0;
+      const uint32_t q = fdiv(jj, cdiv);
+      const uint32_t c = jj - q * cdiv.d;
+      const bool isv = kv && (q & 1);
+      char* dbase = isv ? v.dst : k.dst;
+      const int64_t dstride = isv ? v.dst_stride : k.dst_stride;
+      const bool ok = j < total && to[u] >= 0 && to[u] < dst_nrows;
+      C::store(ok ? dbase + to[u] * dstride + static_cast<int64_t>(c) * W : store_sink(), val[u]);
+    }
   }
 }
 

@@ -75,6 +75,18 @@ struct Chunk<4> {
   static __device__ __forceinline__ void store(char* p, T v) { *reinterpret_cast<uint32_t*>(p) = v; }
 };
 
+// s_waitcnt immediate for vmcnt(0) alone: vmcnt bits [3:0] and [15:14] zero,
+// expcnt [6:4] and lgkmcnt [11:8] at their no-wait maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Lanes with nothing to store in a branch-free round write a private 16-byte
+// slot here instead. One slot per lane of a workgroup of up to 1024; the
+// slots hold garbage and are never read.
+namespace {
+__device__ __align__(16) u32x4 g_store_sink[1024];
+}
+__device__ __forceinline__ char* store_sink() { return reinterpret_cast<char*>(&g_store_sink[threadIdx.x]); }
+
 // Chunks a row of `row_bytes` splits into at width W.
 inline int64_t chunks_per_row(int64_t row_bytes, int W) { return row_bytes / W; }
 

@@ -42,9 +42,6 @@ constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused
 #define HS_EARLY_CHUNKS 1
 #endif
 constexpr int kEarlyChunks = HS_EARLY_CHUNKS;  // fused copy: chunks per lane loaded before the victims
-// s_waitcnt immediate for vmcnt(0) alone: vmcnt bits [3:0] and [15:14] zero,
-// expcnt [6:4] and lgkmcnt [11:8] at their no-wait maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
 // 1024 lanes exactly), LRU phases four (H = 4096). A lane slot past the end of
 // a pass still costs issue cycles, so the unroll follows the common sizes.
