@@ -11,8 +11,11 @@
 // Work is one flat stream of (pair, layer, chunk) items rather than one warp
 // per item looping over layers: every lane moves one 16-byte chunk, lanes of a
 // wave cover consecutive chunks of consecutive rows, and a grid-stride loop
-// with several independent loads in flight per lane keeps enough bytes
-// outstanding to cover host-link latency as well as HBM latency.
+// takes several chunks per lane per round. In the transfer the generated code
+// waits for each read before the next, so the waves in flight, not the
+// unroll, keep bytes outstanding; that form measured best on the host link
+// and in HBM. The scatter, with too few rows to fill the chip, issues all of
+// a round's reads before its stores.
 #include <hip/hip_runtime.h>
 
 #include "hs_common.hpp"
@@ -21,7 +24,7 @@ namespace hs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;          // chunks in flight per lane, HBM-sized launches
+constexpr int kUnroll = 4;          // chunks per lane per round, HBM-sized launches
 constexpr int kHostLinkUnroll = 8;  // ... and with HS_TRANSFER_HOST_LINK
 constexpr int kMaxStagedLayers = 256;
 
@@ -227,7 +230,7 @@ int launch_transfer(const LayerPtrs& lp, const int64_t* src_idx, const int64_t* 
     const uint32_t total = static_cast<uint32_t>(np * per_pair);
     if (host_link) {
       // The host link is full with far fewer requesters than HBM needs:
-      // one workgroup per two CUs, 8 chunks in flight per lane (all-layer
+      // one workgroup per two CUs, 8 chunks per lane per round (all-layer
       // load of 656-byte rows: 44.7 -> 47.7 GB/s against the HBM-sized
       // launch; offload 51.9 -> 51.7).
       const uint64_t need = (total + kThreads * kHostLinkUnroll - 1) / (kThreads * kHostLinkUnroll);

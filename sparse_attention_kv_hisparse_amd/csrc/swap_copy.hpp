@@ -21,7 +21,7 @@ namespace hs {
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 8;        // chunks in flight per copy lane
+constexpr int kCopyUnroll = 8;        // chunks per copy lane per round
 constexpr int kMaxStagedPairs = 256;  // layer pointer pairs staged in LDS
 
 // One miss list and the row spaces it indexes.
@@ -47,8 +47,11 @@ struct MissList {
 // Workgroup g serves request g % B, part g / B of `parts`. Items are
 // (miss, layer, chunk) -- or (miss, K/V, chunk) for a single non-MLA pair --
 // with the chunk fastest: consecutive lanes take consecutive chunks of one
-// row, so each wave's accesses coalesce, and every lane keeps kCopyUnroll
-// independent loads in flight.
+// row, so each wave's accesses coalesce. A lane takes kCopyUnroll chunks per
+// round; the generated code reads them one after another (it waits for each
+// list entry, and so for every earlier access), and the waves of a full chip
+// keep HBM busy. Rewrites with every read of a round in flight measured
+// slower here, in HBM and over the host link alike.
 template <int W, bool kLayers>
 __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int32_t parts) {
   typedef Chunk<W> C;

@@ -21,6 +21,10 @@
 //    list in the caller's workspace, are copied by many 256-lane workgroups
 //    per request as a flat stream of 16-byte chunks. The kernel boundary is
 //    the only hand-off between the two, so no workgroup ever waits on another.
+//  * With a pinned-host pool the resolve kernel copies its own request's rows
+//    as well (phase 5): the host link is full with one workgroup per request.
+//    Each lane issues its first chunk's read right after the probe, while the
+//    victims and outputs are still being worked out.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -37,7 +41,7 @@ constexpr int kWaves = kThreads / kWave;
 #ifndef HS_FUSE_UNROLL
 #define HS_FUSE_UNROLL 12
 #endif
-constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks in flight per lane, fused copy
+constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks per lane per round, fused copy
 #ifndef HS_EARLY_CHUNKS
 #define HS_EARLY_CHUNKS 1
 #endif
@@ -769,9 +773,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 
   // ---- 5. (host pools) the request's own row copies -------------------------
   // The workgroup copies its misses straight from the LDS list, as soon as its
-  // own resolution is done: over the host link a few dozen CUs with every
-  // lane keeping kFuseUnroll chunks in flight already fill the link, and this
-  // saves a second launch and its start-up and drain.
+  // own resolution is done, in rounds of kFuseUnroll chunks per lane. This
+  // saves a second launch and its start-up and drain. The generated code
+  // waits for each read before issuing the next, so a lane keeps about one
+  // read in flight. A few dozen workgroups of 1024 lanes fill the host link
+  // that way, and rewrites with every read of a round in flight moved less
+  // over the link, so the loop stays in this plain form.
   if constexpr (kCopyW != 0) {
     typedef Chunk<kCopyW> CW;
     __syncthreads();
