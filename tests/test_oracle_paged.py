@@ -67,8 +67,8 @@ def test_paged_worked_example():
         assert lru.tolist() == e["lru"]
 
 
-def _random_tables(rng, R, H, ctx):
-    hb = int(rng.choice([1, 2, 4, 8]))
+def _random_tables(rng, R, H, ctx, hb=None):
+    hb = int(rng.choice([1, 2, 4, 8])) if hb is None else hb
     nhb = -(-H // hb)
     extra = 3
     hot_blocks = rng.permutation(R * nhb + extra)[:R * nhb].reshape(R, nhb).astype(np.int32)
