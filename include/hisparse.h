@@ -218,11 +218,12 @@ int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t worksp
  * copy: outputs, state and miss counts are final, and the workspace holds
  * each row's miss list (see hs_swap_in_workspace_layout).
  * hisparse_gather_compact copies the rows that list names, from pool to hot.
- * Both take the same argument struct; gather reads only B, K, pool,
- * pool_nrows, hot, hot_nrows and row_bytes from it, plus the workspace, which
- * must hold the list of a resolve call with the same B and K enqueued before
- * it (on the same stream, or ordered by an event). Resolve then gather is
- * exactly hisparse_swap_in. Errors as for hisparse_swap_in.
+ * Both take the same argument struct and check it the same way. The gather
+ * kernel uses only B, K, pool, pool_nrows, hot, hot_nrows, row_bytes and
+ * pool_v / hot_v from it (it leaves outputs, state and stats alone), plus the
+ * workspace, which must hold the list of a resolve call with the same B and K
+ * enqueued before it (on the same stream, or ordered by an event). Resolve
+ * then gather is exactly hisparse_swap_in. Errors as for hisparse_swap_in.
  * Per list entry (as vLLM's hisparse_gather_compact_kernel): the count is
  * clamped to [0, K]; an entry whose pool row is negative or whose hot row is
  * outside [0, hot_nrows) is skipped; a pool row >= pool_nrows writes zeros to
