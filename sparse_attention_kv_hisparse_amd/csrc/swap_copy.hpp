@@ -20,7 +20,8 @@
 namespace hs {
 namespace {
 
-constexpr int kCopyThreads = 256;
+constexpr int kCopyThreads = 256;       // lanes per copy workgroup: host pools, plan replay
+constexpr int kCopyThreadsHbm = 1024;   // ... single pair from an HBM pool
 constexpr int kCopyUnroll = 8;        // chunks per copy lane per round
 constexpr int kMaxStagedPairs = 256;  // layer pointer pairs staged in LDS
 
@@ -52,14 +53,14 @@ struct MissList {
 // list entry, and so for every earlier access), and the waves of a full chip
 // keep HBM busy. Rewrites with every read of a round in flight measured
 // slower here, in HBM and over the host link alike.
-template <int W, bool kLayers>
-__global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int32_t parts) {
+template <int W, bool kLayers, int kT>
+__global__ __launch_bounds__(kT) void swap_copy_kernel(MissList a, int32_t parts) {
   typedef Chunk<W> C;
   __shared__ uint64_t s_pool[kLayers ? kMaxStagedPairs : 1];
   __shared__ uint64_t s_hot[kLayers ? kMaxStagedPairs : 1];
   const bool staged = kLayers && a.layers <= kMaxStagedPairs;
   if (staged) {
-    for (int l = threadIdx.x; l < a.layers; l += kCopyThreads) {
+    for (int l = threadIdx.x; l < a.layers; l += kT) {
       s_pool[l] = a.pool_layers[l];
       s_hot[l] = a.hot_layers[l];
     }
@@ -74,8 +75,8 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
   const uint32_t total = static_cast<uint32_t>(M) * per_miss;
   const int64_t* src = a.src + static_cast<int64_t>(b) * a.K;
   const int32_t* dst = a.dst + static_cast<int64_t>(b) * a.K;
-  const uint32_t stride = static_cast<uint32_t>(parts) * kCopyThreads;
-  for (uint32_t j0 = static_cast<uint32_t>(part) * kCopyThreads + threadIdx.x; j0 < total;
+  const uint32_t stride = static_cast<uint32_t>(parts) * kT;
+  for (uint32_t j0 = static_cast<uint32_t>(part) * kT + threadIdx.x; j0 < total;
        j0 += stride * kCopyUnroll) {
     typename C::T v[kCopyUnroll];
     char* d[kCopyUnroll];
@@ -125,12 +126,13 @@ __global__ __launch_bounds__(kCopyThreads) void swap_copy_kernel(MissList a, int
   }
 }
 
-// Workgroups per CU at most: HBM wants many loads in flight; the host link
-// does better with fewer requesters (a pinned-host pool copied with one
+// Lanes per CU at most: HBM wants many loads in flight; the host link does
+// better with fewer requesters (a pinned-host pool copied with one 256-lane
 // workgroup per CU takes ~11% less time than with eight, measured on the
-// DeepSeek-V3.2-like decode step).
-constexpr int kCopyWgsPerCu = 8;
-constexpr int kHostCopyWgsPerCu = 1;
+// DeepSeek-V3.2-like decode step). From an HBM pool the same 2048 lanes per CU
+// run as two 1024-lane workgroups: ~1.5% faster than eight of 256.
+constexpr int kCopyLanesPerCu = 2048;
+constexpr int kHostCopyLanesPerCu = 256;
 
 // Grid: enough workgroups per request to cover its worst case (all K ids
 // missing, every layer) at kCopyUnroll chunks per lane, capped per CU
@@ -138,25 +140,32 @@ constexpr int kHostCopyWgsPerCu = 1;
 inline int launch_swap_copy(const MissList& a, int W, int num_cus, hipStream_t stream,
                             bool host_pool = false) {
   const bool layered = a.pool_layers != nullptr;
+  const bool wide = !layered && !host_pool;   // 1024-lane workgroups
+  const int64_t T = wide ? kCopyThreadsHbm : kCopyThreads;
   const int64_t streams = layered ? a.layers : (a.pool_v ? 2 : 1);
   const int64_t max_items = static_cast<int64_t>(a.K) * streams * a.cdiv.d;
-  int64_t parts = (max_items + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
-  const int64_t per_cu = host_pool ? kHostCopyWgsPerCu : kCopyWgsPerCu;
+  int64_t parts = (max_items + T * kCopyUnroll - 1) / (T * kCopyUnroll);
+  const int64_t per_cu = (host_pool ? kHostCopyLanesPerCu : kCopyLanesPerCu) / T;
   const int64_t cap = (per_cu * num_cus + a.B - 1) / a.B;
   if (parts > cap) parts = cap;
   if (parts < 1) parts = 1;
   const dim3 grid(static_cast<unsigned>(a.B * parts));
   const int32_t p = static_cast<int32_t>(parts);
+  const dim3 block(static_cast<unsigned>(T));
   if (W == 16) {
     if (layered)
-      hipLaunchKernelGGL((swap_copy_kernel<16, true>), grid, dim3(kCopyThreads), 0, stream, a, p);
+      hipLaunchKernelGGL((swap_copy_kernel<16, true, kCopyThreads>), grid, block, 0, stream, a, p);
+    else if (wide)
+      hipLaunchKernelGGL((swap_copy_kernel<16, false, kCopyThreadsHbm>), grid, block, 0, stream, a, p);
     else
-      hipLaunchKernelGGL((swap_copy_kernel<16, false>), grid, dim3(kCopyThreads), 0, stream, a, p);
+      hipLaunchKernelGGL((swap_copy_kernel<16, false, kCopyThreads>), grid, block, 0, stream, a, p);
   } else {
     if (layered)
-      hipLaunchKernelGGL((swap_copy_kernel<4, true>), grid, dim3(kCopyThreads), 0, stream, a, p);
+      hipLaunchKernelGGL((swap_copy_kernel<4, true, kCopyThreads>), grid, block, 0, stream, a, p);
+    else if (wide)
+      hipLaunchKernelGGL((swap_copy_kernel<4, false, kCopyThreadsHbm>), grid, block, 0, stream, a, p);
     else
-      hipLaunchKernelGGL((swap_copy_kernel<4, false>), grid, dim3(kCopyThreads), 0, stream, a, p);
+      hipLaunchKernelGGL((swap_copy_kernel<4, false, kCopyThreads>), grid, block, 0, stream, a, p);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(HS_ELAUNCH, "copy launch: %s", hipGetErrorString(e));
