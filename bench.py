@@ -667,7 +667,7 @@ def main():
                           "GBps_rows_read_written": round(
                               d["cold_rows"] * 2 * dcfg.row_bytes / d["us_cold"] / 1e3, 1)},
             "effective_GBps_call": round(dcall, 1), "frac_hbm_call": round(dcall / HBM_PEAK_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16, false>", "achieved": round(dach, 1),
+            "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16, false, 1024>", "achieved": round(dach, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("device_pool")},
         }
