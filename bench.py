@@ -276,7 +276,7 @@ def run_paged(cfg, warmup, steps, torch, hs, wdev, block=64):
     seeded permutation of physical blocks, block 0 unused) to global pool
     rows, and its slots through a hot block table of `block`-slot blocks (a
     seeded permutation). W warm-up calls, then K hisparse_swap_in calls
-    between two events. Returns dict(us_total, rows)."""
+    between two events, queued behind a spin kernel. Returns dict(us_total, rows)."""
     rng = np.random.default_rng(cfg.seed + 99)
     R, B, H, K, ctx = cfg.R, cfg.B, cfg.H, cfg.K, cfg.ctx
     nsb = -(-ctx // block)
@@ -306,6 +306,11 @@ def run_paged(cfg, warmup, steps, torch, hs, wdev, block=64):
         call(t)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The paged arguments cost the Python binding more host time per call than
+    # the flat ones, on some hosts more than the call's kernel. A spin kernel
+    # ahead of the first event (about 10 ms) lets the host enqueue every call
+    # first, so the events bracket the calls' kernels back to back.
+    torch.cuda._sleep(24_000_000)
     e0.record(stream)
     for k in range(steps):
         call(warmup + k)
