@@ -77,8 +77,11 @@ def _small(**kw):
     dict(H=16384, K=2048, ctx=40000, B=2, steps=3, pool_kind="device"),
     dict(B=600, H=96, K=40, ctx=400, steps=4),        # more requests than CUs (fused copy)
     dict(B=600, H=96, K=40, ctx=400, steps=4, pool_kind="device"),
+    # largest sizes the per-request LDS scratch allows (160 KB per workgroup):
+    dict(H=32768, K=584, ctx=70000, B=2, steps=3, row_bytes=16),   # H at its maximum
+    dict(H=4096, K=4096, ctx=9000, B=2, steps=3, row_bytes=16),    # K at its maximum
 ], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single",
-        "unstaged_host", "unstaged_dev", "many_host", "many_dev"])
+        "unstaged_host", "unstaged_dev", "many_host", "many_dev", "max_H", "max_K"])
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
@@ -177,6 +180,30 @@ def test_empty_calls_are_noops():
                         out_rows=out, ctx_stride=cfg.ctx, workspace=st.ws)
     torch.cuda.synchronize()
     assert torch.equal(before, st.lru)
+
+
+@pytest.mark.parametrize("H,K", [(32768, 585), (8192, 4097), (32768, 32768)])
+def test_sizes_beyond_lds_are_rejected(H, K):
+    """K and H whose per-request scratch does not fit one workgroup's LDS
+    return HS_ERANGE before anything is enqueued: state and outputs untouched."""
+    import sparse_attention_kv_hisparse_amd as hs
+    from sparse_attention_kv_hisparse_amd._lib import HisparseError
+    from workloads import device as wdev
+    cfg = _small(H=H, K=K, ctx=2 * H, B=1, row_bytes=16)
+    st = wdev.DeviceSwapState(cfg)
+    pool = wdev.make_pool(cfg)
+    st.out.fill_(7)
+    before = (st.slot_tokens.clone(), st.lru.clone(), st.out.clone())
+    topk = torch.arange(K, dtype=torch.int32, device="cuda").reshape(1, K)
+    with pytest.raises(HisparseError) as e:
+        hs.hisparse_swap_in(topk=topk, req_rows=torch.zeros(1, dtype=torch.int64, device="cuda"),
+                            seq_lens=torch.full((1,), cfg.ctx, dtype=torch.int64, device="cuda"),
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws)
+    assert e.value.status == -2 and "LDS" in str(e.value)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (st.slot_tokens, st.lru, st.out)):
+        assert torch.equal(a, b)
 
 
 def test_replay_from_restored_state_is_identical():
