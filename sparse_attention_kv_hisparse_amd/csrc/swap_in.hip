@@ -38,14 +38,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-#ifndef HS_FUSE_UNROLL
-#define HS_FUSE_UNROLL 12
-#endif
-constexpr int kFuseUnroll = HS_FUSE_UNROLL;  // chunks per lane per round, fused copy
-#ifndef HS_EARLY_CHUNKS
-#define HS_EARLY_CHUNKS 1
-#endif
-constexpr int kEarlyChunks = HS_EARLY_CHUNKS;  // fused copy: chunks per lane loaded before the victims
+constexpr int kFuseUnroll = 12;  // chunks per lane per round, fused copy
+constexpr int kEarlyChunks = 1;  // fused copy: chunks per lane loaded before the victims
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
 // 1024 lanes exactly), LRU phases four (H = 4096). A lane slot past the end of
 // a pass still costs issue cycles, so the unroll follows the common sizes.
@@ -907,10 +901,6 @@ const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged) {
                    : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false>);
 }
 
-#ifndef HS_FUSE_HOST_COPY
-#define HS_FUSE_HOST_COPY 1
-#endif
-
 // Everything a launch needs, validated once per call.
 struct Plan {
   SwapArgs s;
@@ -1061,7 +1051,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // link, not the CU count, bounds the copy); an HBM pool gets the wide copy
   // kernel, which spreads every request over many CUs.
   const void* fused_fn = nullptr;
-  if (HS_FUSE_HOST_COPY && attr.type == hipMemoryTypeHost) {
+  if (attr.type == hipMemoryTypeHost) {
     fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg) : pick_resolve<4>(sr, prw, pg);
     if (lay.total > 65536) {
       rc = allow_lds(di.device, fused_fn, lay.total);
