@@ -119,6 +119,13 @@ static int check_args(const oracle_swap_in_args *a) {
     if (p->src_block_table && (p->src_block_size <= 0 || p->src_num_blocks < 0)) return ORACLE_EARG;
     if (p->resident_block_table && (p->resident_block_size <= 0 || p->resident_num_blocks < 0))
       return ORACLE_EARG;
+    /* vLLM page, host checks of hisparse_resolve_residency: a resident lookup
+     * needs the source block table, the resident and hot block sizes must
+     * match, and the resident null block must be non-negative. */
+    if (p->resident_block_table &&
+        (!p->src_block_table || p->resident_block_size != p->hot_block_size ||
+         p->resident_null_block < 0))
+      return ORACLE_EARG;
     if (a->pool_nrows > INT32_MAX) return ORACLE_EARG;   /* keys are int32 global ids */
   }
   return ORACLE_OK;

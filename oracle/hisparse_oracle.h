@@ -59,7 +59,10 @@ typedef struct {
   /* Optional: positions still resident in the device cache. Block
    * t / resident_block_size (below resident_num_blocks) maps to p; p >= 0 and
    * p != resident_null_block makes the entry resident at row
-   * p * resident_block_size + t % resident_block_size, served as is. */
+   * p * resident_block_size + t % resident_block_size, served as is.
+   * As the vLLM page's host checks require: the table needs a source block
+   * table, resident_block_size == hot_block_size and resident_null_block >= 0;
+   * otherwise the call returns ORACLE_EARG. */
   const int32_t *resident_block_table;
   int64_t resident_table_stride;
   int32_t resident_num_blocks, resident_block_size, resident_null_block;

@@ -1,8 +1,11 @@
 """MI355X HiSparse swap-in: Python binding of libhisparse.so.
 
-Argument marshalling only. Each function takes torch tensors, checks
-dtype/device/shape enough to pass correct pointers, and calls the C ABI of
-``include/hisparse.h`` on torch's current HIP stream. All work runs in the
+Argument marshalling only. Each function takes torch tensors, checks the
+dtype, device, contiguity and shape of every tensor against the sizes the call
+derives (B, K, R, H, S_r, ctx_stride, n), raising ValueError before anything
+is enqueued, and calls the C ABI of ``include/hisparse.h`` on torch's current
+HIP stream. A tensor too small for the pointer the library is handed would
+otherwise be read or written out of bounds on the device. All work runs in the
 library's HIP kernels; nothing here computes, and nothing falls back.
 """
 
@@ -37,6 +40,21 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
 
 def _opt(t: Optional[torch.Tensor], dtype, name) -> Optional[int]:
     return None if t is None else _dev(t, dtype, name)
+
+
+def _vec(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """A contiguous 1-D tensor of at least n elements (or None)."""
+    if t is not None and (t.dim() != 1 or not t.is_contiguous() or t.numel() < n):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of at least {n} elements, "
+                         f"got shape {tuple(t.shape)}")
+
+
+def _mat(t: Optional[torch.Tensor], rows: int, cols: int, name: str) -> None:
+    """A contiguous 2-D tensor of at least `rows` rows and exactly `cols` columns (or None)."""
+    if t is not None and (t.dim() != 2 or not t.is_contiguous() or t.shape[0] < rows
+                          or t.shape[1] != cols):
+        raise ValueError(f"{name} must be a contiguous [>={rows}, {cols}] tensor, "
+                         f"got shape {tuple(t.shape)}")
 
 
 def swap_in_workspace_bytes(B: int, K: int) -> int:
@@ -98,9 +116,21 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         raise ValueError("pool and hot must be contiguous [rows, row_bytes] with equal row_bytes")
     if pool.dtype != torch.uint8 or hot.dtype != torch.uint8:
         raise ValueError("pool and hot are uint8 byte rows")
-    if not hot.is_cuda:
-        raise ValueError("hot must be a device tensor")
+    if slot_tokens.dim() != 2 or lru.dim() != 2:
+        raise ValueError("slot_tokens must be [R, S_r] and lru [R, H]")
     R, S_r = slot_tokens.shape
+    H = lru.shape[1]
+    if lru.shape[0] != R:
+        raise ValueError(f"lru has {lru.shape[0]} rows, slot_tokens {R}")
+    if tuple(out_rows.shape) != (B, K) or out_rows.dim() != 2:
+        raise ValueError("out_rows must be [B, K]")
+    _vec(req_rows, B, "req_rows")
+    _vec(seq_lens, B, "seq_lens")
+    _vec(miss_counts, B, "miss_counts")
+    _vec(num_real, 1, "num_real")
+    _mat(slot_rows, R, S_r, "slot_rows")
+    if pool_rows is not None:
+        _mat(pool_rows, R, ctx_stride, "pool_rows")
     pg = None
     if paged is not None:
         def tab(name):
@@ -109,10 +139,15 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                 return None, 0
             if t.dim() != 2 or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous 2-D int32 tensor")
-            return _dev(t, torch.int32, name), t.shape[1]
+            if t.shape[0] < R:   # tables are indexed by the state row
+                raise ValueError(f"{name} must have a row for each of the {R} state rows")
+            return t, t.shape[1]
         hbt, hst = tab("hot_block_table")
         sbt, sst = tab("src_block_table")
         rbt, rst = tab("resident_block_table")
+        hbt = _opt(hbt, torch.int32, "hot_block_table")
+        sbt = _opt(sbt, torch.int32, "src_block_table")
+        rbt = _opt(rbt, torch.int32, "resident_block_table")
         att = paged.get("attention_indices")
         if att is not None and (att.dim() != 2 or att.shape[0] != B or not att.is_contiguous()):
             raise ValueError("attention_indices must be a contiguous [B, >=K] int32 tensor")
@@ -126,8 +161,10 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
             attention_indices=_opt(att, torch.int32, "attention_indices"),
             attention_row_stride=0 if att is None else att.shape[1],
             attention_block_stride=paged.get("attention_block_stride", 0))
+    if not hot.is_cuda:
+        raise ValueError("hot must be a device tensor")
     a = SwapInArgs(
-        B=B, K=K, H=lru.shape[1], S_r=S_r, R=R,
+        B=B, K=K, H=H, S_r=S_r, R=R,
         topk_ids=_dev(topk, torch.int32, "topk"), topk_stride=topk.stride(0),
         req_rows=_dev(req_rows, torch.int64, "req_rows"),
         seq_lens=None if seq_lens is None else _dev(seq_lens, torch.int64, "seq_lens"),
@@ -194,6 +231,9 @@ def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: tor
     L = src_layer_ptrs.numel()
     if dst_layer_ptrs.numel() != L or src_idx.numel() != dst_idx.numel():
         raise ValueError("pointer arrays / index arrays must have equal lengths")
+    for t, n in ((src_layer_ptrs, "src_layer_ptrs"), (dst_layer_ptrs, "dst_layer_ptrs"),
+                 (src_idx, "src_idx"), (dst_idx, "dst_idx")):
+        _vec(t, 0, n)
     check("transfer_rows_all_layer", load().transfer_rows_all_layer(
         _dev(src_layer_ptrs, torch.int64, "src_layer_ptrs"),
         _dev(dst_layer_ptrs, torch.int64, "dst_layer_ptrs"),
@@ -214,6 +254,10 @@ def transfer_kv_all_layer(*, k_src_layer_ptrs: torch.Tensor, v_src_layer_ptrs: t
         raise ValueError("layer pointer arrays must have equal lengths")
     if src_idx.numel() != dst_idx.numel():
         raise ValueError("index arrays must have equal lengths")
+    for t, n in ((k_src_layer_ptrs, "k_src_layer_ptrs"), (v_src_layer_ptrs, "v_src_layer_ptrs"),
+                 (k_dst_layer_ptrs, "k_dst_layer_ptrs"), (v_dst_layer_ptrs, "v_dst_layer_ptrs"),
+                 (src_idx, "src_idx"), (dst_idx, "dst_idx")):
+        _vec(t, 0, n)
     check("transfer_kv_all_layer", load().transfer_kv_all_layer(
         _dev(k_src_layer_ptrs, torch.int64, "k_src_layer_ptrs"),
         _dev(v_src_layer_ptrs, torch.int64, "v_src_layer_ptrs"),
@@ -233,7 +277,12 @@ def store_kv_cache(*, k_src: torch.Tensor, v_src: torch.Tensor, k_dst: torch.Ten
             raise ValueError(f"{n} must be a 2-D uint8 tensor with contiguous rows")
     if k_dst.shape[0] != v_dst.shape[0] or k_src.shape != v_src.shape:
         raise ValueError("K and V sides must have matching row counts")
+    _vec(loc, 0, "loc")
+    if loc.numel() > k_src.shape[0]:
+        raise ValueError(f"loc has {loc.numel()} entries, the sources {k_src.shape[0]} rows")
     rb = row_bytes or k_src.shape[1]
+    if rb > min(k_src.shape[1], k_dst.shape[1], v_dst.shape[1]):
+        raise ValueError("row_bytes exceeds a row of the sources or destinations")
     check("store_kv_cache", load().store_kv_cache(
         _dev(k_src, torch.uint8, "k_src"), k_src.stride(0), _dev(v_src, torch.uint8, "v_src"),
         v_src.stride(0), _dev(k_dst, torch.uint8, "k_dst"), k_dst.stride(0),
@@ -248,7 +297,12 @@ def store_kv_scatter(*, src: torch.Tensor, dst: torch.Tensor, loc: torch.Tensor,
         raise ValueError("src and dst are 2-D uint8 row tensors")
     if src.stride(1) != 1 or dst.stride(1) != 1:
         raise ValueError("rows must be contiguous")
+    _vec(loc, 0, "loc")
+    if loc.numel() > src.shape[0]:
+        raise ValueError(f"loc has {loc.numel()} entries, src {src.shape[0]} rows")
     rb = row_bytes or src.shape[1]
+    if rb > min(src.shape[1], dst.shape[1]):
+        raise ValueError("row_bytes exceeds a row of src or dst")
     check("store_kv_scatter", load().store_kv_scatter(
         _dev(src, torch.uint8, "src"), src.stride(0), _dev(dst, torch.uint8, "dst"), dst.stride(0),
         dst.shape[0], _dev(loc, torch.int64, "loc"), loc.numel(), rb, _stream(stream)))
@@ -261,6 +315,8 @@ def hisparse_invalidate_written(*, slot_keys: torch.Tensor, rows: torch.Tensor,
         raise ValueError("slot_keys must be a contiguous [R, S_r] int32 tensor")
     if rows.numel() != written.numel():
         raise ValueError("rows and written must have equal lengths")
+    _vec(rows, 0, "rows")
+    _vec(written, 0, "written")
     R, S_r = slot_keys.shape
     check("hisparse_invalidate_written", load().hisparse_invalidate_written(
         _dev(slot_keys, torch.int32, "slot_keys"), R, S_r, _dev(rows, torch.int64, "rows"),
@@ -269,6 +325,11 @@ def hisparse_invalidate_written(*, slot_keys: torch.Tensor, rows: torch.Tensor,
 
 def hisparse_state_reset(*, slot_tokens: torch.Tensor, lru: torch.Tensor, rows: torch.Tensor,
                          stream=None) -> None:
+    """Initial state for state rows ``rows``: every slot token -1, LRU 0..H-1."""
+    if slot_tokens.dim() != 2 or lru.dim() != 2 or not slot_tokens.is_contiguous() \
+            or not lru.is_contiguous() or lru.shape[0] != slot_tokens.shape[0]:
+        raise ValueError("slot_tokens [R, S_r] and lru [R, H] must be contiguous with R rows each")
+    _vec(rows, 0, "rows")
     R, S_r = slot_tokens.shape
     check("hisparse_state_reset", load().hisparse_state_reset(
         _dev(slot_tokens, torch.int32, "slot_tokens"), _dev(lru, torch.int16, "lru"),

@@ -945,6 +945,13 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
         (pa->resident_block_size <= 0 || pa->resident_num_blocks < 0 ||
          pa->resident_table_stride < pa->resident_num_blocks))
       return set_error(HS_EINVAL, "bad resident block table geometry");
+    // vLLM page, host checks of hisparse_resolve_residency.
+    if (pa->resident_block_table && !pa->src_block_table)
+      return set_error(HS_EINVAL, "a resident block table needs a source block table");
+    if (pa->resident_block_table && pa->resident_block_size != pa->hot_block_size)
+      return set_error(HS_EINVAL, "resident and hot block sizes must match");
+    if (pa->resident_block_table && pa->resident_null_block < 0)
+      return set_error(HS_EINVAL, "the resident null block must be non-negative");
     if (pa->attention_indices && pa->attention_row_stride < a->K)
       return set_error(HS_EINVAL, "attention_row_stride must be >= K");
     if (a->pool_nrows > 0x7fffffffll || a->hot_nrows > 0x7fffffffll)

@@ -230,6 +230,15 @@ def test_paged_addressing_validation(lib):
     assert call(src_block_table=f, src_block_size=4, src_num_blocks=5, src_table_stride=4) == -1
     assert call(resident_block_table=f, resident_block_size=4, resident_num_blocks=2,
                 resident_table_stride=1) == -1
+    # The vLLM page's host checks of a resident table: it needs the source
+    # table, block sizes equal to the hot block size, a non-negative null block.
+    src = dict(src_block_table=f, src_block_size=4, src_num_blocks=4, src_table_stride=4)
+    res = dict(resident_block_table=f, resident_block_size=2, resident_num_blocks=4,
+               resident_table_stride=4, resident_null_block=0)
+    assert call(**res) == -1                                      # no source table
+    assert call(**src, **dict(res, resident_block_size=4)) == -1  # sizes differ
+    assert call(**src, **dict(res, resident_null_block=-1)) == -1
+    assert call(**src, **res) != -1                               # in the page's domain
     assert call(attention_indices=f, attention_row_stride=3) == -1   # < K = 4
     a = _args(seq_lens=None)
     assert lib.hisparse_swap_in(ctypes.byref(a), ctypes.c_void_p(0x200000), 1 << 20, None) == -1

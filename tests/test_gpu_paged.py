@@ -120,7 +120,9 @@ def test_paged_full_size_dsv32():
     """The DeepSeek-V3.2-like shape (B=32, H=4096, K=2048, 32,768-token contexts,
     pinned-host pool) with vLLM-style addressing: 64-row source blocks (a seeded
     permutation, block 0 unused) and 64-slot hot blocks; the cold step and three
-    steady steps against the oracle, with attention indices."""
+    steady steps against the oracle, with attention indices. A resident table
+    of 64-row blocks (the hot block size) with null block 0 serves about 5% of
+    each request's blocks from the device cache."""
     import sparse_attention_kv_hisparse_amd as hs
     cfg = gen.DSV32
     block = 64
@@ -132,6 +134,9 @@ def test_paged_full_size_dsv32():
     pool_nrows = (B * nsb + 1) * block
     nhb = H // block
     hot_tab = rng.permutation(R * nhb).astype(np.int32).reshape(R, nhb)
+    res_tab = np.zeros((R, nsb), np.int32)                   # null block 0 everywhere ...
+    live = rng.random((R, nsb)) < 0.05
+    res_tab[live] = rng.integers(1, 1 << 14, int(live.sum()))  # ... but ~5% resident
     print(f"  paged full size: pool {pool_nrows} rows", flush=True)
     pool = wdev.make_pool(cfg.with_(B=1, ctx=pool_nrows))
     keys = torch.full((R, H + 1), -1, dtype=torch.int32, device="cuda")
@@ -143,6 +148,8 @@ def test_paged_full_size_dsv32():
     ws = torch.empty(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
     paged_dev = {"hot_block_table": torch.as_tensor(hot_tab).cuda(), "hot_block_size": block,
                  "src_block_table": torch.as_tensor(src).cuda(), "src_block_size": block,
+                 "resident_block_table": torch.as_tensor(res_tab).cuda(),
+                 "resident_block_size": block, "resident_null_block": 0,
                  "attention_indices": att, "attention_block_stride": 128}
     o_keys = np.full((R, H + 1), -1, np.int32)
     o_lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
@@ -158,8 +165,9 @@ def test_paged_full_size_dsv32():
             topk=topk, req_rows=rows, seq_lens=None, slot_tokens=o_keys, lru=o_lru,
             pool=pool.numpy(), hot=o_hot, ctx_stride=0,
             paged={"hot_block_table": hot_tab, "hot_block_size": block, "src_block_table": src,
-                   "src_block_size": block, "attention_indices": o_att,
-                   "attention_block_stride": 128})
+                   "src_block_size": block, "resident_block_table": res_tab,
+                   "resident_block_size": block, "resident_null_block": 0,
+                   "attention_indices": o_att, "attention_block_stride": 128})
         torch.cuda.synchronize()
         print(f"  paged full size step {t}: {int(o_cnt.sum())} misses", flush=True)
         assert np.array_equal(_np(out), o_out), f"step {t}: out_rows"

@@ -31,21 +31,21 @@ def _harness():
 
 def test_tiny_trace_with_invariants():
     h = _harness()
-    counts = h.run_trace(gen.TINY, full_hot_steps=range(gen.TINY.steps), check_invariants=True)
+    counts = h.run_trace(gen.TINY, check_invariants=True)
     assert (counts[0] == gen.TINY.K).all()
 
 
 def test_dsv32_like_host_pool_full():
     h = _harness()
     cfg = gen.DSV32
-    counts = h.run_trace(cfg, full_hot_steps=(0, cfg.steps // 2))
+    counts = h.run_trace(cfg)
     assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
 
 def test_device_pool_full():
     h = _harness()
     cfg = gen.DEVPOOL
-    counts = h.run_trace(cfg, full_hot_steps=(0, cfg.steps // 2))
+    counts = h.run_trace(cfg)
     # cold step: every id misses except the newest token when a row drew it
     assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
@@ -53,7 +53,7 @@ def test_device_pool_full():
 @pytest.mark.parametrize("cfg", [gen.ADVERSARIAL, gen.ADVERSARIAL_132], ids=["1152B", "132B"])
 def test_adversarial_full(cfg):
     h = _harness()
-    counts = h.run_trace(cfg, full_hot_steps=(0,))
+    counts = h.run_trace(cfg)
     assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
 
@@ -85,7 +85,7 @@ def _small(**kw):
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
-    h.run_trace(cfg, full_hot_steps=range(cfg.steps), check_invariants=cfg.K * cfg.B <= 4096)
+    h.run_trace(cfg, check_invariants=cfg.K * cfg.B <= 4096)
 
 
 def test_padding_permuted_rows_tables_invalid_ids():
@@ -108,18 +108,48 @@ def test_padding_permuted_rows_tables_invalid_ids():
                                           n_invalid=int(rng.integers(0, 3)))
         run.req_rows = rows
         num_real = int(rng.integers(1, 5)) if t % 3 == 2 else -1
-        run.step(topk, seq, num_real=num_real, full_hot=True, check_invariants=True)
+        run.step(topk, seq, num_real=num_real, check_invariants=True)
 
 
 def test_state_row_out_of_range_is_padding():
+    """State rows 5 and -1 with R = 3: padding. The pool and the hot buffer are
+    sized for six state rows, so row 5's ids would have pool rows and hot rows
+    in range: only the state-row bound makes them padding."""
     h = _harness()
     cfg = _small(B=3)
-    run = h.ParityRun(cfg, R=3, req_rows=np.asarray([0, 5, -1], dtype=np.int64))
+    run = h.ParityRun(cfg, R=3, req_rows=np.asarray([0, 5, -1], dtype=np.int64),
+                      pool_nrows=6 * cfg.ctx, hot_nrows=6 * cfg.S_r)
     rng = np.random.default_rng(3)
     for _ in range(3):
         _, seq, topk = gen.random_case(rng, B=3, R=3, H=cfg.H, K=cfg.K, ctx=cfg.ctx)
-        out, cnt = run.step(topk, seq, full_hot=True)
+        out, cnt = run.step(topk, seq)
         assert (out[1:] == -1).all() and (cnt[1:] == 0).all()
+
+
+def test_negative_pool_row_entries_are_invalid():
+    """A pool-row table with negative entries: those ids output -1, are not
+    copied and are not counted (the pool has spare rows, so a kernel that let
+    a negative row through would copy real bytes and differ)."""
+    h = _harness()
+    rng = np.random.default_rng(21)
+    cfg = _small(B=3, H=40, K=12, ctx=120, row_bytes=48)
+    R = 3
+    pool_rows = rng.permutation(R * cfg.ctx).astype(np.int64).reshape(R, cfg.ctx)
+    neg = rng.random(pool_rows.shape) < 0.2
+    pool_rows[neg] = -rng.integers(1, 4, int(neg.sum()))
+    run = h.ParityRun(cfg, R=R, pool_rows=pool_rows)
+    seen_neg = 0
+    for t in range(8):
+        rows, seq, topk = gen.random_case(rng, B=3, R=R, H=cfg.H, K=cfg.K, ctx=cfg.ctx)
+        run.req_rows = rows
+        out, _ = run.step(topk, seq, check_invariants=True)
+        for b in range(3):
+            for i in range(cfg.K):
+                t_id = int(topk[b, i])
+                if 0 <= t_id < seq[b] and pool_rows[rows[b], t_id] < 0:
+                    assert out[b, i] == -1
+                    seen_neg += 1
+    assert seen_neg > 0
 
 
 def test_strided_topk_rows():
@@ -127,7 +157,7 @@ def test_strided_topk_rows():
     cfg = _small(B=5, H=70, K=33, ctx=400)
     run = h.ParityRun(cfg)
     for t, topk in enumerate(gen.topk_trace(cfg, 4)):
-        run.step(topk, gen.seq_lens(cfg, t), full_hot=True, topk_pad=11)
+        run.step(topk, gen.seq_lens(cfg, t), topk_pad=11)
 
 
 def test_misaligned_hot_uses_4byte_path():
@@ -135,7 +165,7 @@ def test_misaligned_hot_uses_4byte_path():
     cfg = _small(row_bytes=64)
     run = h.ParityRun(cfg, hot_misalign=True)
     for t, topk in enumerate(gen.topk_trace(cfg, 4)):
-        run.step(topk, gen.seq_lens(cfg, t), full_hot=True)
+        run.step(topk, gen.seq_lens(cfg, t))
 
 
 def test_clusters_under_the_kernel_hash():
@@ -162,7 +192,7 @@ def test_clusters_under_the_kernel_hash():
                 fresh = np.setdiff1d(cand, prev[b])
                 topk[b, K // 2:] = rng.choice(fresh, size=K - K // 2, replace=False)
         prev = topk.copy()
-        run.step(topk, seq, full_hot=True)
+        run.step(topk, seq)
 
 
 def test_empty_calls_are_noops():

@@ -133,6 +133,28 @@ def test_state_row_out_of_range_is_padding():
     assert out[1].tolist() == [-1, -1] and cnt[1] == 0 and cnt[0] == 2
 
 
+def test_state_row_past_R_is_padding_with_otherwise_valid_ids():
+    """req_rows names state row R (one past the last). The pool and the hot
+    buffer have rows for it and the state arrays are views of arrays with a
+    spare row, so its ids would be valid and its slots addressable: only the
+    state-row bound makes the row padding. The spare row and the hot rows
+    past R*S_r stay untouched."""
+    R, H, K, ctx, rb = 2, 4, 2, 10, 4
+    S_r = H + 1
+    st_big, lru_big = gen.initial_state(R + 1, H, S_r)
+    pool = np.arange((R + 1) * ctx * rb, dtype=np.uint32).astype(np.uint8).reshape((R + 1) * ctx, rb)
+    hot = np.zeros(((R + 1) * S_r, rb), dtype=np.uint8)
+    out, cnt = oracle.swap_in(topk=np.asarray([[1, 2], [3, 4]], dtype=np.int32),
+                              req_rows=np.asarray([0, R], dtype=np.int64),
+                              seq_lens=np.asarray([10, 10], dtype=np.int64),
+                              slot_tokens=st_big[:R], lru=lru_big[:R], pool=pool, hot=hot,
+                              ctx_stride=ctx)
+    assert out[1].tolist() == [-1, -1] and cnt.tolist() == [2, 0]
+    assert out[0].tolist() == [0, 1]
+    assert st_big[R].tolist() == [-1] * S_r and lru_big[R].tolist() == list(range(H))
+    assert not hot[R * S_r:].any()
+
+
 def test_ids_past_ctx_stride_or_pool_are_invalid():
     kw = _base()
     kw["seq_lens"] = np.asarray([30, 10], dtype=np.int64)

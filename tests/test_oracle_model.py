@@ -56,7 +56,11 @@ def _expected_stats(c, st, *, R, H, ctx_stride, pool_rows, pool_nrows):
 
 def _run_both(calls, *, R, H, S_r, ctx_stride, rb=8, slot_rows=None, pool_rows=None,
               hot_nrows=None, pool_nrows=None, kv=False):
-    pool = _pool(pool_nrows or R * ctx_stride, rb)
+    # The pool is a view past four spare rows, so a negative pool row that
+    # were let through would read bytes (and differ from the model) instead
+    # of leaving the array.
+    n = pool_nrows or R * ctx_stride
+    pool = _pool(n + 4, rb)[4:]
     hot_nrows = hot_nrows or R * S_r
     st_o, lru_o = gen.initial_state(R, H, S_r)
     st_m, lru_m = st_o.copy(), lru_o.copy()
@@ -134,12 +138,15 @@ def test_exhaustive_k3_h4_growing_seq():
 @pytest.mark.parametrize("seed", range(6))
 def test_random_multirow_with_tables(seed, kv=False):
     """Random calls over permuted state rows, padding, invalid ids, slot-row and
-    pool-row tables."""
+    pool-row tables. About a tenth of the pool-row entries are negative (-1 to
+    -3): those ids have no pool row and are invalid."""
     rng = np.random.default_rng(seed)
     R, B, H, K, ctx = 5, 3, 12, 6, 40
     S_r = H + 2
     slot_rows = rng.permutation(R * S_r + 7)[:R * S_r].astype(np.int32).reshape(R, S_r)
     pool_rows = rng.permutation(R * ctx + 9)[:R * ctx].astype(np.int64).reshape(R, ctx)
+    neg = rng.random(pool_rows.shape) < 0.1
+    pool_rows[neg] = -rng.integers(1, 4, int(neg.sum()))
     calls = []
     for _ in range(12):
         rows, seq, topk = gen.random_case(rng, B=B, R=R, H=H, K=K, ctx=ctx, n_invalid=int(rng.integers(0, 3)))

@@ -62,6 +62,11 @@ MUTANTS = {
                                "                               o % p->attention_block_stride);"),
     "stats_hits_are_evictables": ("a->stats[0] += (uint64_t)nh;", "a->stats[0] += (uint64_t)ne;"),
     "stats_misses_not_added": ("a->stats[1] += (uint64_t)M;", ""),
+    "paged_resident_null_block_ignored": ("if (pb != p->resident_null_block && pb >= 0)",
+                                          "if (pb >= 0)"),
+    "negative_pool_row_accepted": ("if (pr < 0 || pr >= a->pool_nrows) { out[i] = -1; continue; }",
+                                   "if (pr >= a->pool_nrows) { out[i] = -1; continue; }"),
+    "state_row_past_R_processed": ("if (b >= nreal || r < 0 || r >= a->R) {", "if (b >= nreal || r < 0) {"),
     "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
                                       "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }
@@ -75,6 +80,7 @@ def _pins():
     import test_oracle_plan as pl
     import test_oracle_kv as kvt
     import test_oracle_paged as pgt
+    import test_oracle_copies_and_errors as ce
     failed = []
     checks = [
         ("golden1", lambda: g.test_swap_in_worked_examples("swap_in_worked_example_1.json")),
@@ -90,6 +96,7 @@ def _pins():
         ("kv_model", lambda: m.test_random_multirow_kv(0)),
         ("paged_golden", pgt.test_paged_worked_example),
         ("paged_model", lambda: pgt.test_paged_matches_model(0)),
+        ("state_row_past_R", ce.test_state_row_past_R_is_padding_with_otherwise_valid_ids),
     ]
     for name, fn in checks:
         try:

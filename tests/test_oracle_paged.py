@@ -79,14 +79,22 @@ def _random_tables(rng, R, H, ctx, hb=None):
     nulls = rng.random((R, nsb)) < 0.1
     phys[nulls] = rng.choice([0, -1], size=int(nulls.sum()))
     pool_nrows = (R * nsb + 4) * sb - sb // 2           # the last block is cut: some ids have no row
-    rbs = 8
+    # Resident table inside the vLLM page's domain (its host checks): block
+    # size equal to the hot block size and a non-negative null block. Most
+    # blocks hold the null block, some a negative block, some a real one;
+    # the null block is drawn so that it is often 0 and sometimes a block id
+    # that real entries could also hold.
+    rbs = hb
     nrb = -(-ctx // rbs)
-    res = np.full((R, nrb), -1, np.int32)
+    null = int(rng.choice([0, 0, 3, 17]))
+    res = np.full((R, nrb), null, np.int32)
+    neg = rng.random((R, nrb)) < 0.1
+    res[neg] = -1
     hit = rng.random((R, nrb)) < 0.15
     res[hit] = rng.integers(0, 50, int(hit.sum()))
     paged = {"hot_block_table": hot_blocks, "hot_block_size": hb, "src_block_table": phys,
              "src_block_size": sb, "resident_block_table": res, "resident_block_size": rbs,
-             "resident_null_block": -1}
+             "resident_null_block": null}
     return paged, hot_nrows, pool_nrows
 
 
@@ -169,6 +177,34 @@ def test_paged_reduces_to_position_keying(seed):
                                np.take_along_axis(pool_rows, np.maximum(st_q[:, :H], 0).astype(np.int64), 1),
                                -1)
         assert st_p[:, :H].tolist() == keys_from_q.tolist()
+
+
+@pytest.mark.parametrize("change", ["no_source_table", "block_sizes_differ", "negative_null"])
+def test_paged_rejects_resident_tables_the_page_rejects(change):
+    """vLLM hisparse_kernels.cu, host checks of hisparse_resolve_residency: a
+    resident lookup needs the source block table, the resident and hot block
+    sizes must match, and the resident null block must be non-negative."""
+    R, H, K, ctx, rb = 2, 4, 2, 16, 4
+    hb = 2
+    paged = {"hot_block_table": np.array([[0, 1], [2, 3]], np.int32), "hot_block_size": hb,
+             "src_block_table": np.array([[1, 2, 3, 4], [5, 6, 7, 8]], np.int32),
+             "src_block_size": 4,
+             "resident_block_table": np.zeros((2, ctx // hb), np.int32),
+             "resident_block_size": hb, "resident_null_block": 0}
+    st, lru = gen.initial_state(R, H, H + 1)
+    kw = dict(topk=np.array([[1, 2], [3, 4]], np.int32), req_rows=np.arange(2, dtype=np.int64),
+              seq_lens=None, slot_tokens=st, lru=lru, pool=np.zeros((40, rb), np.uint8),
+              hot=np.zeros((8, rb), np.uint8), ctx_stride=0)
+    oracle.swap_in(**kw, paged=paged)              # inside the page's domain: accepted
+    if change == "no_source_table":
+        paged = {k: v for k, v in paged.items() if not k.startswith("src")}
+    elif change == "block_sizes_differ":
+        paged = dict(paged, resident_block_size=4, resident_block_table=np.zeros((2, 4), np.int32))
+    else:
+        paged = dict(paged, resident_null_block=-1)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.swap_in(**kw, paged=paged)
+    assert e.value.code == -1
 
 
 def test_invalidate_matches_numpy():
