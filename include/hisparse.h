@@ -214,6 +214,30 @@ int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t worksp
                      hipStream_t stream);
 
 /*
+ * hisparse_swap_in_noalloc -- hisparse_swap_in without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Computes exactly what hisparse_swap_in computes (same arguments, same
+ * kernels, same results). The miss list that hisparse_swap_in keeps in the
+ * caller's workspace lives instead in a fixed device array of
+ * HS_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends; the call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine). The array needs no initialisation.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (different streams with no ordering between them) race and give
+ * unspecified results; order them on one stream. The list is not published
+ * for hisparse_gather_compact_layers (use hisparse_resolve with a workspace).
+ *
+ * Returns HS_ERANGE, with nothing enqueued, when the list of B rows of K ids
+ * (hs_swap_in_workspace_bytes(B, K)) exceeds HS_NOALLOC_SCRATCH_BYTES: 4 MiB
+ * holds B * K up to about 349,000 (B = 128 at K = 2048). Every other status as
+ * for hisparse_swap_in (never HS_EWORKSPACE).
+ */
+#define HS_NOALLOC_SCRATCH_BYTES (4u << 20)
+int hisparse_swap_in_noalloc(const hs_swap_in_args* args, hipStream_t stream);
+
+/*
  * hisparse_resolve / hisparse_gather_compact -- the two halves of
  * hisparse_swap_in, for callers that want to run the row copy later, on
  * another stream, or once per layer group.

@@ -18,7 +18,7 @@ import torch
 
 from ._lib import EXPORTS, HisparseError, PagedAddressing, SwapInArgs, check, load
 
-__all__ = ["hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
+__all__ = ["hisparse_swap_in", "hisparse_swap_in_noalloc", "hisparse_resolve", "hisparse_gather_compact",
            "hisparse_gather_compact_layers", "transfer_kv_all_layer", "store_kv_cache",
            "hisparse_invalidate_written",
            "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
@@ -72,7 +72,7 @@ def swap_in_workspace_layout(B: int, K: int) -> dict:
 def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: torch.Tensor,
                      slot_tokens: torch.Tensor, lru: torch.Tensor, pool: torch.Tensor,
                      hot: torch.Tensor, out_rows: torch.Tensor, ctx_stride: int,
-                     workspace: torch.Tensor, miss_counts: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor], miss_counts: Optional[torch.Tensor] = None,
                      num_real: Optional[torch.Tensor] = None,
                      slot_rows: Optional[torch.Tensor] = None,
                      pool_rows: Optional[torch.Tensor] = None,
@@ -187,8 +187,21 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
         if stats.dtype not in (torch.int64, torch.uint64) or stats.numel() != 2 or not stats.is_contiguous():
             raise ValueError("stats must be a contiguous 2-element int64 or uint64 tensor")
         a.stats = _dev(stats, stats.dtype, "stats")
+    if _entry == "hisparse_swap_in_noalloc":
+        check(_entry, load().hisparse_swap_in_noalloc(ctypes.byref(a), _stream(stream)))
+        return
     ws = _dev(workspace, torch.uint8, "workspace")
     check(_entry, getattr(load(), _entry)(ctypes.byref(a), ws, workspace.numel(), _stream(stream)))
+
+
+def hisparse_swap_in_noalloc(**kw) -> None:
+    """``hisparse_swap_in_noalloc``: the swap-in without a workspace argument (for
+    callers that cannot allocate); same arguments as ``hisparse_swap_in`` minus
+    ``workspace``. The miss list lives in the library's fixed per-device array
+    of ``HS_NOALLOC_SCRATCH_BYTES``; calls that overlap on one device race."""
+    if "workspace" in kw:
+        raise ValueError("hisparse_swap_in_noalloc takes no workspace")
+    hisparse_swap_in(_entry="hisparse_swap_in_noalloc", workspace=None, **kw)
 
 
 def hisparse_resolve(**kw) -> None:

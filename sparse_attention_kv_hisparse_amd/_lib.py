@@ -13,11 +13,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libhisparse.so")
 
 HS_OK = 0
+HS_NOALLOC_SCRATCH_BYTES = 4 << 20   # include/hisparse.h
 STATUS = {0: "HS_OK", -1: "HS_EINVAL", -2: "HS_ERANGE", -3: "HS_EMEMKIND", -4: "HS_ELAUNCH",
           -5: "HS_EWORKSPACE"}
 
 # Every function include/hisparse.h declares.
-EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_resolve",
+EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_swap_in_noalloc",
+           "hisparse_resolve",
            "hisparse_gather_compact", "hisparse_gather_compact_layers",
            "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_kv_all_layer",
            "store_kv_scatter", "store_kv_cache", "hisparse_invalidate_written",
@@ -86,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact"):
         getattr(lib, name).argtypes = [ctypes.POINTER(SwapInArgs), vp, sz, vp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.hisparse_swap_in_noalloc.argtypes = [ctypes.POINTER(SwapInArgs), vp]
+    lib.hisparse_swap_in_noalloc.restype = ctypes.c_int
     lib.hisparse_gather_compact_layers.argtypes = [vp, sz, i32, i32, vp, i64, vp, i64, i32, i64, vp]
     lib.hisparse_gather_compact_layers.restype = ctypes.c_int
     szp = ctypes.POINTER(ctypes.c_size_t)

@@ -913,7 +913,22 @@ struct Plan {
   int num_cus;
 };
 
-int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, Plan* pl) {
+// Point the plan's miss list (count, pool rows, hot rows) into a workspace of
+// at least ws_layout(B, K).total bytes, 256-byte aligned.
+void bind_workspace(Plan* pl, void* workspace) {
+  const WsLayout wl = ws_layout(pl->s.B, pl->s.K);
+  char* ws = static_cast<char*>(workspace);
+  pl->s.count = reinterpret_cast<int32_t*>(ws + wl.count);
+  pl->s.src = reinterpret_cast<int64_t*>(ws + wl.src);
+  pl->s.dst = reinterpret_cast<int32_t*>(ws + wl.dst);
+}
+
+// Validates the call and fills the plan; the workspace must hold the list.
+// With bind_later (the allocation-free entry point only) the workspace
+// arguments are ignored and the caller binds its own array afterwards
+// (bind_workspace), having checked its size itself.
+int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, Plan* pl,
+            bool bind_later = false) {
   if (!a) return set_error(HS_EINVAL, "args is NULL");
   if (a->B < 0 || a->K < 0) return set_error(HS_EINVAL, "B and K must be >= 0");
   if (a->B == 0 || a->K == 0) return kEmptyCall;
@@ -983,7 +998,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   if (static_cast<int64_t>(a->K) * (kv ? 2 : 1) * C >= (1ll << 31))
     return set_error(HS_ERANGE, "top_k * streams * chunks per row exceeds 2^31");
   const WsLayout wl = ws_layout(a->B, a->K);
-  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256))
+  if (!bind_later && (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)))
     return set_error(HS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned", wl.total);
 
   DeviceInfo di;
@@ -1066,7 +1081,6 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     }
   }
 
-  char* ws = static_cast<char*>(workspace);
   SwapArgs& s = pl->s;
   s.topk = a->topk_ids;
   s.topk_stride = a->topk_stride;
@@ -1112,9 +1126,6 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.miss_counts = a->miss_counts;
   s.miss_mask = a->miss_mask;
   s.stats = reinterpret_cast<unsigned long long*>(a->stats);
-  s.count = reinterpret_cast<int32_t*>(ws + wl.count);
-  s.src = reinterpret_cast<int64_t*>(ws + wl.src);
-  s.dst = reinterpret_cast<int32_t*>(ws + wl.dst);
   s.B = a->B;
   s.K = a->K;
   s.H = a->H;
@@ -1129,6 +1140,14 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.sbs_div = make_fastdiv(static_cast<uint32_t>(s.sbs));
   s.rbs_div = make_fastdiv(static_cast<uint32_t>(s.rbs));
   s.cdiv = make_fastdiv(static_cast<uint32_t>(C));
+
+  if (bind_later) {
+    s.count = nullptr;
+    s.src = nullptr;
+    s.dst = nullptr;
+  } else {
+    bind_workspace(pl, workspace);
+  }
 
   pl->resolve_fn = resolve_fn;
   pl->fused_fn = fused_fn;
@@ -1257,4 +1276,71 @@ extern "C" int hisparse_gather_compact_layers(const void* workspace, size_t work
   l.cdiv = make_fastdiv(static_cast<uint32_t>(C));
   l.ldiv = make_fastdiv(static_cast<uint32_t>(num_layers));
   return launch_swap_copy(l, W, di.num_cus, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free swap-in, for callers that cannot allocate device memory
+// (code under HIP graph capture, tight serving loops, harnesses that forbid
+// it): the miss list that hisparse_swap_in keeps in the caller's workspace
+// lives in `scratch`, a fixed array that each device holds for the life of
+// the process. Every call on a device shares that device's array, so calls
+// that overlap on one device (different streams, no ordering) race on it.
+// Nothing in it has to start at zero: the resolve kernel writes each row's
+// count and list entries before the copy reads them.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[HS_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current. In host code the array's name is only a stand-in for
+// the symbol: passing it to a kernel would fault, so only this address is used.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  static bool have[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return set_error(HS_ELAUNCH, "hipGetDevice failed");
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return set_error(HS_ELAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                       hipGetErrorString(e));
+    }
+    addr[dev] = p;
+    have[dev] = true;
+  }
+  *out = addr[dev];
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" int hisparse_swap_in_noalloc(const hs_swap_in_args* a, hipStream_t stream) {
+  if (!a) return set_error(HS_EINVAL, "args is NULL");
+  if (a->B > 0 && a->K > 0) {
+    const size_t need = ws_layout(a->B, a->K).total;
+    if (need > HS_NOALLOC_SCRATCH_BYTES)
+      return set_error(HS_ERANGE,
+                       "B=%d, K=%d need a %zu-byte miss list; the allocation-free swap-in holds "
+                       "%zu bytes (use hisparse_swap_in with a workspace)",
+                       a->B, a->K, need, static_cast<size_t>(HS_NOALLOC_SCRATCH_BYTES));
+  }
+  Plan pl;
+  int rc = prepare(a, nullptr, 0, &pl, /*bind_later=*/true);
+  if (rc != HS_OK) return rc == kEmptyCall ? HS_OK : rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != HS_OK) return rc;
+  bind_workspace(&pl, ws);
+  if (pl.fused_fn) return launch_resolve(pl, pl.fused_fn, stream);
+  rc = launch_resolve(pl, pl.resolve_fn, stream);
+  if (rc != HS_OK) return rc;
+  return launch_copy(pl, stream);
 }

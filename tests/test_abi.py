@@ -255,3 +255,18 @@ def test_invalidate_rejects(lib):
     assert g(f, 4, 9, f, f, -1, None) == -1
     assert g(None, 4, 9, f, f, 3, None) == -1
     assert g(f, 4, 9, None, f, 3, None) == -1
+
+
+def test_noalloc_rejects_before_touching_the_gpu(lib):
+    """hisparse_swap_in_noalloc: empty calls are no-ops, NULL args and miss
+    lists beyond the fixed array (HS_NOALLOC_SCRATCH_BYTES) are rejected on the
+    host, before any HIP call."""
+    from sparse_attention_kv_hisparse_amd._lib import HS_NOALLOC_SCRATCH_BYTES
+    f = lib.hisparse_swap_in_noalloc
+    assert f(None, None) == -1
+    assert f(ctypes.byref(_args(B=0)), None) == 0
+    assert f(ctypes.byref(_args(K=0)), None) == 0
+    assert lib.hs_swap_in_workspace_bytes(256, 2048) > HS_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(_args(B=256, K=2048, H=2048, topk_stride=2048)), None) == -2
+    assert b"allocation-free" in lib.hisparse_last_error()
+    assert lib.hs_swap_in_workspace_bytes(128, 2048) <= HS_NOALLOC_SCRATCH_BYTES
