@@ -9,11 +9,19 @@ timed; inputs for every step are resident in HBM before timing starts.
 
 Also reported in the same JSON line:
   * cold_step: the first (all-miss) call of the headline trace, timed alone;
+  * roofline: the fused kernel's mean launch time from the timed calls
+    replayed back to back behind a spin kernel (events on the launch stream);
   * device_pool: the same call on the device-pool workload (B=128, 16,384-token
-    contexts, pool of 2,097,152 rows in HBM, 60% retention) against 8 TB/s;
+    contexts, pool of 2,097,152 rows in HBM, 60% retention) against 8 TB/s,
+    beside what this part's HBM gives a plain 1 GiB copy (hipMemcpy and the
+    library's copy engine), and the steady state timed step by step from a
+    restored state after a 512 MiB flush;
   * adversarial: B=64, hot_size 8192, 65,536-token contexts, ids that collide
-    in the low-bit multiplicative hash, 1152-byte and 132-byte rows: the cold
-    step and the steps after it;
+    in the pages' low-bit multiplicative hash (1152-byte and 132-byte rows) and
+    ids that collide in the kernel's own high-bit buckets (1152-byte rows):
+    the cold step and the steps after it;
+  * tiny: B=2, hot_size 64, top_k 16 -- GPU time and caller-visible latency
+    per call;
   * kv_decode: non-MLA caches -- the headline's shape with 1024-byte K and V
     rows in two pinned pools, every miss moving both;
   * paged: vLLM-style paged addressing (64-row source and hot blocks, global
@@ -26,7 +34,8 @@ Also reported in the same JSON line:
   * all_layer: the fused all-layer transfer (61 layers x 262,144 rows x 656 B,
     8192 pairs) in both directions against the host-link ceiling;
   * host_link: the measured host-link ceiling the host-pool rooflines use;
-  * cpu_baseline: the CPU oracle (single thread) on the headline steps.
+  * cpu_baseline: the CPU oracle (single thread, and on every host core the
+    process may use) on the headline steps, with the host CPU's model name.
 """
 
 from __future__ import annotations
@@ -65,6 +74,7 @@ def parse():
     p.add_argument("--no-kv", action="store_true")
     p.add_argument("--no-paged", action="store_true")
     p.add_argument("--no-scatter", action="store_true")
+    p.add_argument("--no-tiny", action="store_true")
     p.add_argument("--replay-layers", type=int, default=4,
                    help="layers per index-sharing group in the plan-replay leg (1 resolving "
                         "layer + the rest replaying its plan)")
@@ -95,7 +105,7 @@ class Trace:
         self.rows = torch.arange(cfg.B, dtype=torch.int64, device="cuda")
 
 
-def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False):
+def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False, b2b_pass=False):
     """Time K swap-in calls after W warm-up calls.
 
     Pass 1 (the timed region of the contract): W untimed calls, then K plain
@@ -113,7 +123,11 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False):
     events bracket the kernels alone (for traces of a few calls, where the
     host time ahead of the first launch is not amortised); the wall clock then
     includes the spin and is not meaningful.
-    Returns dict(us_total, us_resolve, us_copy, us_cold, cold_rows, counts, wall).
+    With b2b_pass=True a third pass replays the K timed calls from the same
+    starting state queued behind a spin kernel, so the events bracket the K
+    launches back to back with no host time between them: us_b2b / K is the
+    mean launch time of the call's kernel (one fused kernel on a host pool).
+    Returns dict(us_total, us_resolve, us_copy, us_cold, cold_rows, counts, wall, us_b2b).
     """
     log(f"[bench] {cfg.name}: building pool ({cfg.pool_nrows} x {cfg.row_bytes} B, {cfg.pool_kind})"
         + (" x 2 (K and V)" if kv else ""))
@@ -196,10 +210,155 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False):
     us_resolve = r0.elapsed_time(r1) * 1000.0
     us_copy = g0.elapsed_time(g1) * 1000.0
     assert (counts.cpu().numpy()[warmup:] == c).all(), "replay diverged from the timed pass"
+    us_b2b = None
+    if b2b_pass:
+        # pass 3: the timed calls again, queued behind a spin kernel
+        hs.hisparse_state_reset(slot_tokens=st.slot_tokens, lru=st.lru,
+                                rows=torch.arange(st.R, dtype=torch.int64, device="cuda"))
+        for t in range(warmup):
+            call(t, hs.hisparse_swap_in, st.ws)
+        torch.cuda.synchronize()
+        b0, b1 = events()
+        torch.cuda._sleep(24_000_000)
+        b0.record(stream)
+        for k in range(steps):
+            call(warmup + k, hs.hisparse_swap_in, st.ws)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        us_b2b = b0.elapsed_time(b1) * 1000.0
+        assert (counts.cpu().numpy()[warmup:] == c).all(), "back-to-back pass diverged"
     del pool, st, tr, wss
     torch.cuda.empty_cache()
     return dict(us_total=us_total, us_resolve=us_resolve, us_copy=us_copy, us_cold=us_cold,
-                cold_rows=cold_rows, counts=c, wall=wall)
+                cold_rows=cold_rows, counts=c, wall=wall, us_b2b=us_b2b)
+
+
+def run_flushed(cfg, steps, replays, torch, hs, wdev):
+    """The step-by-step protocol: after the cold step, each of `steps` steps
+    is replayed `replays` + 1 times from a snapshot of the state taken before
+    it; before every replay the state is restored and 512 MiB are written to a
+    scratch buffer (evicting L2 and the MALL), both untimed, and a short spin
+    kernel hides the host time of the call. Replays of a step move the same
+    rows to the same slots. Returns the median over steps of each step's
+    median replay time (µs), and the rows per step."""
+    log(f"[bench] {cfg.name}: per-step replays with state restore and a 512 MiB flush")
+    pool = wdev.make_pool(cfg)
+    st = wdev.DeviceSwapState(cfg)
+    tr = Trace(cfg, 1 + steps, torch)
+    counts = torch.empty((1 + steps, cfg.B), dtype=torch.int32, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(t):
+        hs.hisparse_swap_in(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t],
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+                            miss_counts=counts[t], stream=stream)
+
+    call(0)
+    per_step = []
+    for t in range(1, 1 + steps):
+        snap = (st.slot_tokens.clone(), st.lru.clone())
+        us = []
+        for rep in range(replays + 1):
+            st.slot_tokens.copy_(snap[0])
+            st.lru.copy_(snap[1])
+            flush.fill_(rep)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(200_000)
+            e0.record(stream)
+            call(t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                us.append(e0.elapsed_time(e1) * 1000.0)
+        us.sort()
+        per_step.append(us[len(us) // 2])
+    rows = int(counts[1:].sum().item())
+    del pool, st, tr, flush
+    torch.cuda.empty_cache()
+    per_step.sort()
+    return per_step[len(per_step) // 2], rows / steps
+
+
+def run_tiny(torch, hs, wdev):
+    """The tiny workload (B=2, H=64, K=16, 656-byte rows, pinned-host pool):
+    the cold step, then 7 steps, each timed two ways -- the GPU time of the
+    call's kernel (the 7 calls queued behind a spin kernel, between two
+    events) and the latency a caller sees (host wall time of the call plus a
+    synchronize, median over the 7 steps)."""
+    from workloads import gen
+    cfg = gen.TINY
+    r = run_gpu(cfg, 1, cfg.steps - 1, torch, hs, wdev, lead_spin=True)
+    pool = wdev.make_pool(cfg)
+    st = wdev.DeviceSwapState(cfg)
+    tr = Trace(cfg, cfg.steps, torch)
+    lat = []
+    for t in range(cfg.steps):
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        hs.hisparse_swap_in(topk=tr.topk[t], req_rows=tr.rows, seq_lens=tr.seq[t],
+                            slot_tokens=st.slot_tokens, lru=st.lru, pool=pool, hot=st.hot,
+                            out_rows=st.out, ctx_stride=cfg.ctx, workspace=st.ws,
+                            miss_counts=st.counts)
+        torch.cuda.synchronize()
+        if t:
+            lat.append((time.perf_counter() - w0) * 1e6)
+    lat.sort()
+    n = cfg.steps - 1
+    return {"workload": "tiny_swap_in_pinned_host_pool", "batch": cfg.B, "hot_size": cfg.H,
+            "top_k": cfg.K, "context": cfg.ctx, "row_bytes": cfg.row_bytes, "steps_after_cold": n,
+            "rows_per_call": round(float(r["counts"].sum()) / n, 2),
+            "us_per_call_gpu": round(r["us_total"] / n, 2),
+            "us_per_call_sync": round(lat[len(lat) // 2], 2),
+            "cold_step_us_gpu": round(r["us_cold"], 2),
+            "bound": "latency (launch and one workgroup per request)"}
+
+
+def hbm_ceiling(torch, hs):
+    """What this part's HBM delivers to a plain copy: a 1 GiB device-to-device
+    hipMemcpyAsync, and the library's own 16-byte-per-lane copy engine
+    (transfer_rows_all_layer, HBM-sized launch) over the same 1 GiB as
+    contiguous 1 MiB rows. Best of 5 each; GB/s counts bytes read + written."""
+    n = 1 << 30
+    src = torch.full((n,), 3, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def best(fn, reps=5):
+        b = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            b = max(b, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        return b
+
+    res = {"memcpy_d2d_GBps": best(lambda: dst.copy_(src, non_blocking=True))}
+    rb = 1 << 20
+    idx = torch.arange(n // rb, dtype=torch.int64, device="cuda")
+    sp = torch.tensor([src.data_ptr()], dtype=torch.int64, device="cuda")
+    dp = torch.tensor([dst.data_ptr()], dtype=torch.int64, device="cuda")
+    res["library_copy_contiguous_GBps"] = best(lambda: hs.transfer_rows_all_layer(
+        src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=idx, dst_idx=idx, row_bytes=rb,
+        src_nrows=n // rb, dst_nrows=n // rb))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {k: round(v, 1) for k, v in res.items()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def run_plan_replay(cfg, layers, warmup, steps, torch, hs, wdev):
@@ -634,15 +793,16 @@ def main():
     if link:
         log(f"[bench] host link: {json.dumps({k: round(v, 2) for k, v in link.items()})}")
 
-    r = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev)
+    r = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev, b2b_pass=True)
     K = args.steps
     rows = int(r["counts"].sum())
     bytes_link = rows * cfg.row_bytes
     value = rows / r["wall"]
     # Host pools: each call is ONE launch of the resolve kernel with the
-    # request's copies fused in, so its average launch is the timed pass's
-    # per-call time. (Pass 2 still reports the split API's two kernels.)
-    us_kernel = r["us_total"]
+    # request's copies fused in. Its mean launch time comes from pass 3: the
+    # K launches queued back to back behind a spin kernel, between two events
+    # on the launch stream. (Pass 2 reports the split API's two kernels.)
+    us_kernel = r["us_b2b"]
     kernel = "resolve_kernel<false, false, 16, false> (resolution + the request's own row copies)"
     achieved = bytes_link / (us_kernel * 1e-6) / 1e9
     call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
@@ -674,7 +834,10 @@ def main():
                       "GBps": round(r["cold_rows"] * cfg.row_bytes / r["us_cold"] / 1e3, 2)},
         "effective_GBps_call": round(call_gbs, 2),
         "frac_host_link_call": round(call_gbs / peak, 4) if peak else None,
+        "us_per_launch_back_to_back": round(us_kernel / K, 2),
         "roofline": {"bound": "host_link", "kernel": kernel,
+                     "timing": "mean launch time, launches queued back to back behind a spin "
+                               "kernel, two events on the launch stream",
                      "achieved": round(achieved, 2), "peak": round(peak, 2) if peak else None,
                      "unit": "GB/s", "frac": round(achieved / peak, 4) if peak else None,
                      "peak_published": PCIE5_X16_GBS,
@@ -686,6 +849,9 @@ def main():
         dcfg = gen.DEVPOOL
         n = args.device_pool_steps
         d = run_gpu(dcfg, 1, n, torch, hs, wdev)
+        ceil = hbm_ceiling(torch, hs)
+        log(f"[bench] HBM ceiling: {json.dumps(ceil)}")
+        fl_us, fl_rows = run_flushed(dcfg, 8, 5, torch, hs, wdev)
         drows = int(d["counts"].sum())
         d_copy = d["us_copy"]
         # algorithmic HBM bytes of the copy kernel: each missed row read once and
@@ -707,7 +873,18 @@ def main():
                           "GBps_rows_read_written": round(
                               d["cold_rows"] * 2 * dcfg.row_bytes / d["us_cold"] / 1e3, 1)},
             "effective_GBps_call": round(dcall, 1), "frac_hbm_call": round(dcall / HBM_PEAK_GBS, 4),
+            "steady_state_protocol": {
+                "back_to_back_us_per_call": round(d["us_total"] / n, 2),
+                "restore_and_flush_us_per_call": round(fl_us, 2),
+                "restore_and_flush_rows_per_call": round(fl_rows, 1),
+                "note": "median over 8 steps of the median of 5 replays, each from a restored "
+                        "state after a 512 MiB write"},
+            "hbm_ceiling": dict(ceil, frac_of_peak_library_copy=round(
+                ceil["library_copy_contiguous_GBps"] / HBM_PEAK_GBS, 4)),
+            "frac_achievable_copy_kernel": round(dach / ceil["library_copy_contiguous_GBps"], 4),
             "roofline": {"bound": "hbm", "kernel": "swap_copy_kernel<16, false, 1024>", "achieved": round(dach, 1),
+                         "timing": "mean launch time, copy launches queued back to back behind a "
+                                   "spin kernel, two events on the launch stream",
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("device_pool")},
         }
@@ -782,7 +959,7 @@ def main():
         # cold step (all misses, ids that collide in the pages' low-bit hash),
         # then the remaining steps of the 4-step trace
         adv = {}
-        for acfg in (gen.ADVERSARIAL, gen.ADVERSARIAL_132):
+        for acfg in (gen.ADVERSARIAL, gen.ADVERSARIAL_132, gen.ADVERSARIAL_KERNEL_HASH):
             a = run_gpu(acfg, 1, acfg.steps - 1, torch, hs, wdev, lead_spin=True)
             n = acfg.steps - 1
             arows = int(a["counts"].sum())
@@ -790,6 +967,9 @@ def main():
             adv[acfg.name] = {
                 "batch": acfg.B, "hot_size": acfg.H, "top_k": acfg.K, "context": acfg.ctx,
                 "row_bytes": acfg.row_bytes,
+                "ids_collide_in": ("the kernel's own hash (top 11 bits of id * 2654435761)"
+                                   if acfg.collide_high_bits else
+                                   "the pages' hash (id * 2654435761 mod 2^32 mod 2*hot_size)"),
                 "cold_step": {"us": round(a["us_cold"], 2), "rows": a["cold_rows"],
                               "GBps": round(cold_gbs, 2),
                               "frac_host_link": round(cold_gbs / peak, 4) if peak else None},
@@ -829,11 +1009,14 @@ def main():
                                "frac_hbm": round(n * 4 * rb / sc["kv"] / 1e3 / HBM_PEAK_GBS, 4)},
         }
 
+    if not args.no_tiny:
+        out["tiny"] = run_tiny(torch, hs, wdev)
+
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on the headline steps")
         crow, csec, passes = cpu_baseline(cfg, args.warmup, args.steps, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(crow / csec, 1), "unit": "rows/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"the headline trace's {args.steps} timed steps "
                                          f"(B={cfg.B}, K={cfg.K}, H={cfg.H}) run {passes} times "
                                          f"from the same starting state, single thread, host "
@@ -845,6 +1028,7 @@ def main():
                                                max(3.0, args.cpu_seconds / 2), threads=nt)
             out["cpu_baseline_all_cores"] = {
                 "value": round(trow / tsec, 1), "unit": "rows/s", "cores": nt, "kind": "oracle",
+                "cpu_model": cpu_model(),
                 "sample": f"the same {args.steps} steps run {tpasses} times, each step's {cfg.B} "
                           f"requests split over {nt} threads (one oracle call per group); "
                           f"{trow} rows in {tsec:.2f} s of wall time"}

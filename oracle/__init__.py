@@ -46,15 +46,25 @@ class OracleError(RuntimeError):
         self.code = code
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain C11, -O2)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+_LIB_SANITIZED = os.path.join(_HERE, "liboracle_hisparse_sanitized.so")
+
+
+def build(force: bool = False, sanitize: bool = False, out: Optional[str] = None) -> str:
+    """Compile the oracle with gcc (plain C11, -O2). With ``sanitize`` the build
+    is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer (any
+    report aborts) into a separate library (``out``, or one beside the plain
+    build); a process loading it needs gcc's libasan and libubsan preloaded
+    (``tests/test_sanitizers.py`` does this)."""
+    lib = out or (_LIB_SANITIZED if sanitize else _LIB)
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < max(
             os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "hisparse_oracle.h"))):
-        tmp = _LIB + ".tmp"
+        tmp = lib + ".tmp"
+        extra = (["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"] if sanitize else [])
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared",
-                               "-o", tmp, _SRC])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               *extra, "-o", tmp, _SRC])
+        os.replace(tmp, lib)
+    return lib
 
 
 class _Paged(ctypes.Structure):

@@ -50,7 +50,8 @@ def test_device_pool_full():
     assert (counts[0] <= cfg.K).all() and (counts[0] >= cfg.K - 1).all()
 
 
-@pytest.mark.parametrize("cfg", [gen.ADVERSARIAL, gen.ADVERSARIAL_132], ids=["1152B", "132B"])
+@pytest.mark.parametrize("cfg", [gen.ADVERSARIAL, gen.ADVERSARIAL_132, gen.ADVERSARIAL_KERNEL_HASH],
+                         ids=["1152B", "132B", "kernel_hash_1152B"])
 def test_adversarial_full(cfg):
     h = _harness()
     counts = h.run_trace(cfg)

@@ -58,3 +58,9 @@ def test_adversarial_reduced(rb):
     cfg = gen.ADVERSARIAL.with_(B=2, row_bytes=rb)
     counts = _trace(cfg, 3, check_every=2)
     assert (counts[0] == cfg.K).all()
+
+
+def test_adversarial_kernel_hash_reduced():
+    cfg = gen.ADVERSARIAL_KERNEL_HASH.with_(B=2)
+    counts = _trace(cfg, 3, check_every=2)
+    assert (counts[0] == cfg.K).all()

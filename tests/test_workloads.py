@@ -58,6 +58,18 @@ def test_collide_ids_share_low_bit_buckets():
         assert len(span) <= cfg.collide_window
 
 
+def test_kernel_hash_ids_share_high_bit_buckets():
+    cfg = gen.ADVERSARIAL_KERNEL_HASH.with_(B=2)
+    tk = _check_trace(cfg, 2)
+    for b in range(cfg.B):
+        ids = tk[b].astype(np.uint64)
+        bucket = ((ids * np.uint64(gen.KNUTH_A)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - 11)
+        assert len(np.unique(bucket)) <= cfg.collide_window
+        # one window: every id's bucket within 128 of some start (wrapping)
+        starts = np.unique(bucket.astype(np.int64))
+        assert any(((bucket.astype(np.int64) - s0) % 2048 < 128).all() for s0 in starts)
+
+
 @pytest.mark.parametrize("cfg", [gen.DEVPOOL.with_(B=2), gen.DSV32.with_(B=2)])
 def test_retention(cfg):
     _check_trace(cfg, 3)

@@ -55,6 +55,10 @@ class SwapConfig:
     zipf_s: float = 1.1
     collide_window: int = 1024      # buckets per request window ("collide")
     collide_table: int = 0          # table size the ids collide in (2*H)
+    # "collide" with collide_high_bits > 0: buckets are the TOP collide_high_bits
+    # bits of the 32-bit product instead (collide_table = 2**collide_high_bits),
+    # the form the GPU kernel hashes with (its home bucket of an id)
+    collide_high_bits: int = 0
     newest_every_odd: bool = False  # request 0 picks L_t-1 at odd steps
 
     @property
@@ -103,11 +107,19 @@ ADVERSARIAL = SwapConfig("adversarial", B=64, H=8192, K=2048, ctx=65536,
                          row_bytes=1152, steps=4, rho=0.5, dist="collide",
                          pool_kind="host", seed=20260005, collide_table=16384)
 ADVERSARIAL_132 = ADVERSARIAL.with_(name="adversarial_132", row_bytes=132)
+# The adversarial shape with ids that collide in the GPU kernel's own hash: at
+# top_k 2048 the kernel's LDS table has 8192 entries in 2048 buckets of four,
+# and an id's home bucket is the top 11 bits of id * 2654435761 (mod 2^32). A
+# window of 128 of those buckets holds about 4096 ids of a 65,536-token
+# context, the same 1/16 share as the low-bit window above.
+ADVERSARIAL_KERNEL_HASH = ADVERSARIAL.with_(name="adversarial_kernel_hash", collide_high_bits=11,
+                                            collide_table=2048, collide_window=128)
 # Non-MLA caches (K and V rows per token): the DeepSeek-V3.2-like decode shape
 # with 1024-byte rows, as for 4 KV heads x 128 dims x 2 bytes.
 KV_DECODE = DSV32.with_(name="kv_decode", row_bytes=1024, seed=20260006)
 
-SWAP_CONFIGS = {c.name: c for c in (TINY, DSV32, DEVPOOL, ADVERSARIAL, ADVERSARIAL_132)}
+SWAP_CONFIGS = {c.name: c for c in (TINY, DSV32, DEVPOOL, ADVERSARIAL, ADVERSARIAL_132,
+                                    ADVERSARIAL_KERNEL_HASH)}
 
 
 # --------------------------------------------------------------------------
@@ -154,10 +166,16 @@ def _zipf_cdf(L: int, s: float) -> np.ndarray:
 
 
 def _collide_candidates(cfg: SwapConfig, L: int, window_start: int) -> np.ndarray:
-    """Ids in [0, L) whose low-bit multiplicative bucket mod ``collide_table`` falls
-    in ``[window_start, window_start + collide_window)`` (wrapping)."""
+    """Ids in [0, L) whose multiplicative bucket falls in
+    ``[window_start, window_start + collide_window)`` (wrapping): the low-bit
+    bucket ``(id*A mod 2^32) mod collide_table`` of the pages' hash, or with
+    ``collide_high_bits`` the top bits ``(id*A mod 2^32) >> (32 - collide_high_bits)``."""
     ids = np.arange(L, dtype=np.uint64)
-    bucket = ((ids * np.uint64(KNUTH_A)) & np.uint64(0xFFFFFFFF)) % np.uint64(cfg.collide_table)
+    prod = (ids * np.uint64(KNUTH_A)) & np.uint64(0xFFFFFFFF)
+    if cfg.collide_high_bits:
+        bucket = prod >> np.uint64(32 - cfg.collide_high_bits)
+    else:
+        bucket = prod % np.uint64(cfg.collide_table)
     rel = (bucket.astype(np.int64) - window_start) % cfg.collide_table
     return np.nonzero(rel < cfg.collide_window)[0].astype(np.int64)
 
