@@ -75,6 +75,10 @@ def parse():
     p.add_argument("--no-paged", action="store_true")
     p.add_argument("--no-scatter", action="store_true")
     p.add_argument("--no-tiny", action="store_true")
+    p.add_argument("--only", default="",
+                   help="comma-separated legs to run, the rest skipped (for profiling runs): "
+                        "headline, device_pool, plan_replay, kv, paged, adversarial, all_layer, "
+                        "scatter, tiny, cpu_baseline, host_link")
     p.add_argument("--replay-layers", type=int, default=4,
                    help="layers per index-sharing group in the plan-replay leg (1 resolving "
                         "layer + the rest replaying its plan)")
@@ -768,8 +772,23 @@ def host_threads():
     return max(1, min(16, n))
 
 
+LEGS = ("headline", "device_pool", "plan_replay", "kv", "paged", "adversarial", "all_layer",
+        "scatter", "tiny", "cpu_baseline", "host_link")
+
+
 def main():
     args = parse()
+    if args.only:
+        keep = set(args.only.split(","))
+        bad = keep - set(LEGS)
+        if bad:
+            print(f"unknown legs: {sorted(bad)}", file=sys.stderr)
+            sys.exit(2)
+        for leg in LEGS[1:]:
+            setattr(args, "no_" + leg, leg not in keep)
+        args.skip_headline = "headline" not in keep
+    else:
+        args.skip_headline = False
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): requests shard across "
               f"GPUs with no exchange between them, so there is no multi-GPU leg to time.",
@@ -793,6 +812,20 @@ def main():
     if link:
         log(f"[bench] host link: {json.dumps({k: round(v, 2) for k, v in link.items()})}")
 
+    K = args.steps
+    peak = link["h2d_ceiling_gbs"] if link else None
+    if args.skip_headline:
+        out = {"metric": "swapped-in rows/s + effective GB/s (% of HBM/host-link peak); "
+                         "µs per decode-step call", "value": None, "unit": "rows/s", "n_gpus": 1,
+               "steps": K, "warmup": args.warmup, "legs": args.only}
+    else:
+        out = headline(cfg, args, link, peak, torch, hs, wdev)
+    legs(cfg, args, out, link, peak, torch, hs, wdev)
+    print(json.dumps(out), flush=True)
+
+
+def headline(cfg, args, link, peak, torch, hs, wdev):
+    """The contract's timed region on the DeepSeek-V3.2-like decode trace."""
     r = run_gpu(cfg, args.warmup, args.steps, torch, hs, wdev, b2b_pass=True)
     K = args.steps
     rows = int(r["counts"].sum())
@@ -806,8 +839,7 @@ def main():
     kernel = "resolve_kernel<false, false, 16, false> (resolution + the request's own row copies)"
     achieved = bytes_link / (us_kernel * 1e-6) / 1e9
     call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
-    peak = link["h2d_ceiling_gbs"] if link else None
-    out = {
+    return {
         "metric": "swapped-in rows/s + effective GB/s (% of HBM/host-link peak); µs per decode-step call",
         "value": round(value, 1),
         "unit": "rows/s",
@@ -845,6 +877,11 @@ def main():
         "host_link": {k: round(v, 2) for k, v in link.items()} if link else None,
     }
 
+
+def legs(cfg, args, out, link, peak, torch, hs, wdev):
+    """Every other leg, each added to `out` under its own key."""
+    from workloads import gen
+    K = args.steps
     if not args.no_device_pool:
         dcfg = gen.DEVPOOL
         n = args.device_pool_steps
@@ -1032,7 +1069,6 @@ def main():
                 "sample": f"the same {args.steps} steps run {tpasses} times, each step's {cfg.B} "
                           f"requests split over {nt} threads (one oracle call per group); "
                           f"{trow} rows in {tsec:.2f} s of wall time"}
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <type_traits>
 #include <mutex>
 
 #include "hs_common.hpp"
@@ -46,15 +47,48 @@ constexpr int kEarlyChunks = 1;  // fused copy: chunks per lane loaded before th
 constexpr int kKU = 2;
 constexpr int kHU = 4;
 constexpr int32_t kPending = INT32_MIN;    // s_out value of an id still unresolved
+// Loop trips (bucket steps) an insert or a lookup may take under Knuth's hash
+// before the workgroup switches to the salted one. Dense and uniform top-k
+// sets take at most 3 or 4 at a quarter-full table.
+constexpr int kTripLimit = 8;
 
-// Knuth's multiplicative hashing (TAOCP vol. 3, 6.4): multiply by
-// floor(2^32 / golden ratio) = 2654435761 and keep the TOP bits of the 32-bit
-// product -- here the top log2(buckets) bits pick the home bucket. Both pages
-// use this multiplier but keep the low bits (product mod size), which for
-// power-of-two sizes only permutes id mod size; the high bits spread ids that
-// share low bits. Only speed depends on this choice, never a result.
-__device__ __forceinline__ uint32_t bucket_of(int32_t key, uint32_t bshift) {
+// Home bucket of a key: Knuth's multiplicative hashing (TAOCP vol. 3, 6.4).
+// Multiply by floor(2^32 / golden ratio) = 2654435761 and keep the TOP bits
+// of the 32-bit product -- the top log2(buckets) bits pick the bucket. Both
+// pages use this multiplier but keep the low bits (product mod size), which
+// for power-of-two sizes only permutes id mod size. The top bits spread a run
+// of consecutive ids evenly (three-distance theorem), and top-k ids are dense
+// runs of recent positions. Only speed depends on the hash, never a result.
+__device__ __forceinline__ uint32_t bucket_knuth(int32_t key, uint32_t bshift) {
   return (static_cast<uint32_t>(key) * 2654435761u) >> bshift;
+}
+
+// The fallback when Knuth's hash clusters. Any fixed hash lets whoever picks
+// the ids pick ones that share home buckets (a 65,536-token context holds
+// ~4,000 ids in any 1/16 of the buckets; such a set made the probe phase ~40x
+// slower). When an insert or a lookup runs past kTripLimit buckets, the
+// workgroup rebuilds its table with this hash: the key XOR a 32-bit salt
+// drawn per workgroup and call (a splitmix64 mix of the shader clock and the
+// batch row), through MurmurHash3's 32-bit finalizer (a bijection in which
+// every input bit flips each output bit with probability close to 1/2); its
+// top bits pick the bucket. A random multiplier alone was tried as the only
+// hash and dropped: some draws spread dense position runs badly, and the
+// slowest of B workgroups sets the kernel's time.
+__device__ __forceinline__ uint32_t bucket_salted(int32_t key, uint32_t salt, uint32_t bshift) {
+  uint32_t h = static_cast<uint32_t>(key) ^ salt;
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h >> bshift;
+}
+
+// splitmix64's output function (Steele, Lea and Flood, 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
 }
 
 struct SwapArgs {
@@ -107,8 +141,8 @@ struct SwapArgs {
 };
 
 struct LdsLayout {
-  uint32_t hash, hidx, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, dummy, hbt,
-      sbt, total;
+  uint32_t hash, hidx, bcnt, out, topk, lru, nlru, tok, victim, hitpos, missw, wtot, seed, dummy,
+      hbt, sbt, total;
 };
 
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) / a * a; }
@@ -134,7 +168,8 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
   l.hitpos = o; o = align_up(o + 8 * hwords, 16);
   l.missw = o;  o = align_up(o + 8 * kwords, 16);
-  l.wtot = o;   o = align_up(o + 4 * (2 * (kWaves + 1) + 1), 16);
+  l.wtot = o;   o = align_up(o + 4 * (2 * (kWaves + 1) + 2), 16);
+  l.seed = o;   o = align_up(o + 16, 16);                      // this call's hash salt
   l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
   l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
@@ -195,11 +230,13 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
   uint64_t* missw = reinterpret_cast<uint64_t*>(lds + lay.missw);
   // Cross-wave counts: pre_hit[w] / pre_miss[w] collect the totals of the
-  // waves before w, entry kWaves the grand total; s_pending the pending ids.
+  // waves before w, entry kWaves the grand total; s_pending the pending ids;
+  // s_retry the hash fallback flag.
   int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
   int32_t* pre_hit = wtot;
   int32_t* pre_miss = wtot + kWaves + 1;
   int32_t* s_pending = wtot + 2 * (kWaves + 1);
+  int32_t* s_retry = s_pending + 1;   // set when Knuth's hash clusters
   int16_t* s_lru = reinterpret_cast<int16_t*>(lds + lay.lru);
   int16_t* victim = reinterpret_cast<int16_t*>(lds + lay.victim);
   // Inactive lanes aim their CAS at a private word, so the CAS of every
@@ -209,6 +246,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   uint32_t* sinku = reinterpret_cast<uint32_t*>(sink64);
   const uint32_t bmask = a.T / 4 - 1;       // buckets - 1
   const uint32_t bshift = a.shift + 2;      // top log2(buckets) bits
+  uint32_t* s_salt = reinterpret_cast<uint32_t*>(lds + lay.seed);
   const int32_t* ids = a.topk + static_cast<int64_t>(b) * a.topk_stride;
 
   const int64_t r = a.req_rows[b];
@@ -282,7 +320,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
     u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
     for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
-    if (tid < 2 * (kWaves + 1) + 1) wtot[tid] = 0;
+    if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
     if constexpr (kPaged) {
       // The request's hot block table row: every slot -> row translation in
       // the probe and the assign step then stays in LDS.
@@ -373,191 +411,248 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     if (L >= 1 && L - 1 < l64) newest_t = static_cast<int32_t>(L - 1);
     row_newest = row_of(H);
   }
-  for (int base = 0; base < K; base += kKU * kThreads) {
-    int32_t t[kKU], o[kKU];
-    uint32_t bk[kKU];
-    bool ins[kKU];
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int i = base + u * kThreads + tid;
-      t[u] = base == 0 ? vi[u] : (i < K ? s_topk[i] : 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int i = base + u * kThreads + tid;
-      if constexpr (kPaged) {
-        // vLLM page, first phase: position -> global id through the source
-        // block table (a physical block of 0 or below has no row), and a
-        // resident row when the resident table holds the position.
-        const int32_t tt = t[u];
-        int64_t g = -1, res = -1;
-        if (i < K) {
-          g = tt;
-          // Block and offset by multiply-shift division (tt < 2^31).
-          const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
-          const int32_t rq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.rbs_div));
-          if (a.sbt) {
-            g = -1;
-            if (tt >= 0 && sq < a.sbt_nblocks) {
-              const int32_t pb = a.sbt_n ? reinterpret_cast<const int32_t*>(lds + lay.sbt)[sq]
-                                         : a.sbt[r * a.sbt_stride + sq];
-              if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
-            }
-          }
-          if (g >= a.pool_nrows) g = -1;
-          if (a.rbt && tt >= 0 && rq < a.rbt_nblocks) {
-            const int32_t pb = a.rbt[r * a.rbt_stride + rq];
-            if (pb != a.r_null && pb >= 0) {
-              res = static_cast<int64_t>(pb) * a.rbs + (tt - rq * a.rbs);
-              if (res > INT32_MAX) res = -1;
-            }
-          }
-        }
-        ins[u] = i < K && res < 0 && g >= 0;
-        o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
-        t[u] = static_cast<int32_t>(g);            // the key from here on
-        if (ins[u]) s_topk[i] = t[u];
-      } else {
-        bool valid = i < K && static_cast<uint32_t>(t[u]) < lim;
-        if constexpr (kPoolRows) {
-          if (valid) {
-            const int64_t pr = prow[t[u]];
-            valid = pr >= 0 && pr < a.pool_nrows;
-          }
-        }
-        const bool newest = valid && t[u] == newest_t;
-        ins[u] = valid && !newest;
-        o[u] = !valid ? -1 : (newest ? row_newest : kPending);
-      }
-      bk[u] = bucket_of(t[u], bshift);
-    }
-    int npend = 0;
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) npend += __popcll(__ballot(ins[u]));
-    // Each pending id takes the next entry of its home bucket with one LDS
-    // atomicAdd on the bucket's count; a full bucket passes it on to the next
-    // bucket (linear probing over buckets). A lookup stops at the first bucket
-    // that is not full, which this order guarantees to be past the key; the
-    // table is at most half full, so insertion terminates.
-    const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
-    while (__ballot(any_of(ins)) != 0) {
-      uint32_t p[kKU];
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
+  // Classification + inserts (1) and the LRU scan (2), written once and run
+  // with Knuth's hash. If an insert or a lookup runs past kTripLimit buckets,
+  // the workgroup clears the table and its counts and runs both again with
+  // the salted hash, reading the ids from global memory again. Nothing the
+  // first run writes outside LDS survives into the second.
+  auto classify_insert = [&](auto salted_tag, uint32_t salt) {
+    constexpr bool kSalted = decltype(salted_tag)::value;
+    for (int base = 0; base < K; base += kKU * kThreads) {
+      int32_t t[kKU], o[kKU];
+      uint32_t bk[kKU];
+      bool ins[kKU];
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
-        if (ins[u] && p[u] < 4) {
-          hkey[4 * bk[u] + p[u]] = t[u];
-          hidx[4 * bk[u] + p[u]] = static_cast<int16_t>(base + u * kThreads + tid);
-        }
-        const bool full = ins[u] && p[u] >= 4;
-        bk[u] = full ? ((bk[u] + 1) & bmask) : bk[u];
-        ins[u] = full;
+        const int i = base + u * kThreads + tid;
+        t[u] = kSalted ? (i < K ? ids[i] : 0) : (base == 0 ? vi[u] : (i < K ? s_topk[i] : 0));
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int i = base + u * kThreads + tid;
-      if (i < K) s_out[i] = o[u];
+      for (int u = 0; u < kKU; ++u) {
+        const int i = base + u * kThreads + tid;
+        if constexpr (kPaged) {
+          // vLLM page, first phase: position -> global id through the source
+          // block table (a physical block of 0 or below has no row), and a
+          // resident row when the resident table holds the position.
+          const int32_t tt = t[u];
+          int64_t g = -1, res = -1;
+          if (i < K) {
+            g = tt;
+            // Block and offset by multiply-shift division (tt < 2^31).
+            const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
+            const int32_t rq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.rbs_div));
+            if (a.sbt) {
+              g = -1;
+              if (tt >= 0 && sq < a.sbt_nblocks) {
+                const int32_t pb = a.sbt_n ? reinterpret_cast<const int32_t*>(lds + lay.sbt)[sq]
+                                           : a.sbt[r * a.sbt_stride + sq];
+                if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
+              }
+            }
+            if (g >= a.pool_nrows) g = -1;
+            if (a.rbt && tt >= 0 && rq < a.rbt_nblocks) {
+              const int32_t pb = a.rbt[r * a.rbt_stride + rq];
+              if (pb != a.r_null && pb >= 0) {
+                res = static_cast<int64_t>(pb) * a.rbs + (tt - rq * a.rbs);
+                if (res > INT32_MAX) res = -1;
+              }
+            }
+          }
+          ins[u] = i < K && res < 0 && g >= 0;
+          o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
+          t[u] = static_cast<int32_t>(g);            // the key from here on
+          if (ins[u]) s_topk[i] = t[u];
+        } else {
+          bool valid = i < K && static_cast<uint32_t>(t[u]) < lim;
+          if constexpr (kPoolRows) {
+            if (valid) {
+              const int64_t pr = prow[t[u]];
+              valid = pr >= 0 && pr < a.pool_nrows;
+            }
+          }
+          const bool newest = valid && t[u] == newest_t;
+          ins[u] = valid && !newest;
+          o[u] = !valid ? -1 : (newest ? row_newest : kPending);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u)
+        bk[u] = kSalted ? bucket_salted(t[u], salt, bshift) : bucket_knuth(t[u], bshift);
+      int npend = 0;
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) npend += __popcll(__ballot(ins[u]));
+      // Each pending id takes the next entry of its home bucket with one LDS
+      // atomicAdd on the bucket's count; a full bucket passes it on to the next
+      // bucket (linear probing over buckets). A lookup stops at the first bucket
+      // that is not full, which this order guarantees to be past the key; the
+      // table is at most half full, so insertion terminates.
+      const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
+      int trips = 0;
+      while (__ballot(any_of(ins)) != 0) {
+        if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
+          if (lane == 0) *s_retry = 1;
+          break;
+        }
+        uint32_t p[kKU];
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) p[u] = u < nu ? atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u) : 4u;
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          if (ins[u] && p[u] < 4) {
+            hkey[4 * bk[u] + p[u]] = t[u];
+            hidx[4 * bk[u] + p[u]] = static_cast<int16_t>(base + u * kThreads + tid);
+          }
+          const bool full = ins[u] && p[u] >= 4;
+          bk[u] = full ? ((bk[u] + 1) & bmask) : bk[u];
+          ins[u] = full;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int i = base + u * kThreads + tid;
+        if (i < K) s_out[i] = o[u];
+      }
+      if (lane == 0 && npend) atomicAdd(s_pending, npend);
     }
-    if (lane == 0 && npend) atomicAdd(s_pending, npend);
-  }
-  __syncthreads();
+  };
 
   // ---- 2. LRU scan: probe each slot's token -------------------------------
   // Wave w walks its own 64-aligned segment of LRU positions. A slot whose
   // token is pending is a hit and serves that top-k entry; the first claimant
   // wins (a second slot with the same token -- corrupt state -- stays
   // evictable instead of serving the entry twice).
-  const int pending_n = *s_pending;
-  int run = 0;
-  for (int c0 = 0; c0 < segH; c0 += 4 * kWave) {
-    int32_t sl[4], key[4], idx[4];
-    uint32_t bk[4];
-    bool act[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = h0 + c0 + u * kWave + lane;
-      sl[u] = c0 == 0 ? vl[u] : ((c0 + u * kWave < segH && p < H) ? s_lru[p] : -1);
-    }
-    // Each slot's hot row, worked out beside the token read (with paged
-    // addressing it is an LDS table read of its own, kept off the CAS's path).
-    int32_t rw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rw[u] = row_of((sl[u] >= 0 && sl[u] < H) ? sl[u] : 0);
-    // The staging choice is uniform: branching once keeps all four token
-    // reads of a lane in flight together.
-    if (a.stage_tokens) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? s_tok[sl[u]] : -1;
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? tokens[sl[u]] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      act[u] = key[u] >= 0;
-      bk[u] = bucket_of(key[u], bshift);
-      idx[u] = -1;
-    }
-    // Branch-free lookup step over one bucket (four keys, 16 bytes) per
-    // query. Buckets fill in entry order, so a bucket whose last key is empty
-    // is not full and ends a miss. Ends when no lane of the wave is still
-    // searching; the top-k index of each found key is read once afterwards.
-    // The bucket's four top-k indices (8 bytes) are read beside its keys, so
-    // a found key's index needs no further LDS round trip.
-    while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
-      u32x4 kv[4];
-      uint64_t iv[4];
+  // Returns the wave's hits.
+  auto probe = [&](auto salted_tag, uint32_t salt) -> int {
+    constexpr bool kSalted = decltype(salted_tag)::value;
+    int run = 0;
+    for (int c0 = 0; c0 < segH; c0 += 4 * kWave) {
+      int32_t sl[4], key[4], idx[4];
+      uint32_t bk[4];
+      bool act[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
-        iv[u] = reinterpret_cast<const uint64_t*>(hidx)[bk[u]];
+        const int p = h0 + c0 + u * kWave + lane;
+        sl[u] = c0 == 0 ? vl[u] : ((c0 + u * kWave < segH && p < H) ? s_lru[p] : -1);
+      }
+      // Each slot's hot row, worked out beside the token read (with paged
+      // addressing it is an LDS table read of its own, kept off the CAS's path).
+      int32_t rw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rw[u] = row_of((sl[u] >= 0 && sl[u] < H) ? sl[u] : 0);
+      // The staging choice is uniform: branching once keeps all four token
+      // reads of a lane in flight together.
+      if (a.stage_tokens) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? s_tok[sl[u]] : -1;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? tokens[sl[u]] : -1;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int32_t kk = key[u];
-        const bool m0 = static_cast<int32_t>(kv[u].x) == kk;
-        const bool m1 = static_cast<int32_t>(kv[u].y) == kk;
-        const bool m2 = static_cast<int32_t>(kv[u].z) == kk;
-        const bool m3 = static_cast<int32_t>(kv[u].w) == kk;
-        const bool found = m0 | m1 | m2 | m3;
-        const uint32_t j = m0 ? 0u : (m1 ? 1u : (m2 ? 2u : 3u));
-        const bool open = static_cast<int32_t>(kv[u].w) == -1;
-        const int ii = static_cast<int16_t>(static_cast<uint32_t>(iv[u] >> (16 * j)) & 0xffffu);
-        const int take = -static_cast<int>(act[u] && found);   // all ones or zero
-        idx[u] = (ii & take) | (idx[u] & ~take);
-        act[u] = act[u] && !found && !open;
-        bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
+        act[u] = key[u] >= 0;
+        idx[u] = -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        bk[u] = kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift);
+      // Branch-free lookup step over one bucket (four keys, 16 bytes) per
+      // query. Buckets fill in entry order, so a bucket whose last key is empty
+      // is not full and ends a miss. Ends when no lane of the wave is still
+      // searching; the top-k index of each found key is read once afterwards.
+      // The bucket's four top-k indices (8 bytes) are read beside its keys, so
+      // a found key's index needs no further LDS round trip.
+      int trips = 0;
+      while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
+        if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
+          if (lane == 0) *s_retry = 1;
+          break;
+        }
+        u32x4 kv[4];
+        uint64_t iv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
+          iv[u] = reinterpret_cast<const uint64_t*>(hidx)[bk[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int32_t kk = key[u];
+          const bool m0 = static_cast<int32_t>(kv[u].x) == kk;
+          const bool m1 = static_cast<int32_t>(kv[u].y) == kk;
+          const bool m2 = static_cast<int32_t>(kv[u].z) == kk;
+          const bool m3 = static_cast<int32_t>(kv[u].w) == kk;
+          const bool found = m0 | m1 | m2 | m3;
+          const uint32_t j = m0 ? 0u : (m1 ? 1u : (m2 ? 2u : 3u));
+          const bool open = static_cast<int32_t>(kv[u].w) == -1;
+          const int ii = static_cast<int16_t>(static_cast<uint32_t>(iv[u] >> (16 * j)) & 0xffffu);
+          const int take = -static_cast<int>(act[u] && found);   // all ones or zero
+          idx[u] = (ii & take) | (idx[u] & ~take);
+          act[u] = act[u] && !found && !open;
+          bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
+        }
+      }
+      int32_t prev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending, idx[u] >= 0 ? rw[u] : 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool hit = idx[u] >= 0 && prev[u] == kPending;
+        const uint64_t m = __ballot(hit);
+        const int p0 = h0 + c0 + u * kWave;
+        if (c0 + u * kWave < segH && p0 < H) {
+          if (lane == 0) hitpos[p0 >> 6] = m;
+          run += __popcll(m);
+        }
       }
     }
-    int32_t prev[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending, idx[u] >= 0 ? rw[u] : 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool hit = idx[u] >= 0 && prev[u] == kPending;
-      const uint64_t m = __ballot(hit);
-      const int p0 = h0 + c0 + u * kWave;
-      if (c0 + u * kWave < segH && p0 < H) {
-        if (lane == 0) hitpos[p0 >> 6] = m;
-        run += __popcll(m);
-      }
-    }
-  }
+    return run;
+  };
+
+  classify_insert(std::false_type{}, 0u);
+  __syncthreads();
+  const int2 pend_retry = *reinterpret_cast<const int2*>(s_pending);   // one LDS read
+  int pending_n = pend_retry.x;
+  int run = pend_retry.y == 0 ? probe(std::false_type{}, 0u) : 0;
   // Wave w adds its total to the prefix of every later wave and to the grand
   // total: one LDS atomic per lane, no scan after the barrier.
   if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
   __syncthreads();
+  int hits = pre_hit[kWaves];
+  int hits_before = pre_hit[wave];
+  if (*s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
+    // Fallback: once every lane has read the flag, clear the table, its
+    // counts and the cross-wave counters (the flag with them), then run
+    // classification and the scan again with the salted hash.
+    __syncthreads();
+    u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
+    for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+    for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+    if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
+    if (tid == 0) {   // the salt, fresh per workgroup and call
+      const uint64_t z = static_cast<uint64_t>(clock64()) ^ (static_cast<uint64_t>(b) << 40);
+      *s_salt = static_cast<uint32_t>(mix64(z + 0x9E3779B97F4A7C15ull));
+    }
+    __syncthreads();
+    // The same for the whole workgroup (a scalar register).
+    const uint32_t salt = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*s_salt));
+    classify_insert(std::true_type{}, salt);
+    __syncthreads();
+    pending_n = *s_pending;
+    run = probe(std::true_type{}, salt);
+    if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
+    __syncthreads();
+    hits = pre_hit[kWaves];
+    hits_before = pre_hit[wave];
+  }
 
   // ---- 3. miss words, (host pools) early row loads, victims, new LRU order ---
   // New order: stale evictables, then the M victims (they receive the misses,
   // in miss order), then the hits -- every group in its old order. A
   // position's rank among hits is the hits of earlier waves, plus this wave's
   // earlier chunks, plus the hit lanes below it.
-  const int hits = pre_hit[kWaves];
-  const int hits_before = pre_hit[wave];
   const int E = H - hits;            // evictable slots
   const int M = pending_n - hits;    // misses (<= E because K <= H)
   // The fused copy's list (pool row, hot row) in miss order, kept in the key

@@ -170,8 +170,9 @@ def test_misaligned_hot_uses_4byte_path():
 
 
 def test_clusters_under_the_kernel_hash():
-    """Ids that share the top bits of the multiplicative hash (long probe chains
-    in the LDS table) still resolve exactly."""
+    """Ids that share the top bits of Knuth's multiplicative hash: inserts and
+    lookups run past the kernel's trip limit, the workgroup rebuilds its table
+    with the salted hash, and everything still resolves exactly."""
     h = _harness()
     K, H = 512, 1024
     T = 1024                                        # table entries for K = 512
