@@ -210,7 +210,7 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // table to global ids, which are the slot keys and the pool rows; resident
 // ids are served from the device cache as they are; slots live where the hot
 // block table says; there is no newest-token slot.
-template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged>
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -296,6 +296,15 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   const int segK = static_cast<int>(wave_segment(K));
   const int h0 = wave * segH;
   const int k0 = wave * segK;
+  // Tile guards. With kExact (K a multiple of kKU * 1024 and H of kHU * 1024,
+  // which the host checks) every top-k entry a pass or a wave segment names
+  // is below K, every LRU position a segment chunk names is below H, and
+  // every chunk offset lies inside its segment, so these fold to true and
+  // the guarded loads and stores need no exec-mask branches.
+  auto in_k = [&](int i) { return kExact || i < K; };
+  auto in_h = [&](int p) { return kExact || p < H; };
+  auto in_seg_h = [&](int off) { return kExact || off < segH; };
+  auto in_seg_k = [&](int off) { return kExact || off < segK; };
   int32_t vi[kKU];
   int16_t vl[4];   // LRU entries at h0 + u*64 + lane
   {
@@ -303,17 +312,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
-      vi[u] = x < K ? ids[x] : 0;
+      vi[u] = in_k(x) ? ids[x] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + u * kWave + lane;
-      vl[u] = (u * kWave < segH && p < H) ? lru[p] : static_cast<int16_t>(-1);
+      vl[u] = (in_seg_h(u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(-1);
     }
 #pragma unroll
     for (int u = 0; u < kHU; ++u) {
       const int x = u * kThreads + tid;
-      vt[u] = (a.stage_tokens && x < H) ? tokens[x] : 0;
+      vt[u] = (a.stage_tokens && in_h(x)) ? tokens[x] : 0;
     }
     // Keys start empty (-1, never a token id) and bucket counts at 0.
     u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
@@ -334,18 +343,18 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int x = u * kThreads + tid;
-      if (x < K) s_topk[x] = vi[u];
+      if (in_k(x)) s_topk[x] = vi[u];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + u * kWave + lane;
-      if (u * kWave < segH && p < H) s_lru[p] = vl[u];
+      if (in_seg_h(u * kWave) && in_h(p)) s_lru[p] = vl[u];
     }
     if (a.stage_tokens) {
 #pragma unroll
       for (int u = 0; u < kHU; ++u) {
         const int x = u * kThreads + tid;
-        if (x < H) s_tok[x] = vt[u];
+        if (in_h(x)) s_tok[x] = vt[u];
       }
     }
   }
@@ -367,12 +376,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      wl[u] = (c0 + u * kWave < segH && p < H) ? lru[p] : static_cast<int16_t>(0);
+      wl[u] = (in_seg_h(c0 + u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      if (c0 + u * kWave < segH && p < H) s_lru[p] = wl[u];
+      if (in_seg_h(c0 + u * kWave) && in_h(p)) s_lru[p] = wl[u];
     }
   }
   if (a.stage_tokens) {
@@ -381,12 +390,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int x = base + u * kThreads + tid;
-        wt[u] = x < H ? tokens[x] : 0;
+        wt[u] = in_h(x) ? tokens[x] : 0;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int x = base + u * kThreads + tid;
-        if (x < H) s_tok[x] = wt[u];
+        if (in_h(x)) s_tok[x] = wt[u];
       }
     }
   }
@@ -425,7 +434,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
         const int i = base + u * kThreads + tid;
-        t[u] = kSalted ? (i < K ? ids[i] : 0) : (base == 0 ? vi[u] : (i < K ? s_topk[i] : 0));
+        t[u] = kSalted ? (in_k(i) ? ids[i] : 0) : (base == 0 ? vi[u] : (in_k(i) ? s_topk[i] : 0));
       }
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
@@ -436,7 +445,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
           // resident row when the resident table holds the position.
           const int32_t tt = t[u];
           int64_t g = -1, res = -1;
-          if (i < K) {
+          if (in_k(i)) {
             g = tt;
             // Block and offset by multiply-shift division (tt < 2^31).
             const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
@@ -458,12 +467,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
               }
             }
           }
-          ins[u] = i < K && res < 0 && g >= 0;
+          ins[u] = in_k(i) && res < 0 && g >= 0;
           o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
           t[u] = static_cast<int32_t>(g);            // the key from here on
           if (ins[u]) s_topk[i] = t[u];
         } else {
-          bool valid = i < K && static_cast<uint32_t>(t[u]) < lim;
+          bool valid = in_k(i) && static_cast<uint32_t>(t[u]) < lim;
           if constexpr (kPoolRows) {
             if (valid) {
               const int64_t pr = prow[t[u]];
@@ -510,7 +519,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
         const int i = base + u * kThreads + tid;
-        if (i < K) s_out[i] = o[u];
+        if (in_k(i)) s_out[i] = o[u];
       }
       if (lane == 0 && npend) atomicAdd(s_pending, npend);
     }
@@ -532,7 +541,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int p = h0 + c0 + u * kWave + lane;
-        sl[u] = c0 == 0 ? vl[u] : ((c0 + u * kWave < segH && p < H) ? s_lru[p] : -1);
+        sl[u] = c0 == 0 ? vl[u] : ((in_seg_h(c0 + u * kWave) && in_h(p)) ? s_lru[p] : -1);
       }
       // Each slot's hot row, worked out beside the token read (with paged
       // addressing it is an LDS table read of its own, kept off the CAS's path).
@@ -601,7 +610,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         const bool hit = idx[u] >= 0 && prev[u] == kPending;
         const uint64_t m = __ballot(hit);
         const int p0 = h0 + c0 + u * kWave;
-        if (c0 + u * kWave < segH && p0 < H) {
+        if (in_seg_h(c0 + u * kWave) && in_h(p0)) {
           if (lane == 0) hitpos[p0 >> 6] = m;
           run += __popcll(m);
         }
@@ -663,18 +672,18 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // segment's miss words and adds its miss total to the later waves' prefixes.
   auto miss_words = [&]() {
     int mrun = 0;
-    for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+    for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
       int32_t so[kKU];
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
         const int i = k0 + c0 + u * kWave + lane;
-        so[u] = (c0 + u * kWave < segK && i < K) ? s_out[i] : 0;
+        so[u] = (in_seg_k(c0 + u * kWave) && in_k(i)) ? s_out[i] : 0;
       }
 #pragma unroll
       for (int u = 0; u < kKU; ++u) {
         const int q = k0 + c0 + u * kWave;
         const uint64_t mm = __ballot(so[u] == kPending);
-        if (c0 + u * kWave < segK && q < K) {
+        if (in_seg_k(c0 + u * kWave) && in_k(q)) {
           if (lane == 0) missw[q >> 6] = mm;
           mrun += __popcll(mm);
         }
@@ -697,16 +706,16 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       miss_words();
       __syncthreads();
       int mrun = pre_miss[wave];
-      for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+      for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
         uint64_t wd[kKU];
         int32_t t[kKU];
 #pragma unroll
         for (int u = 0; u < kKU; ++u) {
           const int q = k0 + c0 + u * kWave;
           const int i = q + lane;
-          const bool in = c0 + u * kWave < segK && q < K;
+          const bool in = in_seg_k(c0 + u * kWave) && in_k(q);
           wd[u] = in ? missw[q >> 6] : 0;
-          t[u] = (in && i < K) ? s_topk[i] : 0;
+          t[u] = (in && in_k(i)) ? s_topk[i] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kKU; ++u) {
@@ -739,22 +748,22 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   }
   run = hits_before;
   int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
-  for (int c0 = 0; c0 < segH && h0 + c0 < H; c0 += 4 * kWave) {
+  for (int c0 = 0; c0 < segH && in_h(h0 + c0); c0 += 4 * kWave) {
     // The chunk's four hit words arrive in one LDS read (lanes 0-3) and are
     // broadcast with readlane, so no read waits on the one before it.
     int16_t sp[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = h0 + c0 + u * kWave;     // chunk start
-      const bool in = c0 + u * kWave < segH && q < H;
-      sp[u] = c0 == 0 ? vl[u] : ((in && q + lane < H) ? s_lru[q + lane] : static_cast<int16_t>(0));
+      const bool in = in_seg_h(c0 + u * kWave) && in_h(q);
+      sp[u] = c0 == 0 ? vl[u] : ((in && in_h(q + lane)) ? s_lru[q + lane] : static_cast<int16_t>(0));
     }
-    const uint64_t wl = (lane < 4 && c0 + lane * kWave < segH) ? hitpos[((h0 + c0) >> 6) + lane] : 0;
+    const uint64_t wl = (lane < 4 && in_seg_h(c0 + lane * kWave)) ? hitpos[((h0 + c0) >> 6) + lane] : 0;
     uint64_t wd[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = h0 + c0 + u * kWave;
-      const bool in = c0 + u * kWave < segH && q < H;
+      const bool in = in_seg_h(c0 + u * kWave) && in_h(q);
       const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(wl), u);
       const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(wl >> 32), u);
       wd[u] = in ? (static_cast<uint64_t>(hi) << 32 | lo) : 0;
@@ -762,7 +771,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + c0 + u * kWave + lane;
-      if (c0 + u * kWave < segH) {       // uniform
+      if (in_seg_h(c0 + u * kWave)) {       // uniform
         const bool h = (wd[u] >> lane) & 1ull;
         const int hr = run + rank_below(wd[u]);
         const int e = p - hr;              // rank among evictables
@@ -770,7 +779,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         // hit: E + hr; victim: E - M + e; other evictable: e - M
         const int hm = -static_cast<int>(h);
         const int np = (hm & (E + hr)) | (~hm & (e - M + (vic ? E : 0)));
-        if (p < H) {
+        if (in_h(p)) {
           // Lanes that are not victims write their private sink instead,
           // which keeps this step free of branches.
           *(vic ? &victim[e] : sink16) = sp[u];
@@ -792,17 +801,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int32_t* ws_dst = a.dst + static_cast<int64_t>(b) * K;
   int32_t* mask = a.miss_mask ? a.miss_mask + static_cast<int64_t>(b) * K : nullptr;
   run = miss_before;
-  for (int c0 = 0; c0 < segK && k0 + c0 < K; c0 += kKU * kWave) {
+  for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
     uint64_t wd[kKU];
     int32_t so[kKU], t[kKU];
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int q = k0 + c0 + u * kWave;
       const int i = q + lane;
-      const bool in = c0 + u * kWave < segK && q < K;
+      const bool in = in_seg_k(c0 + u * kWave) && in_k(q);
       wd[u] = in ? missw[q >> 6] : 0;
-      so[u] = (in && i < K) ? s_out[i] : 0;
-      t[u] = (in && i < K) ? s_topk[i] : 0;
+      so[u] = (in && in_k(i)) ? s_out[i] : 0;
+      t[u] = (in && in_k(i)) ? s_topk[i] : 0;
     }
     int m[kKU], v[kKU];
 #pragma unroll
@@ -814,7 +823,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int i = k0 + c0 + u * kWave + lane;
-      if (c0 + u * kWave >= segK || i >= K) continue;
+      if (!in_seg_k(c0 + u * kWave) || !in_k(i)) continue;
       int32_t o = so[u];
       const bool missed = ((wd[u] >> lane) & 1ull) && v[u] >= 0 && v[u] < H;
       if (mask) mask[i] = missed ? 1 : 0;
@@ -926,12 +935,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 // Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
 // (pool row, hot row) and its length to the workspace for the copy kernel;
 // with kCopyW != 0 also copies the rows itself (W-byte chunks).
-template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged>
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0, static_cast<uint32_t>(a.hbt_n),
                                    static_cast<uint32_t>(a.sbt_n));
-  resolve<kSlotRows, kPoolRows, kCopyW, kPaged>(a, blockIdx.x, lds, lay);
+  resolve<kSlotRows, kPoolRows, kCopyW, kPaged, kExact>(a, blockIdx.x, lds, lay);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -986,14 +995,19 @@ int allow_lds(int device, const void* fn, uint32_t bytes) {
 }
 
 // The resolve kernel for the given tables and fused copy width (0 = none).
+// `exact` (K a multiple of kKU * 1024, H of kHU * 1024) selects the
+// instantiation without tile guards, for the flat and the paged layouts.
 template <int kW>
-const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged) {
-  if (paged) return reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true>);
+const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged, bool exact) {
+  if (paged)
+    return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, true>)
+                 : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, false>);
   if (slot_rows)
-    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW, false>)
-                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW, false>);
-  return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<false, true, kW, false>)
-                   : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false>);
+    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW, false, false>)
+                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW, false, false>);
+  if (pool_rows) return reinterpret_cast<const void*>(&resolve_kernel<false, true, kW, false, false>);
+  return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, true>)
+               : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, false>);
 }
 
 // Everything a launch needs, validated once per call.
@@ -1130,7 +1144,8 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
   const bool sr = a->slot_rows != nullptr, prw = a->pool_rows != nullptr;
-  const void* resolve_fn = pick_resolve<0>(sr, prw, pg);
+  const bool exact = a->K % (kKU * kThreads) == 0 && a->H % (kHU * kThreads) == 0;
+  const void* resolve_fn = pick_resolve<0>(sr, prw, pg, exact);
   if (lay.total > 65536) {
     rc = allow_lds(di.device, resolve_fn, lay.total);
     if (rc != HS_OK) return rc;
@@ -1169,7 +1184,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // kernel, which spreads every request over many CUs.
   const void* fused_fn = nullptr;
   if (attr.type == hipMemoryTypeHost) {
-    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg) : pick_resolve<4>(sr, prw, pg);
+    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg, exact) : pick_resolve<4>(sr, prw, pg, exact);
     if (lay.total > 65536) {
       rc = allow_lds(di.device, fused_fn, lay.total);
       if (rc != HS_OK) return rc;
