@@ -131,7 +131,8 @@ struct SwapArgs {
   int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
   int32_t B, K, H;
   int64_t S_r, R;
-  uint32_t T;         // hash entries, power of two >= 2K
+  uint32_t T;         // hash entries, power of two >= 2K (0 with a direct table)
+  uint32_t dtab;      // direct-address table entries (ctx_stride), or 0 for the hash
   uint32_t shift;     // 32 - log2(T)
   int32_t stage_tokens;
   int32_t hbt_n;      // paged: hot block table entries staged in LDS (0 = read from HBM)
@@ -153,16 +154,26 @@ __host__ __device__ inline uint32_t wave_segment(int32_t n) {
   return align_up((static_cast<uint32_t>(n) + kWaves - 1) / kWaves, 64);
 }
 
+// dtab != 0: the direct-address table of dtab int16 entries replaces the hash
+// (keys, indices and counts); the region still holds the fused copy's miss
+// list (12 bytes per miss) after the probe.
 __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T, bool stage_tokens,
-                                                uint32_t hbt_n, uint32_t sbt_n) {
+                                                uint32_t hbt_n, uint32_t sbt_n, uint32_t dtab) {
   const uint32_t hwords = kWaves * wave_segment(H) / 64;
   const uint32_t kwords = kWaves * wave_segment(K) / 64;
   LdsLayout l;
   // every region starts on a 16-byte boundary
   uint32_t o = 0;
-  l.hash = o;   o = align_up(o + 4 * T, 16);                  // keys; later: miss list
-  l.hidx = o;   o = align_up(o + 2 * T, 16);                  // top-k index of each key
-  l.bcnt = o;   o = align_up(o + T, 16);                      // one count per 4-key bucket
+  if (dtab) {
+    const uint32_t list = 12 * static_cast<uint32_t>(K);
+    l.hash = o; o = align_up(o + (2 * dtab > list ? 2 * dtab : list), 16);   // table; later: miss list
+    l.hidx = o;
+    l.bcnt = o;
+  } else {
+    l.hash = o;   o = align_up(o + 4 * T, 16);                // keys; later: miss list
+    l.hidx = o;   o = align_up(o + 2 * T, 16);                // top-k index of each key
+    l.bcnt = o;   o = align_up(o + T, 16);                    // one count per 4-key bucket
+  }
   l.out = o;    o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.topk = o;   o = align_up(o + 4 * static_cast<uint32_t>(K), 16);
   l.tok = o;    o = align_up(o + (stage_tokens ? 4 * static_cast<uint32_t>(H) : 0), 16);
@@ -210,7 +221,7 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // table to global ids, which are the slot keys and the pool rows; resident
 // ids are served from the device cache as they are; slots live where the hot
 // block table says; there is no newest-token slot.
-template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact>
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact, bool kDirect>
 __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsLayout& lay) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -221,6 +232,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
   int32_t* hkey = reinterpret_cast<int32_t*>(lds + lay.hash);
+  // Direct-address table (kDirect): entry t holds the top-k index of pending
+  // position t. Never cleared: a lookup checks that the index it reads names
+  // an entry holding that very position, so stale contents never match.
+  int16_t* dtab = reinterpret_cast<int16_t*>(lds + lay.hash);
   int16_t* hidx = reinterpret_cast<int16_t*>(lds + lay.hidx);
   uint32_t* bcnt = reinterpret_cast<uint32_t*>(lds + lay.bcnt);
   int16_t* nlru = reinterpret_cast<int16_t*>(lds + lay.nlru);
@@ -324,11 +339,13 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int x = u * kThreads + tid;
       vt[u] = (a.stage_tokens && in_h(x)) ? tokens[x] : 0;
     }
-    // Keys start empty (-1, never a token id) and bucket counts at 0.
-    u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
-    for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
-    u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
-    for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!kDirect) {
+      // Keys start empty (-1, never a token id) and bucket counts at 0.
+      u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
+      for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+      u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+      for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
     if constexpr (kPaged) {
       // The request's hot block table row: every slot -> row translation in
@@ -484,12 +501,21 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
           o[u] = !valid ? -1 : (newest ? row_newest : kPending);
         }
       }
-#pragma unroll
-      for (int u = 0; u < kKU; ++u)
-        bk[u] = kSalted ? bucket_salted(t[u], salt, bshift) : bucket_knuth(t[u], bshift);
       int npend = 0;
 #pragma unroll
       for (int u = 0; u < kKU; ++u) npend += __popcll(__ballot(ins[u]));
+      if constexpr (kDirect) {
+        // A pending position t (< lim <= ctx_stride = table size) records its
+        // top-k index; ids are unique, so no two entries meet.
+#pragma unroll
+        for (int u = 0; u < kKU; ++u)
+          if (ins[u]) dtab[t[u]] = static_cast<int16_t>(base + u * kThreads + tid);
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) ins[u] = false;
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u)
+        bk[u] = kDirect ? 0u : (kSalted ? bucket_salted(t[u], salt, bshift) : bucket_knuth(t[u], bshift));
       // Each pending id takes the next entry of its home bucket with one LDS
       // atomicAdd on the bucket's count; a full bucket passes it on to the next
       // bucket (linear probing over buckets). A lookup stops at the first bucket
@@ -497,7 +523,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       // table is at most half full, so insertion terminates.
       const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
       int trips = 0;
-      while (__ballot(any_of(ins)) != 0) {
+      while (!kDirect && __ballot(any_of(ins)) != 0) {
         if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
           if (lane == 0) *s_retry = 1;
           break;
@@ -559,12 +585,25 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        act[u] = key[u] >= 0;
+        act[u] = !kDirect && key[u] >= 0;
         idx[u] = -1;
+      }
+      if constexpr (kDirect) {
+        // Direct table: the entry of the slot's position names a top-k index;
+        // the slot is a candidate hit when that index's id is this position.
+        // Two dependent LDS reads, no search.
+        int32_t ti[4], tk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          ti[u] = (key[u] >= 0 && static_cast<uint32_t>(key[u]) < a.dtab) ? dtab[key[u]] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tk[u] = (ti[u] >= 0 && ti[u] < K) ? s_topk[ti[u]] : -2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) idx[u] = tk[u] == key[u] ? ti[u] : -1;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        bk[u] = kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift);
+        bk[u] = kDirect ? 0u : (kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift));
       // Branch-free lookup step over one bucket (four keys, 16 bytes) per
       // query. Buckets fill in entry order, so a bucket whose last key is empty
       // is not full and ends a miss. Ends when no lane of the wave is still
@@ -572,7 +611,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       // The bucket's four top-k indices (8 bytes) are read beside its keys, so
       // a found key's index needs no further LDS round trip.
       int trips = 0;
-      while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
+      while (!kDirect && __ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
         if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
           if (lane == 0) *s_retry = 1;
           break;
@@ -630,7 +669,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   __syncthreads();
   int hits = pre_hit[kWaves];
   int hits_before = pre_hit[wave];
-  if (*s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
+  if (!kDirect && *s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
     // Fallback: once every lane has read the flag, clear the table, its
     // counts and the cross-wave counters (the flag with them), then run
     // classification and the scan again with the salted hash.
@@ -935,12 +974,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 // Resolve: one 1024-lane workgroup per batch row. Publishes the miss list
 // (pool row, hot row) and its length to the workspace for the copy kernel;
 // with kCopyW != 0 also copies the rows itself (W-byte chunks).
-template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact>
+template <bool kSlotRows, bool kPoolRows, int kCopyW, bool kPaged, bool kExact, bool kDirect>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(SwapArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LdsLayout lay = lds_layout(a.K, a.H, a.T, a.stage_tokens != 0, static_cast<uint32_t>(a.hbt_n),
-                                   static_cast<uint32_t>(a.sbt_n));
-  resolve<kSlotRows, kPoolRows, kCopyW, kPaged, kExact>(a, blockIdx.x, lds, lay);
+                                   static_cast<uint32_t>(a.sbt_n), a.dtab);
+  resolve<kSlotRows, kPoolRows, kCopyW, kPaged, kExact, kDirect>(a, blockIdx.x, lds, lay);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -996,18 +1035,22 @@ int allow_lds(int device, const void* fn, uint32_t bytes) {
 
 // The resolve kernel for the given tables and fused copy width (0 = none).
 // `exact` (K a multiple of kKU * 1024, H of kHU * 1024) selects the
-// instantiation without tile guards, for the flat and the paged layouts.
+// instantiation without tile guards, for the flat and the paged layouts;
+// `direct` the direct-address table instead of the hash, for the flat layout.
 template <int kW>
-const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged, bool exact) {
+const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged, bool exact, bool direct) {
   if (paged)
-    return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, true>)
-                 : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, false>);
+    return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, true, false>)
+                 : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, false, false>);
   if (slot_rows)
-    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW, false, false>)
-                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW, false, false>);
-  if (pool_rows) return reinterpret_cast<const void*>(&resolve_kernel<false, true, kW, false, false>);
-  return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, true>)
-               : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, false>);
+    return pool_rows ? reinterpret_cast<const void*>(&resolve_kernel<true, true, kW, false, false, false>)
+                     : reinterpret_cast<const void*>(&resolve_kernel<true, false, kW, false, false, false>);
+  if (pool_rows) return reinterpret_cast<const void*>(&resolve_kernel<false, true, kW, false, false, false>);
+  if (direct)
+    return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, true, true>)
+                 : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, false, true>);
+  return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, true, false>)
+               : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, false, false, false>);
 }
 
 // Everything a launch needs, validated once per call.
@@ -1113,10 +1156,13 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   DeviceInfo di;
   int rc = device_info(&di);
   if (rc != HS_OK) return rc;
-  // LDS plan, best first: a quarter-full hash table with the slot-token row
-  // staged; a half-full table with the row staged; then the same without
-  // staging (tokens gathered from HBM). Shorter probe chains matter most: a
-  // wave's probe loop runs as long as its longest chain.
+  // LDS plan, best first. Flat layout with positions below ctx_stride as
+  // keys: a direct-address table of ctx_stride int16 entries when it fits,
+  // with the slot-token row staged, then without. Otherwise a quarter-full
+  // hash table with the slot-token row staged; a half-full table with the row
+  // staged; then the same without staging (tokens gathered from HBM). Shorter
+  // probe chains matter most: a wave's probe loop runs as long as its longest
+  // chain.
   const uint32_t k2 = 2u * static_cast<uint32_t>(a->K) < 64u ? 64u : 2u * static_cast<uint32_t>(a->K);
   // Paged: the request's hot block table row (one entry per block of slots)
   // and source block table row go to LDS when they are small; larger rows
@@ -1127,25 +1173,30 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
     if (nb <= 2048) hbt_n = static_cast<uint32_t>(nb);
     if (pa->src_block_table && pa->src_num_blocks <= 2048) sbt_n = static_cast<uint32_t>(pa->src_num_blocks);
   }
-  const uint32_t plans_T[4] = {pow2_at_least(2 * k2), pow2_at_least(k2), pow2_at_least(2 * k2),
+  const bool flat = !pg && !a->slot_rows && !a->pool_rows;
+  const uint32_t dtab_n = (flat && a->ctx_stride <= (1 << 16)) ? static_cast<uint32_t>(a->ctx_stride) : 0u;
+  const uint32_t plans_T[6] = {0u, 0u, pow2_at_least(2 * k2), pow2_at_least(k2), pow2_at_least(2 * k2),
                                pow2_at_least(k2)};
-  const bool plans_stage[4] = {true, true, false, false};
+  const uint32_t plans_D[6] = {dtab_n, dtab_n, 0u, 0u, 0u, 0u};
+  const bool plans_stage[6] = {true, false, true, true, false, false};
   int plan = -1;
   LdsLayout lay{};
-  for (int i = 0; i < 4 && plan < 0; ++i) {
-    lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i], hbt_n, sbt_n);
+  for (int i = 0; i < 6 && plan < 0; ++i) {
+    if (i < 2 && dtab_n == 0) continue;
+    lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i], hbt_n, sbt_n, plans_D[i]);
     if (static_cast<int>(lay.total) <= di.max_lds) plan = i;
   }
   if (plan < 0)
     return set_error(HS_ERANGE, "K=%d, H=%d need %u bytes of LDS; the device allows %d", a->K,
                      a->H, lay.total, di.max_lds);
   const uint32_t T = plans_T[plan];
+  const uint32_t dtab = plans_D[plan];
   const bool stage = plans_stage[plan];
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
   const bool sr = a->slot_rows != nullptr, prw = a->pool_rows != nullptr;
   const bool exact = a->K % (kKU * kThreads) == 0 && a->H % (kHU * kThreads) == 0;
-  const void* resolve_fn = pick_resolve<0>(sr, prw, pg, exact);
+  const void* resolve_fn = pick_resolve<0>(sr, prw, pg, exact, dtab != 0);
   if (lay.total > 65536) {
     rc = allow_lds(di.device, resolve_fn, lay.total);
     if (rc != HS_OK) return rc;
@@ -1184,7 +1235,8 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // kernel, which spreads every request over many CUs.
   const void* fused_fn = nullptr;
   if (attr.type == hipMemoryTypeHost) {
-    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg, exact) : pick_resolve<4>(sr, prw, pg, exact);
+    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg, exact, dtab != 0)
+                       : pick_resolve<4>(sr, prw, pg, exact, dtab != 0);
     if (lay.total > 65536) {
       rc = allow_lds(di.device, fused_fn, lay.total);
       if (rc != HS_OK) return rc;
@@ -1242,6 +1294,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   s.S_r = a->S_r;
   s.R = a->R;
   s.T = T;
+  s.dtab = dtab;
   s.shift = 32 - log2T;
   s.stage_tokens = stage ? 1 : 0;
   s.hbt_n = static_cast<int32_t>(hbt_n);
