@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
+static_assert(kWaves % 4 == 0, "per-wave counts are summed four at a time");
 constexpr int kFuseUnroll = 12;  // chunks per lane per round, fused copy
 constexpr int kEarlyChunks = 1;  // fused copy: chunks per lane loaded before the victims
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
@@ -180,7 +181,7 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.hitpos = o; o = align_up(o + 8 * hwords, 16);
   l.missw = o;  o = align_up(o + 8 * kwords, 16);
   l.wtot = o;   o = align_up(o + 4 * (2 * (kWaves + 1) + 2), 16);
-  l.seed = o;   o = align_up(o + 16, 16);                      // this call's hash salt
+  l.seed = o;   o = align_up(o + (dtab ? 4 * kWaves : 16), 16);   // hash salt / per-wave pending ids
   l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
   l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
@@ -245,8 +246,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   uint64_t* hitpos = reinterpret_cast<uint64_t*>(lds + lay.hitpos);
   uint64_t* missw = reinterpret_cast<uint64_t*>(lds + lay.missw);
   // Cross-wave counts: pre_hit[w] / pre_miss[w] collect the totals of the
-  // waves before w, entry kWaves the grand total; s_pending the pending ids;
-  // s_retry the hash fallback flag.
+  // waves before w, entry kWaves the grand total; s_pending the pending ids
+  // (hashed plans) and s_retry the hash fallback flag.
   int32_t* wtot = reinterpret_cast<int32_t*>(lds + lay.wtot);
   int32_t* pre_hit = wtot;
   int32_t* pre_miss = wtot + kWaves + 1;
@@ -259,6 +260,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   unsigned long long* sink64 = reinterpret_cast<unsigned long long*>(lds + lay.dummy) + tid;
   int32_t* sink32 = reinterpret_cast<int32_t*>(sink64);
   uint32_t* sinku = reinterpret_cast<uint32_t*>(sink64);
+  // Direct plans: the pending ids each wave classified, written (not added,
+  // so nothing clears them first) where hashed plans keep their salt.
+  int32_t* wpend = reinterpret_cast<int32_t*>(lds + lay.seed);
   const uint32_t bmask = a.T / 4 - 1;       // buckets - 1
   const uint32_t bshift = a.shift + 2;      // top log2(buckets) bits
   uint32_t* s_salt = reinterpret_cast<uint32_t*>(lds + lay.seed);
@@ -322,101 +326,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   auto in_seg_k = [&](int off) { return kExact || off < segK; };
   int32_t vi[kKU];
   int16_t vl[4];   // LRU entries at h0 + u*64 + lane
-  {
-    int32_t vt[kHU];
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int x = u * kThreads + tid;
-      vi[u] = in_k(x) ? ids[x] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = h0 + u * kWave + lane;
-      vl[u] = (in_seg_h(u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(-1);
-    }
-#pragma unroll
-    for (int u = 0; u < kHU; ++u) {
-      const int x = u * kThreads + tid;
-      vt[u] = (a.stage_tokens && in_h(x)) ? tokens[x] : 0;
-    }
-    if constexpr (!kDirect) {
-      // Keys start empty (-1, never a token id) and bucket counts at 0.
-      u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
-      for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
-      u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
-      for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
-    if constexpr (kPaged) {
-      // The request's hot block table row: every slot -> row translation in
-      // the probe and the assign step then stays in LDS.
-      int32_t* hb = reinterpret_cast<int32_t*>(lds + lay.hbt);
-      for (int i = tid; i < a.hbt_n; i += kThreads) hb[i] = a.hbt[r * a.hbt_stride + i];
-      // ... and the source block table row, so classifying an id needs no
-      // dependent HBM read.
-      int32_t* sb = reinterpret_cast<int32_t*>(lds + lay.sbt);
-      for (int i = tid; i < a.sbt_n; i += kThreads) sb[i] = a.sbt[r * a.sbt_stride + i];
-    }
-#pragma unroll
-    for (int u = 0; u < kKU; ++u) {
-      const int x = u * kThreads + tid;
-      if (in_k(x)) s_topk[x] = vi[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = h0 + u * kWave + lane;
-      if (in_seg_h(u * kWave) && in_h(p)) s_lru[p] = vl[u];
-    }
-    if (a.stage_tokens) {
-#pragma unroll
-      for (int u = 0; u < kHU; ++u) {
-        const int x = u * kThreads + tid;
-        if (in_h(x)) s_tok[x] = vt[u];
-      }
-    }
-  }
-  for (int base = kKU * kThreads; base < K; base += 4 * kThreads) {
-    int32_t wi[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
-      wi[u] = x < K ? ids[x] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = base + u * kThreads + tid;
-      if (x < K) s_topk[x] = wi[u];
-    }
-  }
-  for (int c0 = 4 * kWave; c0 < segH; c0 += 4 * kWave) {    // H > 4096
-    int16_t wl[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = h0 + c0 + u * kWave + lane;
-      wl[u] = (in_seg_h(c0 + u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = h0 + c0 + u * kWave + lane;
-      if (in_seg_h(c0 + u * kWave) && in_h(p)) s_lru[p] = wl[u];
-    }
-  }
-  if (a.stage_tokens) {
-    for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
-      int32_t wt[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = base + u * kThreads + tid;
-        wt[u] = in_h(x) ? tokens[x] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = base + u * kThreads + tid;
-        if (in_h(x)) s_tok[x] = wt[u];
-      }
-    }
-  }
-  __syncthreads();
+  const bool early_classify = kDirect && K <= kKU * kThreads;   // uniform
 
   // ---- 1. classify ids; bind the newest token; insert pending ids ----------
   // SGLang page: the newest token goes to newest_slot (= H), every other id is
@@ -444,6 +354,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // first run writes outside LDS survives into the second.
   auto classify_insert = [&](auto salted_tag, uint32_t salt) {
     constexpr bool kSalted = decltype(salted_tag)::value;
+    int wave_pending = 0;
     for (int base = 0; base < K; base += kKU * kThreads) {
       int32_t t[kKU], o[kKU];
       uint32_t bk[kKU];
@@ -547,7 +458,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         const int i = base + u * kThreads + tid;
         if (in_k(i)) s_out[i] = o[u];
       }
-      if (lane == 0 && npend) atomicAdd(s_pending, npend);
+      if constexpr (kDirect) wave_pending += npend;
+      else if (lane == 0 && npend) atomicAdd(s_pending, npend);
+    }
+    if constexpr (kDirect) {
+      if (lane == 0) wpend[wave] = wave_pending;
     }
   };
 
@@ -658,11 +573,123 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     return run;
   };
 
-  classify_insert(std::false_type{}, 0u);
+  {
+    int32_t vt[kHU];
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int x = u * kThreads + tid;
+      vi[u] = in_k(x) ? ids[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      vl[u] = (in_seg_h(u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(-1);
+    }
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const int x = u * kThreads + tid;
+      vt[u] = (a.stage_tokens && in_h(x)) ? tokens[x] : 0;
+    }
+    if constexpr (!kDirect) {
+      // Keys start empty (-1, never a token id) and bucket counts at 0.
+      u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
+      for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+      u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+      for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;   // prefixes and the retry flag
+    if constexpr (kPaged) {
+      // The request's hot block table row: every slot -> row translation in
+      // the probe and the assign step then stays in LDS.
+      int32_t* hb = reinterpret_cast<int32_t*>(lds + lay.hbt);
+      for (int i = tid; i < a.hbt_n; i += kThreads) hb[i] = a.hbt[r * a.hbt_stride + i];
+      // ... and the source block table row, so classifying an id needs no
+      // dependent HBM read.
+      int32_t* sb = reinterpret_cast<int32_t*>(lds + lay.sbt);
+      for (int i = tid; i < a.sbt_n; i += kThreads) sb[i] = a.sbt[r * a.sbt_stride + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int x = u * kThreads + tid;
+      if (in_k(x)) s_topk[x] = vi[u];
+    }
+    // With a direct table (nothing to clear) and one pass of ids, the ids
+    // are classified and recorded as soon as they land, while the LRU and
+    // token rows are still on their way, and one barrier less is needed.
+    if (early_classify) classify_insert(std::false_type{}, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      if (in_seg_h(u * kWave) && in_h(p)) s_lru[p] = vl[u];
+    }
+    if (a.stage_tokens) {
+#pragma unroll
+      for (int u = 0; u < kHU; ++u) {
+        const int x = u * kThreads + tid;
+        if (in_h(x)) s_tok[x] = vt[u];
+      }
+    }
+  }
+  for (int base = kKU * kThreads; base < K; base += 4 * kThreads) {
+    int32_t wi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      wi[u] = x < K ? ids[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + u * kThreads + tid;
+      if (x < K) s_topk[x] = wi[u];
+    }
+  }
+  for (int c0 = 4 * kWave; c0 < segH; c0 += 4 * kWave) {    // H > 4096
+    int16_t wl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + c0 + u * kWave + lane;
+      wl[u] = (in_seg_h(c0 + u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + c0 + u * kWave + lane;
+      if (in_seg_h(c0 + u * kWave) && in_h(p)) s_lru[p] = wl[u];
+    }
+  }
+  if (a.stage_tokens) {
+    for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
+      int32_t wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        wt[u] = in_h(x) ? tokens[x] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        if (in_h(x)) s_tok[x] = wt[u];
+      }
+    }
+  }
   __syncthreads();
-  const int2 pend_retry = *reinterpret_cast<const int2*>(s_pending);   // one LDS read
-  int pending_n = pend_retry.x;
-  int run = pend_retry.y == 0 ? probe(std::false_type{}, 0u) : 0;
+  // All pending ids of the request.
+  auto sum_pending = [&]() -> int {
+    if constexpr (!kDirect) return *s_pending;
+    const int4* w4 = reinterpret_cast<const int4*>(wpend);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < kWaves / 4; ++q) {
+      const int4 v = w4[q];
+      n += v.x + v.y + v.z + v.w;
+    }
+    return n;
+  };
+  if (!early_classify) {
+    classify_insert(std::false_type{}, 0u);
+    __syncthreads();
+  }
+  int pending_n = sum_pending();
+  int run = *s_retry == 0 ? probe(std::false_type{}, 0u) : 0;
   // Wave w adds its total to the prefix of every later wave and to the grand
   // total: one LDS atomic per lane, no scan after the barrier.
   if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
@@ -688,7 +715,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     const uint32_t salt = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*s_salt));
     classify_insert(std::true_type{}, salt);
     __syncthreads();
-    pending_n = *s_pending;
+    pending_n = sum_pending();
     run = probe(std::true_type{}, salt);
     if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
     __syncthreads();
