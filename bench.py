@@ -695,14 +695,16 @@ def run_all_layer(torch, hs, reps=5):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream()
     res = {}
-    for name, sp, dp in (("offload", dptr, hptr), ("load", hptr, dptr)):
+    for name, sp, dp, sl, dl in (("offload", dptr, hptr, dev, host), ("load", hptr, dptr, host, dev)):
+        link = hs.transfer_host_link(sl, dl)      # the launch shape from the memory kinds
+        assert link, "one side is pinned host memory"
         us = []
         for rep in range(reps + 1):
             flush.fill_(rep)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
             hs.transfer_rows_all_layer(src_layer_ptrs=sp, dst_layer_ptrs=dp, src_idx=si, dst_idx=di,
-                                       row_bytes=rb, src_nrows=rows, dst_nrows=rows, host_link=True)
+                                       row_bytes=rb, src_nrows=rows, dst_nrows=rows, host_link=link)
             e1.record(s)
             torch.cuda.synchronize()
             if rep:

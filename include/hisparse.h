@@ -324,7 +324,8 @@ size_t hs_swap_in_workspace_layout(int32_t B, int32_t K, size_t* count_offset, s
  * dst indices must be unique and source and destination rows must not overlap.
  * row_bytes > 0, multiple of 4; n == 0 or num_layers == 0 returns HS_OK.
  * flags: 0, or HS_TRANSFER_HOST_LINK when one side is pinned host memory (the
- * offload and load directions). The library cannot see where the layer bases
+ * offload and load directions; hs_transfer_flags_for works it out from one
+ * pair of layer bases). The library cannot see where the layer bases
  * point; with the flag the launch uses one workgroup per two CUs, each lane
  * keeping 8 chunks in flight, which moves more over the host link than the
  * HBM-sized launch and leaves the other CUs to concurrent work. The bytes
@@ -335,6 +336,20 @@ int transfer_rows_all_layer(const uint64_t* src_layer_ptrs, const uint64_t* dst_
                             const int64_t* src_idx, const int64_t* dst_idx, int64_t n,
                             int32_t num_layers, int64_t row_bytes, int64_t src_nrows,
                             int64_t dst_nrows, uint32_t flags, hipStream_t stream);
+
+/*
+ * hs_transfer_flags_for -- the flags argument of transfer_rows_all_layer and
+ * transfer_kv_all_layer for layers that live where src_layer and dst_layer do.
+ * Not on the pages: the transfers take their layer bases from device arrays
+ * the library cannot read on the host, so the caller names the memory kind;
+ * this reads it from one source and one destination layer base (host
+ * pointers as the caller holds them) and is meant to run once, where the
+ * caches are set up. *flags becomes HS_TRANSFER_HOST_LINK when either side
+ * is pinned host memory, else 0. Enqueues nothing.
+ * Errors: NULL argument -> HS_EINVAL; a pointer HIP does not know, or memory
+ * other than device or pinned host -> HS_EMEMKIND (*flags unchanged).
+ */
+int hs_transfer_flags_for(const void* src_layer, const void* dst_layer, uint32_t* flags);
 
 /*
  * transfer_kv_all_layer -- the non-MLA form of transfer_rows_all_layer.

@@ -21,7 +21,7 @@ from ._lib import EXPORTS, HisparseError, PagedAddressing, SwapInArgs, check, lo
 __all__ = ["hisparse_swap_in", "hisparse_swap_in_noalloc", "hisparse_resolve", "hisparse_gather_compact",
            "hisparse_gather_compact_layers", "transfer_kv_all_layer", "store_kv_cache",
            "hisparse_invalidate_written",
-           "swap_in_workspace_layout", "transfer_rows_all_layer", "store_kv_scatter",
+           "swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_host_link", "store_kv_scatter",
            "hisparse_state_reset", "swap_in_workspace_bytes", "HisparseError", "load", "EXPORTS"]
 
 
@@ -253,6 +253,18 @@ def transfer_rows_all_layer(*, src_layer_ptrs: torch.Tensor, dst_layer_ptrs: tor
         _dev(src_idx, torch.int64, "src_idx"), _dev(dst_idx, torch.int64, "dst_idx"),
         src_idx.numel(), L, row_bytes, src_nrows, dst_nrows, HOST_LINK if host_link else 0,
         _stream(stream)))
+
+
+def transfer_host_link(src_layer: torch.Tensor, dst_layer: torch.Tensor) -> bool:
+    """Whether transfers between layers that live where ``src_layer`` and
+    ``dst_layer`` do should take ``host_link=True`` (either side is pinned host
+    memory). Reads the memory kind of the two tensors' storage; meant for
+    once, where the caches are set up."""
+    flags = ctypes.c_uint32(0)
+    check("hs_transfer_flags_for", load().hs_transfer_flags_for(
+        ctypes.c_void_p(src_layer.data_ptr()), ctypes.c_void_p(dst_layer.data_ptr()),
+        ctypes.byref(flags)))
+    return bool(flags.value & HOST_LINK)
 
 
 def transfer_kv_all_layer(*, k_src_layer_ptrs: torch.Tensor, v_src_layer_ptrs: torch.Tensor,

@@ -22,8 +22,8 @@ EXPORTS = ("hs_swap_in_workspace_bytes", "hisparse_swap_in", "hisparse_swap_in_n
            "hisparse_resolve",
            "hisparse_gather_compact", "hisparse_gather_compact_layers",
            "hs_swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_kv_all_layer",
-           "store_kv_scatter", "store_kv_cache", "hisparse_invalidate_written",
-           "hisparse_state_reset", "hisparse_last_error")
+           "hs_transfer_flags_for", "store_kv_scatter", "store_kv_cache",
+           "hisparse_invalidate_written", "hisparse_state_reset", "hisparse_last_error")
 
 
 class PagedAddressing(ctypes.Structure):
@@ -102,6 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.store_kv_scatter.restype = ctypes.c_int
     lib.transfer_kv_all_layer.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i64, i64, i64, u32, vp]
     lib.transfer_kv_all_layer.restype = ctypes.c_int
+    lib.hs_transfer_flags_for.argtypes = [vp, vp, ctypes.POINTER(u32)]
+    lib.hs_transfer_flags_for.restype = ctypes.c_int
     lib.store_kv_cache.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64, i64, vp]
     lib.store_kv_cache.restype = ctypes.c_int
     lib.hisparse_invalidate_written.argtypes = [vp, i64, i64, vp, vp, i64, vp]

@@ -336,6 +336,23 @@ extern "C" int transfer_kv_all_layer(const uint64_t* k_src_layer_ptrs,
                          flags, stream);
 }
 
+extern "C" int hs_transfer_flags_for(const void* src_layer, const void* dst_layer, uint32_t* flags) {
+  if (!src_layer || !dst_layer || !flags) return set_error(HS_EINVAL, "a required pointer is NULL");
+  bool host = false;
+  for (const void* p : {src_layer, dst_layer}) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(HS_EMEMKIND, "a layer base is not a HIP allocation (device or pinned host)");
+    }
+    if (attr.type == hipMemoryTypeHost) host = true;
+    else if (attr.type != hipMemoryTypeDevice)
+      return set_error(HS_EMEMKIND, "a layer base must be device memory or pinned host memory");
+  }
+  *flags = host ? HS_TRANSFER_HOST_LINK : 0u;
+  return HS_OK;
+}
+
 extern "C" int store_kv_scatter(const void* src, int64_t src_row_stride_bytes, void* dst,
                                 int64_t dst_row_stride_bytes, int64_t dst_nrows, const int64_t* loc,
                                 int64_t n, int64_t row_bytes, hipStream_t stream) {

@@ -127,6 +127,14 @@ def test_transfer_rejects(lib):
     assert lib.transfer_rows_all_layer(None, None, None, None, 0, 3, 16, 10, 10, 0x80000000, None) == -1
 
 
+def test_transfer_flags_for_rejects_null(lib):
+    flags = ctypes.c_uint32(7)
+    assert lib.hs_transfer_flags_for(None, ctypes.c_void_p(0x1000), ctypes.byref(flags)) == -1
+    assert lib.hs_transfer_flags_for(ctypes.c_void_p(0x1000), None, ctypes.byref(flags)) == -1
+    assert lib.hs_transfer_flags_for(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000), None) == -1
+    assert flags.value == 7
+
+
 def test_scatter_rejects(lib):
     f = 0x100000
     assert lib.store_kv_scatter(f, 8, f, 16, 10, f, 3, 16, None) == -1      # src stride < rb

@@ -74,6 +74,24 @@ def test_transfer_parity(L, rows, rb, n, src_kind, dst_kind, host_link):
         assert np.array_equal(_np(src_l[l]), want_src[l]), f"source layer {l} changed"
 
 
+@pytest.mark.parametrize("src_kind,dst_kind,want", [
+    ("device", "device", False), ("host", "device", True), ("device", "host", True),
+    ("host", "host", True)])
+def test_transfer_host_link_from_memory_kind(src_kind, dst_kind, want):
+    import sparse_attention_kv_hisparse_amd as hs
+    _, src_l, _ = _layers(2, 8, 656, src_kind, 5)
+    _, dst_l, _ = _layers(2, 8, 656, dst_kind, 6)
+    assert hs.transfer_host_link(src_l[1], dst_l[0]) is want
+
+
+def test_transfer_host_link_rejects_unknown_memory():
+    import sparse_attention_kv_hisparse_amd as hs
+    pageable = torch.zeros((8, 656), dtype=torch.uint8)      # plain host memory, not pinned
+    dev = torch.zeros((8, 656), dtype=torch.uint8, device="cuda")
+    with pytest.raises(hs.HisparseError, match="HS_EMEMKIND"):
+        hs.transfer_host_link(pageable, dev)
+
+
 @pytest.mark.parametrize("direction", ["offload", "load"])
 def test_transfer_all_layer_full_size(direction):
     """61 layers x 262,144 rows x 656 B, 8192 pairs, one direction per case:
