@@ -81,8 +81,15 @@ def _small(**kw):
     # largest sizes the per-request LDS scratch allows (160 KB per workgroup):
     dict(H=32768, K=584, ctx=70000, B=2, steps=3, row_bytes=16),   # H at its maximum
     dict(H=4096, K=4096, ctx=9000, B=2, steps=3, row_bytes=16),    # K at its maximum
+    # positions past 65536 take the hashed plans: two classification passes,
+    # and K at its maximum there too
+    dict(H=5000, K=3000, ctx=70000, B=2),
+    dict(H=4096, K=4096, ctx=70000, B=2, steps=3, row_bytes=16),
+    # a direct table that fits only with the slot-token row left in HBM
+    dict(H=16384, K=2048, ctx=32768, B=2, steps=3),
 ], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single",
-        "unstaged_host", "unstaged_dev", "many_host", "many_dev", "max_H", "max_K"])
+        "unstaged_host", "unstaged_dev", "many_host", "many_dev", "max_H", "max_K",
+        "hashed_two_passes", "hashed_max_K", "direct_unstaged"])
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
@@ -169,16 +176,18 @@ def test_misaligned_hot_uses_4byte_path():
         run.step(topk, gen.seq_lens(cfg, t))
 
 
-def test_clusters_under_the_kernel_hash():
+@pytest.mark.parametrize("K,H,span", [(512, 1024, 200000), (3000, 4096, 600000)],
+                         ids=["one_pass", "two_passes"])
+def test_clusters_under_the_kernel_hash(K, H, span):
     """Ids that share the top bits of Knuth's multiplicative hash: inserts and
     lookups run past the kernel's trip limit, the workgroup rebuilds its table
-    with the salted hash, and everything still resolves exactly."""
+    with the salted hash, and everything still resolves exactly. With K = 3000
+    the ids take two classification passes, both in the first run and in the
+    rebuild."""
     h = _harness()
-    K, H = 512, 1024
-    T = 1024                                        # table entries for K = 512
-    ids = np.arange(200000, dtype=np.uint64)
+    ids = np.arange(span, dtype=np.uint64)
     home = ((ids * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - 10)
-    cand = ids[home < 8].astype(np.int64)           # ~1600 ids in 8 home buckets of 1024
+    cand = ids[home < 8].astype(np.int64)           # ids in 8 of 1024 top-bit windows
     ctx = int(cand.max()) + 2
     cfg = _small(B=2, H=H, K=K, ctx=ctx, row_bytes=16)
     run = h.ParityRun(cfg)
