@@ -766,7 +766,7 @@ def cpu_baseline(cfg, warmup, steps, min_seconds, threads=1):
 
 
 def host_threads():
-    """Host cores this process may use, at most 16 (one GPU's share of the box)."""
+    """Host cores this process may use, at most 16 (one GPU's share of a host's cores)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
