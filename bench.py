@@ -839,6 +839,7 @@ def headline(cfg, args, link, peak, torch, hs, wdev):
     # on the launch stream. (Pass 2 reports the split API's two kernels.)
     us_kernel = r["us_b2b"]
     kernel = "resolve_kernel<false, false, 16, false> (resolution + the request's own row copies)"
+    fl_us, fl_rows = run_flushed(cfg, 8, 5, torch, hs, wdev)
     achieved = bytes_link / (us_kernel * 1e-6) / 1e9
     call_gbs = bytes_link / (r["us_total"] * 1e-6) / 1e9     # whole call
     return {
@@ -869,6 +870,12 @@ def headline(cfg, args, link, peak, torch, hs, wdev):
         "effective_GBps_call": round(call_gbs, 2),
         "frac_host_link_call": round(call_gbs / peak, 4) if peak else None,
         "us_per_launch_back_to_back": round(us_kernel / K, 2),
+        "steady_state_protocol": {
+            "back_to_back_us_per_call": round(r["us_total"] / K, 2),
+            "restore_and_flush_us_per_call": round(fl_us, 2),
+            "restore_and_flush_rows_per_call": round(fl_rows, 1),
+            "note": "median over 8 steps of the median of 5 replays, each from a restored "
+                    "state after a 512 MiB write"},
         "roofline": {"bound": "host_link", "kernel": kernel,
                      "timing": "mean launch time, launches queued back to back behind a spin "
                                "kernel, two events on the launch stream",
