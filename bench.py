@@ -174,7 +174,9 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False, b2b_
             c1.record(stream)
     torch.cuda.synchronize()
     us_cold = c0.elapsed_time(c1) * 1000.0 if warmup else None
-    cold_rows = int(counts[0].sum().item()) if warmup else 0
+    # (The cold step's row count is read after the timed region: the process's
+    # first tensor reduction makes the next launch's host call ~0.1 ms slower
+    # once, which a short timed region would carry.)
     e0, e1 = events()
     if lead_spin:
         torch.cuda._sleep(2_000_000)
@@ -187,6 +189,7 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False, b2b_
     wall = time.perf_counter() - w0
     us_total = e0.elapsed_time(e1) * 1000.0
     log(f"[bench] {cfg.name}: {steps} timed calls after {warmup} warm-up, {us_total / steps:.1f} us/call")
+    cold_rows = int(counts[0].sum().item()) if warmup else 0
     c = counts.cpu().numpy()[warmup:].copy()
 
     # pass 2
