@@ -17,9 +17,15 @@
 //    from ballot + mbcnt plus a running count, and only the 16 per-wave
 //    totals cross waves, so there is no block-wide scan and no wave64 scan
 //    window to get wrong (the pages' per-warp chunk scan needs one).
+//  * Membership (is this slot's token one of the pending ids?) is an LDS
+//    table built per call: a direct-address table of top-k indices over
+//    positions when the layout is flat and the table fits, else a bucketed
+//    hash (Knuth's multiplicative hash, rebuilt with a salted hash when a
+//    chain runs long). No result depends on which one runs.
 //  * swap_copy_kernel: the misses, published as a compact (pool row, hot row)
-//    list in the caller's workspace, are copied by many 256-lane workgroups
-//    per request as a flat stream of 16-byte chunks. The kernel boundary is
+//    list in the caller's workspace, are copied by many workgroups per
+//    request (1024-lane ones, two per CU, from an HBM pool; 256-lane ones
+//    otherwise) as a flat stream of 16-byte chunks. The kernel boundary is
 //    the only hand-off between the two, so no workgroup ever waits on another.
 //  * With a pinned-host pool the resolve kernel copies its own request's rows
 //    as well (phase 5): the host link is full with one workgroup per request.
