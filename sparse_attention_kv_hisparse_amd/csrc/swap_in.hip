@@ -424,9 +424,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       if constexpr (kDirect) {
         // A pending position t (< lim <= ctx_stride = table size) records its
         // top-k index; ids are unique, so no two entries meet.
+        // Lanes with nothing to insert write their private sink instead, so
+        // the stores need no lane masks.
+        int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
 #pragma unroll
         for (int u = 0; u < kKU; ++u)
-          if (ins[u]) dtab[t[u]] = static_cast<int16_t>(base + u * kThreads + tid);
+          *(ins[u] ? &dtab[t[u]] : sink16) = static_cast<int16_t>(base + u * kThreads + tid);
 #pragma unroll
         for (int u = 0; u < kKU; ++u) ins[u] = false;
       }
@@ -497,13 +500,20 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       for (int u = 0; u < 4; ++u) rw[u] = row_of((sl[u] >= 0 && sl[u] < H) ? sl[u] : 0);
       // The staging choice is uniform: branching once keeps all four token
       // reads of a lane in flight together.
+      // Reads at a clamped index and a select afterwards, rather than reads
+      // under a lane mask: no exec-mask bookkeeping between the four reads.
+      bool okl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) okl[u] = sl[u] >= 0 && sl[u] < H;
       if (a.stage_tokens) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? s_tok[sl[u]] : -1;
+        for (int u = 0; u < 4; ++u) key[u] = s_tok[okl[u] ? sl[u] : 0];
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) key[u] = (sl[u] >= 0 && sl[u] < H) ? tokens[sl[u]] : -1;
+        for (int u = 0; u < 4; ++u) key[u] = tokens[okl[u] ? sl[u] : 0];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[u] = okl[u] ? key[u] : -1;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         act[u] = !kDirect && key[u] >= 0;
@@ -514,13 +524,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         // the slot is a candidate hit when that index's id is this position.
         // Two dependent LDS reads, no search.
         int32_t ti[4], tk[4];
+        bool ok[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          ti[u] = (key[u] >= 0 && static_cast<uint32_t>(key[u]) < a.dtab) ? dtab[key[u]] : -1;
+        for (int u = 0; u < 4; ++u) ok[u] = static_cast<uint32_t>(key[u]) < a.dtab;   // key >= 0 too
 #pragma unroll
-        for (int u = 0; u < 4; ++u) tk[u] = (ti[u] >= 0 && ti[u] < K) ? s_topk[ti[u]] : -2;
+        for (int u = 0; u < 4; ++u) ti[u] = dtab[ok[u] ? key[u] : 0];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) idx[u] = tk[u] == key[u] ? ti[u] : -1;
+        for (int u = 0; u < 4; ++u) ok[u] = ok[u] && ti[u] >= 0 && ti[u] < K;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tk[u] = s_topk[ok[u] ? ti[u] : 0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) idx[u] = (ok[u] && tk[u] == key[u]) ? ti[u] : -1;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -565,16 +579,22 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         prev[u] = atomicCAS(idx[u] >= 0 ? &s_out[idx[u]] : sink32, kPending, idx[u] >= 0 ? rw[u] : 0);
+      // The chunk's hit words (one per 64 positions) leave in one store from
+      // lanes 0-3; words past the row or the segment are not written.
+      uint64_t mw = 0;
+      int nw = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool hit = idx[u] >= 0 && prev[u] == kPending;
         const uint64_t m = __ballot(hit);
         const int p0 = h0 + c0 + u * kWave;
-        if (in_seg_h(c0 + u * kWave) && in_h(p0)) {
-          if (lane == 0) hitpos[p0 >> 6] = m;
+        if (in_seg_h(c0 + u * kWave) && in_h(p0)) {   // uniform, and true for a prefix of u
+          mw = lane == u ? m : mw;
           run += __popcll(m);
+          ++nw;
         }
       }
+      if (lane < nw) hitpos[((h0 + c0) >> 6) + lane] = mw;
     }
     return run;
   };
