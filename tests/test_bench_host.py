@@ -16,3 +16,34 @@ def test_threaded_oracle_baseline_copies_the_same_rows():
 def test_host_threads_is_bounded():
     n = bench.host_threads()
     assert 1 <= n <= 16
+
+
+def _run_bench(*args):
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    return subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
+
+
+def test_unknown_legs_are_refused():
+    r = _run_bench("--only", "headline,nonsense")
+    assert r.returncode == 2 and "nonsense" in r.stderr
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_measured_on():
+    import json
+    import os
+    path = os.path.join(bench.ROOT, "profiles", "swap_copy_traffic.json")
+    entries = json.load(open(path))["workloads"]
+    for name, w in entries.items():
+        want = w["bytes_per_launch"] if w["kernel_sources_sha256_16"] == bench.sources_hash(
+            w["kernel_sources"]) else None
+        assert bench.measured_traffic(name) == want
