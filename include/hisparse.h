@@ -78,7 +78,9 @@ typedef enum {
  * With hs_swap_in_args.paged set, the swap-in keys slots by global pool rows
  * instead of in-request positions:
  *   - Row(r, s) = hot_block_table[r][s / hot_block_size] * hot_block_size
- *                 + s % hot_block_size: a paged hot buffer;
+ *                 + s % hot_block_size: a paged hot buffer. Every row a slot
+ *                 can name must lie in [0, hot_nrows) (precondition); a row
+ *                 outside is never written, and one past int32 reads as -1;
  *   - position t of state row r has global id g: with src_block_table, the
  *     physical block p = src_block_table[r][t / src_block_size] (blocks past
  *     src_num_blocks: none) gives g = p * src_block_size + t % src_block_size

@@ -300,7 +300,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     if constexpr (kPaged) {
       const int32_t q = static_cast<int32_t>(fdiv(static_cast<uint32_t>(s), a.hbs_div));
       const int32_t blk = a.hbt_n ? s_hbt[q] : a.hbt[r * a.hbt_stride + q];
-      return blk * a.hbs + (s - q * a.hbs);
+      // In 64 bits: a table entry too large for an int32 row gives no row.
+      const int64_t row = static_cast<int64_t>(blk) * a.hbs + (s - q * a.hbs);
+      return (row < 0 || row > INT32_MAX) ? -1 : static_cast<int32_t>(row);
     }
     if constexpr (kSlotRows) return srows[s];
     return static_cast<int32_t>(hot_base + s);
