@@ -41,6 +41,7 @@ Also reported in the same JSON line:
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -180,13 +181,19 @@ def run_gpu(cfg, warmup, steps, torch, hs, wdev, kv=False, lead_spin=False, b2b_
     e0, e1 = events()
     if lead_spin:
         torch.cuda._sleep(2_000_000)
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(steps):
-        call(warmup + k, hs.hisparse_swap_in, st.ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
+    # Python's collector stays off while the calls are issued, as timeit does:
+    # a collection pause ahead of the first launches would idle the GPU.
+    gc.disable()
+    try:
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(steps):
+            call(warmup + k, hs.hisparse_swap_in, st.ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    finally:
+        gc.enable()
     us_total = e0.elapsed_time(e1) * 1000.0
     log(f"[bench] {cfg.name}: {steps} timed calls after {warmup} warm-up, {us_total / steps:.1f} us/call")
     cold_rows = int(counts[0].sum().item()) if warmup else 0
