@@ -298,10 +298,11 @@ def run_flushed(cfg, steps, replays, torch, hs, wdev):
 
 def run_tiny(torch, hs, wdev):
     """The tiny workload (B=2, H=64, K=16, 656-byte rows, pinned-host pool):
-    the cold step, then 7 steps, each timed two ways -- the GPU time of the
+    the cold step, then 7 steps, each timed three ways -- the GPU time of the
     call's kernel (the 7 calls queued behind a spin kernel, between two
-    events) and the latency a caller sees (host wall time of the call plus a
-    synchronize, median over the 7 steps)."""
+    events), the latency a caller sees (host wall time of the call plus a
+    synchronize, median over the 7 steps), and the same latency with the call
+    replayed from a HIP graph."""
     from workloads import gen
     cfg = gen.TINY
     r = run_gpu(cfg, 1, cfg.steps - 1, torch, hs, wdev, lead_spin=True)
@@ -320,12 +321,44 @@ def run_tiny(torch, hs, wdev):
         if t:
             lat.append((time.perf_counter() - w0) * 1e6)
     lat.sort()
+    # The same steps with the call captured once in a HIP graph over fixed
+    # input buffers: per step the inputs are written into those buffers (as an
+    # indexer writing there would leave them), then the replay is timed with
+    # a synchronize, like the plain calls above.
+    gst = wdev.DeviceSwapState(cfg)
+    topk_in = torch.zeros_like(tr.topk[0])
+    seq_in = torch.zeros_like(tr.seq[0])
+
+    def gcall(num_real=None):
+        hs.hisparse_swap_in(topk=topk_in, req_rows=tr.rows, seq_lens=seq_in,
+                            slot_tokens=gst.slot_tokens, lru=gst.lru, pool=pool, hot=gst.hot,
+                            out_rows=gst.out, ctx_stride=cfg.ctx, workspace=gst.ws,
+                            miss_counts=gst.counts, num_real=num_real)
+    gcall(num_real=torch.zeros(1, dtype=torch.int32, device="cuda"))   # one-time set-up, no change
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gcall()
+    glat = []
+    for t in range(cfg.steps):
+        topk_in.copy_(tr.topk[t])
+        seq_in.copy_(tr.seq[t])
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        if t:
+            glat.append((time.perf_counter() - w0) * 1e6)
+    assert torch.equal(gst.hot, st.hot) and torch.equal(gst.lru, st.lru), "graph replays diverged"
+    glat.sort()
+    del graph
     n = cfg.steps - 1
     return {"workload": "tiny_swap_in_pinned_host_pool", "batch": cfg.B, "hot_size": cfg.H,
             "top_k": cfg.K, "context": cfg.ctx, "row_bytes": cfg.row_bytes, "steps_after_cold": n,
             "rows_per_call": round(float(r["counts"].sum()) / n, 2),
             "us_per_call_gpu": round(r["us_total"] / n, 2),
             "us_per_call_sync": round(lat[len(lat) // 2], 2),
+            "us_per_call_sync_graph": round(glat[len(glat) // 2], 2),
             "cold_step_us_gpu": round(r["us_cold"], 2),
             "bound": "latency (launch and one workgroup per request)"}
 
