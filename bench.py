@@ -298,11 +298,11 @@ def run_flushed(cfg, steps, replays, torch, hs, wdev):
 
 def run_tiny(torch, hs, wdev):
     """The tiny workload (B=2, H=64, K=16, 656-byte rows, pinned-host pool):
-    the cold step, then 7 steps, each timed three ways -- the GPU time of the
+    the cold step, then 7 steps, each timed four ways -- the GPU time of the
     call's kernel (the 7 calls queued behind a spin kernel, between two
     events), the latency a caller sees (host wall time of the call plus a
-    synchronize, median over the 7 steps), and the same latency with the call
-    replayed from a HIP graph."""
+    synchronize, median over the 7 steps), and the same latency through a
+    SwapInCall and with the call replayed from a HIP graph."""
     from workloads import gen
     cfg = gen.TINY
     r = run_gpu(cfg, 1, cfg.steps - 1, torch, hs, wdev, lead_spin=True)
@@ -321,6 +321,22 @@ def run_tiny(torch, hs, wdev):
         if t:
             lat.append((time.perf_counter() - w0) * 1e6)
     lat.sort()
+    # The same steps through a SwapInCall (every argument checked once; per
+    # step only the step's tensors), timed the same way.
+    pst = wdev.DeviceSwapState(cfg)
+    pcall = hs.SwapInCall(slot_tokens=pst.slot_tokens, lru=pst.lru, pool=pool, hot=pst.hot,
+                          out_rows=pst.out, ctx_stride=cfg.ctx, workspace=pst.ws,
+                          miss_counts=pst.counts)
+    plat = []
+    for t in range(cfg.steps):
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        pcall(tr.topk[t], tr.rows, tr.seq[t])
+        torch.cuda.synchronize()
+        if t:
+            plat.append((time.perf_counter() - w0) * 1e6)
+    assert torch.equal(pst.hot, st.hot) and torch.equal(pst.lru, st.lru), "prepared calls diverged"
+    plat.sort()
     # The same steps with the call captured once in a HIP graph over fixed
     # input buffers: per step the inputs are written into those buffers (as an
     # indexer writing there would leave them), then the replay is timed with
@@ -358,6 +374,7 @@ def run_tiny(torch, hs, wdev):
             "rows_per_call": round(float(r["counts"].sum()) / n, 2),
             "us_per_call_gpu": round(r["us_total"] / n, 2),
             "us_per_call_sync": round(lat[len(lat) // 2], 2),
+            "us_per_call_sync_prepared": round(plat[len(plat) // 2], 2),
             "us_per_call_sync_graph": round(glat[len(glat) // 2], 2),
             "cold_step_us_gpu": round(r["us_cold"], 2),
             "bound": "latency (launch and one workgroup per request)"}

@@ -18,7 +18,7 @@ import torch
 
 from ._lib import EXPORTS, HisparseError, PagedAddressing, SwapInArgs, check, load
 
-__all__ = ["hisparse_swap_in", "hisparse_swap_in_noalloc", "hisparse_resolve", "hisparse_gather_compact",
+__all__ = ["hisparse_swap_in", "hisparse_swap_in_noalloc", "SwapInCall", "hisparse_resolve", "hisparse_gather_compact",
            "hisparse_gather_compact_layers", "transfer_kv_all_layer", "store_kv_cache",
            "hisparse_invalidate_written",
            "swap_in_workspace_layout", "transfer_rows_all_layer", "transfer_host_link", "store_kv_scatter",
@@ -79,7 +79,7 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
                      miss_mask: Optional[torch.Tensor] = None,
                      pool_v: Optional[torch.Tensor] = None, hot_v: Optional[torch.Tensor] = None,
                      paged: Optional[dict] = None, stats: Optional[torch.Tensor] = None,
-                     stream=None, _entry: str = "hisparse_swap_in") -> None:
+                     stream=None, _entry: str = "hisparse_swap_in", _prepare_only: bool = False):
     """One decode-step swap-in (``hisparse_swap_in`` in include/hisparse.h).
 
     topk int32 [B, >=K] (rows may be strided), req_rows/seq_lens int64 [B],
@@ -188,10 +188,79 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
             raise ValueError("stats must be a contiguous 2-element int64 or uint64 tensor")
         a.stats = _dev(stats, stats.dtype, "stats")
     if _entry == "hisparse_swap_in_noalloc":
-        check(_entry, load().hisparse_swap_in_noalloc(ctypes.byref(a), _stream(stream)))
-        return
-    ws = _dev(workspace, torch.uint8, "workspace")
-    check(_entry, getattr(load(), _entry)(ctypes.byref(a), ws, workspace.numel(), _stream(stream)))
+        ws = None
+    else:
+        ws = (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    if _prepare_only:
+        return a, ws
+    _launch(_entry, a, ws, stream)
+
+
+def _launch(entry: str, a: SwapInArgs, ws, stream) -> None:
+    if ws is None:
+        check(entry, load().hisparse_swap_in_noalloc(ctypes.byref(a), _stream(stream)))
+    else:
+        check(entry, getattr(load(), entry)(ctypes.byref(a), ws[0], ws[1], _stream(stream)))
+
+
+class SwapInCall:
+    """A swap-in whose state, pool, hot buffer, outputs, workspace and options
+    are fixed, for a loop of decode steps: every argument is checked once here,
+    and each call checks and passes only the step's own tensors (top-k ids,
+    request rows, sequence lengths), which keeps the host time per step small.
+
+    Takes the keyword arguments of ``hisparse_swap_in`` except ``topk``,
+    ``req_rows``, ``seq_lens`` and ``stream``; ``entry`` names the call
+    (``hisparse_swap_in``, ``hisparse_resolve``, ``hisparse_gather_compact`` or
+    ``hisparse_swap_in_noalloc``, which takes no workspace). The tensors given
+    here must stay alive and keep their storage while the object is used.
+    Call it as ``call(topk, req_rows, seq_lens=None, stream=None)``.
+    """
+
+    def __init__(self, *, entry: str = "hisparse_swap_in", **kw):
+        if entry not in ("hisparse_swap_in", "hisparse_resolve", "hisparse_gather_compact",
+                         "hisparse_swap_in_noalloc"):
+            raise ValueError(f"unknown entry {entry}")
+        for k in ("topk", "req_rows", "seq_lens", "stream", "_entry"):
+            if k in kw:
+                raise ValueError(f"{k} is given per call")
+        if entry == "hisparse_swap_in_noalloc":
+            if "workspace" in kw:
+                raise ValueError("hisparse_swap_in_noalloc takes no workspace")
+            kw["workspace"] = None
+        out = kw["out_rows"]
+        if out.dim() != 2:
+            raise ValueError("out_rows must be [B, K]")
+        B, K = out.shape
+        dev = out.device
+        self._B, self._K, self._entry = B, K, entry
+        self._paged = kw.get("paged") is not None
+        # placeholder step tensors: the full argument checks run once on them
+        ph_topk = torch.zeros((B, K), dtype=torch.int32, device=dev)
+        ph_rows = torch.zeros(B, dtype=torch.int64, device=dev)
+        ph_seq = torch.zeros(B, dtype=torch.int64, device=dev)
+        self._args, self._ws = hisparse_swap_in(topk=ph_topk, req_rows=ph_rows, seq_lens=ph_seq,
+                                                _entry=entry, _prepare_only=True, **kw)
+        self._keep = kw
+
+    def __call__(self, topk: torch.Tensor, req_rows: torch.Tensor,
+                 seq_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+        B, K = self._B, self._K
+        if topk.dim() != 2 or topk.shape[0] != B or topk.shape[1] < K or topk.stride(1) != 1:
+            raise ValueError("topk must be [B, >=K] with contiguous columns")
+        _vec(req_rows, B, "req_rows")
+        a = self._args
+        a.topk_ids = _dev(topk, torch.int32, "topk")
+        a.topk_stride = topk.stride(0)
+        a.req_rows = _dev(req_rows, torch.int64, "req_rows")
+        if seq_lens is None:
+            if not self._paged:
+                raise ValueError("seq_lens is required without paged addressing")
+            a.seq_lens = None
+        else:
+            _vec(seq_lens, B, "seq_lens")
+            a.seq_lens = _dev(seq_lens, torch.int64, "seq_lens")
+        _launch(self._entry, a, self._ws, stream)
 
 
 def hisparse_swap_in_noalloc(**kw) -> None:

@@ -69,3 +69,13 @@ def test_state_reset_rejects_mismatched_rows():
         hs.hisparse_state_reset(slot_tokens=torch.zeros((R, S_r), dtype=torch.int32),
                                 lru=torch.zeros((R + 1, H), dtype=torch.int16),
                                 rows=torch.zeros(2, dtype=torch.int64))
+
+
+def test_prepared_call_rejects_step_arguments_and_unknown_entries():
+    import sparse_attention_kv_hisparse_amd as hs
+    with pytest.raises(ValueError, match="given per call"):
+        hs.SwapInCall(topk=torch.zeros((1, 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="unknown entry"):
+        hs.SwapInCall(entry="hisparse_something")
+    with pytest.raises(ValueError, match="no workspace"):
+        hs.SwapInCall(entry="hisparse_swap_in_noalloc", workspace=torch.zeros(8, dtype=torch.uint8))
