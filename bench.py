@@ -86,6 +86,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU seconds of oracle work for cpu_baseline (whole replays "
                         "of the headline's timed steps)")
+    p.add_argument("--copy-row-sizes", action="store_true",
+                   help="the device-pool trace with other row sizes (512, 640, 656, 672, 768 B): "
+                        "copy kernel time per call, one JSON object per size")
     p.add_argument("--copy-ceilings", action="store_true",
                    help="only measure the library's row transfer on scattered rows of several "
                         "sizes (pinned host -> HBM and HBM -> HBM), one JSON line each, then exit")
@@ -673,6 +676,22 @@ def calibrate(torch, hs):
                       "bytes_written_per_launch": n, "launches": 3}), flush=True)
 
 
+def copy_row_sizes(torch, hs, wdev):
+    """The device-pool trace (B=128, K=2048, H=4096, HBM pool) with rows of
+    512, 640, 656, 672 and 768 bytes: the copy kernel's mean launch time over
+    the 31 timed steps (pass 2: the copies back to back), to set the
+    workload's 656-byte rows against rows that are whole 128-byte lines."""
+    from workloads import gen
+    for rb in (512, 640, 656, 672, 768):
+        cfg = gen.DEVPOOL.with_(row_bytes=rb)
+        r = run_gpu(cfg, 1, 31, torch, hs, wdev)
+        rows = float(r["counts"].sum()) / 31
+        us = r["us_copy"] / 31
+        print(json.dumps({"row_bytes": rb, "rows_per_call": rows, "us_copy_kernel": round(us, 2),
+                          "GBps_read_write": round(rows * rb * 2 / us / 1e3, 1),
+                          "us_resolve_kernel": round(r["us_resolve"] / 31, 2)}), flush=True)
+
+
 def copy_ceilings(torch, hs):
     """What the copy engine reaches on scattered rows, by row size and bytes per
     launch: transfer_rows_all_layer with one layer, rows drawn without
@@ -867,6 +886,9 @@ def main():
         return
     if args.copy_ceilings:
         copy_ceilings(torch, hs)
+        return
+    if args.copy_row_sizes:
+        copy_row_sizes(torch, hs, wdev)
         return
     cfg = gen.DSV32
 
