@@ -1158,7 +1158,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
       return set_error(HS_EINVAL, "slot_rows / pool_rows are not used with paged addressing");
     if (!pa->hot_block_table || pa->hot_block_size <= 0)
       return set_error(HS_EINVAL, "paged addressing needs a hot block table and block size");
-    if (pa->hot_table_stride * pa->hot_block_size < a->H)
+    if (pa->hot_table_stride < (static_cast<int64_t>(a->H) + pa->hot_block_size - 1) / pa->hot_block_size)
       return set_error(HS_EINVAL, "the hot block table does not cover H slots");
     if (pa->src_block_table &&
         (pa->src_block_size <= 0 || pa->src_num_blocks < 0 || pa->src_table_stride < pa->src_num_blocks))
@@ -1186,7 +1186,7 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   if (!aligned(a->pool, 4) || !aligned(a->hot, 4))
     return set_error(HS_EINVAL, "pool and hot must be 4-byte aligned");
   if (!a->slot_rows && !pg) {
-    if (a->R * a->S_r > 0x7fffffffll)
+    if (a->R > 0x7fffffffll / a->S_r)   // S_r >= H + 1 >= 2
       return set_error(HS_ERANGE, "R*S_r exceeds int32 hot-row indices");
     if (a->hot_nrows < a->R * a->S_r)
       return set_error(HS_EINVAL, "hot_nrows < R*S_r with flat regions");
