@@ -17,11 +17,13 @@
 //    from ballot + mbcnt plus a running count, and only the 16 per-wave
 //    totals cross waves, so there is no block-wide scan and no wave64 scan
 //    window to get wrong (the pages' per-warp chunk scan needs one).
-//  * Membership (is this slot's token one of the pending ids?) is an LDS
-//    table built per call: a direct-address table of top-k indices over
-//    positions when the layout is flat and the table fits, else a bucketed
-//    hash (Knuth's multiplicative hash, rebuilt with a salted hash when a
-//    chain runs long). No result depends on which one runs.
+//  * Membership (which top-k ids some slot holds) goes through an LDS table
+//    built per call. When the layout is flat and the table fits, it is a
+//    direct-address table over positions naming the slot that holds each
+//    one, and every id is looked up once. Otherwise the pending ids go into a
+//    bucketed hash (Knuth's multiplicative hash, rebuilt with a salted hash
+//    when a chain runs long) and every slot's token is probed. No result
+//    depends on which one runs.
 //  * swap_copy_kernel: the misses, published as a compact (pool row, hot row)
 //    list in the caller's workspace, are copied by many workgroups per
 //    request (1024-lane ones, two per CU, from an HBM pool; 256-lane ones
@@ -29,8 +31,8 @@
 //    the only hand-off between the two, so no workgroup ever waits on another.
 //  * With a pinned-host pool the resolve kernel copies its own request's rows
 //    as well (phase 5): the host link is full with one workgroup per request.
-//    Each lane issues its first chunk's read right after the probe, while the
-//    victims and outputs are still being worked out.
+//    Each lane issues its first chunk's read as soon as the misses are known,
+//    while the victims and outputs are still being worked out.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -45,7 +47,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-static_assert(kWaves % 4 == 0, "per-wave counts are summed four at a time");
 constexpr int kFuseUnroll = 12;  // chunks per lane per round, fused copy
 constexpr int kEarlyChunks = 1;  // fused copy: chunks per lane loaded before the victims
 // Entries per lane per pass: top-k phases take two (K = 2048 fills a pass of
@@ -163,7 +164,7 @@ __host__ __device__ inline uint32_t wave_segment(int32_t n) {
 
 // dtab != 0: the direct-address table of dtab int16 entries replaces the hash
 // (keys, indices and counts); the region still holds the fused copy's miss
-// list (12 bytes per miss) after the probe.
+// list (12 bytes per miss) after the lookup.
 __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T, bool stage_tokens,
                                                 uint32_t hbt_n, uint32_t sbt_n, uint32_t dtab) {
   const uint32_t hwords = kWaves * wave_segment(H) / 64;
@@ -187,10 +188,10 @@ __host__ __device__ inline LdsLayout lds_layout(int32_t K, int32_t H, uint32_t T
   l.hitpos = o; o = align_up(o + 8 * hwords, 16);
   l.missw = o;  o = align_up(o + 8 * kwords, 16);
   l.wtot = o;   o = align_up(o + 4 * (2 * (kWaves + 1) + 2), 16);
-  l.seed = o;   o = align_up(o + (dtab ? 4 * kWaves : 16), 16);   // hash salt / per-wave pending ids
+  l.seed = o;   o = align_up(o + 16, 16);                     // the salted hash's salt
   l.dummy = o;  o = align_up(o + 8 * kThreads, 16);            // per-lane CAS sink
   l.lru = o;    o = align_up(o + 2 * static_cast<uint32_t>(H), 16);
-  l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order
+  l.nlru = o;   o = align_up(o + 2 * static_cast<uint32_t>(H), 16);   // new LRU order; before it, pos_of
   l.victim = o; o = align_up(o + 2 * static_cast<uint32_t>(K), 16);
   l.hbt = o;    o = align_up(o + 4 * hbt_n, 16);                 // paged: hot block table row
   l.sbt = o;    o = align_up(o + 4 * sbt_n, 16);                 // paged: source block table row
@@ -210,6 +211,19 @@ __device__ __forceinline__ bool any_of(const bool (&v)[N]) {
 __device__ __forceinline__ int rank_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+}
+
+// Sum of v over the 64 lanes of a wave, in every lane: an inclusive scan by
+// DPP row shifts (within rows of 16) and row broadcasts (across rows), then
+// lane 63. Called with all lanes active.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Resolve request b (one workgroup): outputs, state updates and the miss list
@@ -239,9 +253,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   int32_t* out = a.out_rows + static_cast<int64_t>(b) * K;
 
   int32_t* hkey = reinterpret_cast<int32_t*>(lds + lay.hash);
-  // Direct-address table (kDirect): entry t holds the top-k index of pending
-  // position t. Never cleared: a lookup checks that the index it reads names
-  // an entry holding that very position, so stale contents never match.
+  // Direct-address table (kDirect): entry t holds the slot of resident
+  // position t. Never cleared: a lookup checks the token of the slot it reads,
+  // so stale contents never match.
   int16_t* dtab = reinterpret_cast<int16_t*>(lds + lay.hash);
   int16_t* hidx = reinterpret_cast<int16_t*>(lds + lay.hidx);
   uint32_t* bcnt = reinterpret_cast<uint32_t*>(lds + lay.bcnt);
@@ -266,9 +280,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   unsigned long long* sink64 = reinterpret_cast<unsigned long long*>(lds + lay.dummy) + tid;
   int32_t* sink32 = reinterpret_cast<int32_t*>(sink64);
   uint32_t* sinku = reinterpret_cast<uint32_t*>(sink64);
-  // Direct plans: the pending ids each wave classified, written (not added,
-  // so nothing clears them first) where hashed plans keep their salt.
-  int32_t* wpend = reinterpret_cast<int32_t*>(lds + lay.seed);
   const uint32_t bmask = a.T / 4 - 1;       // buckets - 1
   const uint32_t bshift = a.shift + 2;      // top log2(buckets) bits
   uint32_t* s_salt = reinterpret_cast<uint32_t*>(lds + lay.seed);
@@ -315,10 +326,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
 
   // ---- stage: ids, the LRU row and the slot-token row -----------------------
   // The first kKU * 1024 ids, the first 256 LRU positions of this wave's
-  // segment (kept in registers for the probe and the victim step, which work
-  // on the same positions) and kHU * 1024 slot tokens land with all loads in
-  // flight at once; the hash table is cleared while they are outstanding.
-  // Longer rows follow in batches of four per lane.
+  // segment (kept in registers for the probe or the lookup and the victim
+  // step, which work on the same positions) and kHU * 1024 slot tokens land
+  // with all loads in flight at once; a hash table is cleared while they are
+  // outstanding. Longer rows follow in batches of four per lane.
   const int segH = static_cast<int>(wave_segment(H));
   const int segK = static_cast<int>(wave_segment(K));
   const int h0 = wave * segH;
@@ -334,7 +345,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   auto in_seg_k = [&](int off) { return kExact || off < segK; };
   int32_t vi[kKU];
   int16_t vl[4];   // LRU entries at h0 + u*64 + lane
-  const bool early_classify = kDirect && K <= kKU * kThreads;   // uniform
 
   // ---- 1. classify ids; bind the newest token; insert pending ids ----------
   // SGLang page: the newest token goes to newest_slot (= H), every other id is
@@ -362,7 +372,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // first run writes outside LDS survives into the second.
   auto classify_insert = [&](auto salted_tag, uint32_t salt) {
     constexpr bool kSalted = decltype(salted_tag)::value;
-    int wave_pending = 0;
     for (int base = 0; base < K; base += kKU * kThreads) {
       int32_t t[kKU], o[kKU];
       uint32_t bk[kKU];
@@ -423,21 +432,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       int npend = 0;
 #pragma unroll
       for (int u = 0; u < kKU; ++u) npend += __popcll(__ballot(ins[u]));
-      if constexpr (kDirect) {
-        // A pending position t (< lim <= ctx_stride = table size) records its
-        // top-k index; ids are unique, so no two entries meet.
-        // Lanes with nothing to insert write their private sink instead, so
-        // the stores need no lane masks.
-        int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
-#pragma unroll
-        for (int u = 0; u < kKU; ++u)
-          *(ins[u] ? &dtab[t[u]] : sink16) = static_cast<int16_t>(base + u * kThreads + tid);
-#pragma unroll
-        for (int u = 0; u < kKU; ++u) ins[u] = false;
-      }
 #pragma unroll
       for (int u = 0; u < kKU; ++u)
-        bk[u] = kDirect ? 0u : (kSalted ? bucket_salted(t[u], salt, bshift) : bucket_knuth(t[u], bshift));
+        bk[u] = kSalted ? bucket_salted(t[u], salt, bshift) : bucket_knuth(t[u], bshift);
       // Each pending id takes the next entry of its home bucket with one LDS
       // atomicAdd on the bucket's count; a full bucket passes it on to the next
       // bucket (linear probing over buckets). A lookup stops at the first bucket
@@ -445,7 +442,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       // table is at most half full, so insertion terminates.
       const int nu = (K - base + kThreads - 1) / kThreads;   // live u, uniform
       int trips = 0;
-      while (!kDirect && __ballot(any_of(ins)) != 0) {
+      while (__ballot(any_of(ins)) != 0) {
         if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
           if (lane == 0) *s_retry = 1;
           break;
@@ -469,15 +466,11 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         const int i = base + u * kThreads + tid;
         if (in_k(i)) s_out[i] = o[u];
       }
-      if constexpr (kDirect) wave_pending += npend;
-      else if (lane == 0 && npend) atomicAdd(s_pending, npend);
-    }
-    if constexpr (kDirect) {
-      if (lane == 0) wpend[wave] = wave_pending;
+      if (lane == 0 && npend) atomicAdd(s_pending, npend);
     }
   };
 
-  // ---- 2. LRU scan: probe each slot's token -------------------------------
+  // ---- 2. LRU scan (hashed plans): probe each slot's token ----------------
   // Wave w walks its own 64-aligned segment of LRU positions. A slot whose
   // token is pending is a hit and serves that top-k entry; the first claimant
   // wins (a second slot with the same token -- corrupt state -- stays
@@ -518,29 +511,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       for (int u = 0; u < 4; ++u) key[u] = okl[u] ? key[u] : -1;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        act[u] = !kDirect && key[u] >= 0;
+        act[u] = key[u] >= 0;
         idx[u] = -1;
-      }
-      if constexpr (kDirect) {
-        // Direct table: the entry of the slot's position names a top-k index;
-        // the slot is a candidate hit when that index's id is this position.
-        // Two dependent LDS reads, no search.
-        int32_t ti[4], tk[4];
-        bool ok[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ok[u] = static_cast<uint32_t>(key[u]) < a.dtab;   // key >= 0 too
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ti[u] = dtab[ok[u] ? key[u] : 0];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ok[u] = ok[u] && ti[u] >= 0 && ti[u] < K;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) tk[u] = s_topk[ok[u] ? ti[u] : 0];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) idx[u] = (ok[u] && tk[u] == key[u]) ? ti[u] : -1;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        bk[u] = kDirect ? 0u : (kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift));
+        bk[u] = kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift);
       // Branch-free lookup step over one bucket (four keys, 16 bytes) per
       // query. Buckets fill in entry order, so a bucket whose last key is empty
       // is not full and ends a miss. Ends when no lane of the wave is still
@@ -548,7 +524,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       // The bucket's four top-k indices (8 bytes) are read beside its keys, so
       // a found key's index needs no further LDS round trip.
       int trips = 0;
-      while (!kDirect && __ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
+      while (__ballot(act[0] | act[1] | act[2] | act[3]) != 0) {
         if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
           if (lane == 0) *s_retry = 1;
           break;
@@ -601,6 +577,182 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     return run;
   };
 
+  // Either plan below yields the hits among the LRU positions before this
+  // wave's segment and in all, and M, the misses (pending ids that take a slot).
+  int hits = 0, hits_before = 0, M = 0;
+  // Direct plans keep the wave's first top-k chunks in registers from the
+  // lookup to the write-out: the ids (vi), their outputs and miss words.
+  [[maybe_unused]] int32_t vo[kKU];
+  [[maybe_unused]] uint64_t vmw[kKU];
+  if constexpr (kDirect) {
+    // ---- 1-2, direct plans: tables of the resident tokens, one lookup per id --
+    // While the rows land, every slot 0..H-1 writes its index into the table
+    // entry of the position it holds, and every LRU position its index into
+    // the entry of the slot it names (pos_of). A pending id is then a hit when
+    // its entry names a slot that holds it: two dependent LDS reads (entry,
+    // then the slot's token and LRU position side by side) per id, K lookups
+    // instead of H probes. Neither table is cleared; the token check rejects
+    // stale entries. The hit sets its LRU position's bit in the hit words, so
+    // the victim step finds hits in LRU order without another pass.
+    int16_t* pos_of = nlru;   // free until the new order is built
+    int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
+    int32_t vt[kHU];
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int i = k0 + u * kWave + lane;
+      vi[u] = (in_seg_k(u * kWave) && in_k(i)) ? ids[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      vl[u] = (in_seg_h(u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(-1);
+    }
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const int x = u * kThreads + tid;
+      vt[u] = in_h(x) ? tokens[x] : -1;
+    }
+    const int nwh = (H + kWave - 1) / kWave;    // hit words
+    for (int i = tid; i < nwh; i += kThreads) hitpos[i] = 0;
+    if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
+    for (int c0 = kKU * kWave; c0 < segK; c0 += kKU * kWave) {   // K > 2048
+      int32_t w[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int i = k0 + c0 + u * kWave + lane;
+        w[u] = (in_seg_k(c0 + u * kWave) && in_k(i)) ? ids[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int i = k0 + c0 + u * kWave + lane;
+        if (in_seg_k(c0 + u * kWave) && in_k(i)) s_topk[i] = w[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = h0 + u * kWave + lane;
+      if (in_seg_h(u * kWave) && in_h(p))
+        *((static_cast<uint16_t>(vl[u]) < static_cast<uint32_t>(H)) ? &pos_of[vl[u]] : sink16) =
+            static_cast<int16_t>(p);
+    }
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const int x = u * kThreads + tid;
+      if (in_h(x)) {
+        if (a.stage_tokens) s_tok[x] = vt[u];
+        *((static_cast<uint32_t>(vt[u]) < a.dtab) ? &dtab[vt[u]] : sink16) = static_cast<int16_t>(x);
+      }
+    }
+    for (int c0 = 4 * kWave; c0 < segH; c0 += 4 * kWave) {    // H > 4096
+      int16_t wl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = h0 + c0 + u * kWave + lane;
+        wl[u] = (in_seg_h(c0 + u * kWave) && in_h(p)) ? lru[p] : static_cast<int16_t>(-1);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = h0 + c0 + u * kWave + lane;
+        if (in_seg_h(c0 + u * kWave) && in_h(p)) {
+          s_lru[p] = wl[u];
+          *((static_cast<uint16_t>(wl[u]) < static_cast<uint32_t>(H)) ? &pos_of[wl[u]] : sink16) =
+              static_cast<int16_t>(p);
+        }
+      }
+    }
+    for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
+      int32_t wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        wt[u] = in_h(x) ? tokens[x] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = base + u * kThreads + tid;
+        if (in_h(x)) {
+          if (a.stage_tokens) s_tok[x] = wt[u];
+          *((static_cast<uint32_t>(wt[u]) < a.dtab) ? &dtab[wt[u]] : sink16) = static_cast<int16_t>(x);
+        }
+      }
+    }
+    __syncthreads();
+
+    // Lookup: each wave classifies and looks up its own segment of top-k
+    // entries, records its miss words and adds its miss total to the later
+    // waves' prefixes.
+    int mrun = 0;
+    for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
+      int32_t t[kKU], o[kKU], sl[kKU], tk[kKU], pp[kKU];
+      bool inr[kKU], pend[kKU], ok[kKU], hit[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int i = k0 + c0 + u * kWave + lane;
+        inr[u] = in_seg_k(c0 + u * kWave) && in_k(i);
+        t[u] = c0 == 0 ? vi[u] : (inr[u] ? s_topk[i] : 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const bool valid = inr[u] && static_cast<uint32_t>(t[u]) < lim;
+        const bool newest = valid && t[u] == newest_t;
+        pend[u] = valid && !newest;
+        o[u] = !valid ? -1 : (newest ? row_newest : kPending);
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) sl[u] = dtab[pend[u] ? t[u] : 0];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) ok[u] = pend[u] && static_cast<uint32_t>(sl[u]) < static_cast<uint32_t>(H);
+      if (a.stage_tokens) {
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) tk[u] = s_tok[ok[u] ? sl[u] : 0];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) tk[u] = tokens[ok[u] ? sl[u] : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) pp[u] = pos_of[ok[u] ? sl[u] : 0];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u)
+        hit[u] = ok[u] && tk[u] == t[u] && static_cast<uint32_t>(pp[u]) < static_cast<uint32_t>(H);
+#pragma unroll
+      for (int u = 0; u < kKU; ++u)
+        atomicOr(hit[u] ? reinterpret_cast<unsigned long long*>(&hitpos[pp[u] >> 6]) : sink64,
+                 hit[u] ? 1ull << (pp[u] & 63) : 0ull);
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) o[u] = hit[u] ? row_of(sl[u]) : o[u];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const uint64_t mm = __ballot(pend[u] && !hit[u]);
+        const int q = k0 + c0 + u * kWave;
+        if (in_seg_k(c0 + u * kWave) && in_k(q)) {   // uniform
+          if (lane == 0) missw[q >> 6] = mm;
+          mrun += __popcll(mm);
+        }
+        if (c0 == 0) {
+          vo[u] = o[u];
+          vmw[u] = mm;
+        } else if (inr[u]) {
+          s_out[q + lane] = o[u];
+        }
+      }
+    }
+    if (lane > wave && lane <= kWaves && mrun) atomicAdd(&pre_miss[lane], mrun);
+    __syncthreads();
+    // Hits before this wave's LRU segment, and in all, from the hit words:
+    // both counts packed in one word (each at most H <= 32768) and summed
+    // over the wave.
+    uint32_t acc = 0;
+    const int wbeg = h0 >> 6;
+    for (int w = lane; w < nwh; w += kWave) {
+      const uint32_t c = static_cast<uint32_t>(__popcll(hitpos[w]));
+      acc += (c << 16) + (w < wbeg ? c : 0u);
+    }
+    acc = wave_sum(acc);
+    hits = static_cast<int>(acc >> 16);
+    hits_before = static_cast<int>(acc & 0xffffu);
+    M = pre_miss[kWaves];
+  } else {
+  // ---- stage (hashed plans) ----------------------------------------------------
   {
     int32_t vt[kHU];
 #pragma unroll
@@ -618,7 +770,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int x = u * kThreads + tid;
       vt[u] = (a.stage_tokens && in_h(x)) ? tokens[x] : 0;
     }
-    if constexpr (!kDirect) {
+    {
       // Keys start empty (-1, never a token id) and bucket counts at 0.
       u32x4* k4 = reinterpret_cast<u32x4*>(hkey);
       for (uint32_t i = tid; i < a.T / 4; i += kThreads) k4[i] = u32x4{~0u, ~0u, ~0u, ~0u};
@@ -641,10 +793,6 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int x = u * kThreads + tid;
       if (in_k(x)) s_topk[x] = vi[u];
     }
-    // With a direct table (nothing to clear) and one pass of ids, the ids
-    // are classified and recorded as soon as they land, while the LRU and
-    // token rows are still on their way, and one barrier less is needed.
-    if (early_classify) classify_insert(std::false_type{}, 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = h0 + u * kWave + lane;
@@ -700,31 +848,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     }
   }
   __syncthreads();
-  // All pending ids of the request.
-  auto sum_pending = [&]() -> int {
-    if constexpr (!kDirect) return *s_pending;
-    const int4* w4 = reinterpret_cast<const int4*>(wpend);
-    int n = 0;
-#pragma unroll
-    for (int q = 0; q < kWaves / 4; ++q) {
-      const int4 v = w4[q];
-      n += v.x + v.y + v.z + v.w;
-    }
-    return n;
-  };
-  if (!early_classify) {
-    classify_insert(std::false_type{}, 0u);
-    __syncthreads();
-  }
-  int pending_n = sum_pending();
+  classify_insert(std::false_type{}, 0u);
+  __syncthreads();
+  int pending_n = *s_pending;
   int run = *s_retry == 0 ? probe(std::false_type{}, 0u) : 0;
   // Wave w adds its total to the prefix of every later wave and to the grand
   // total: one LDS atomic per lane, no scan after the barrier.
   if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
   __syncthreads();
-  int hits = pre_hit[kWaves];
-  int hits_before = pre_hit[wave];
-  if (!kDirect && *s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
+  hits = pre_hit[kWaves];
+  hits_before = pre_hit[wave];
+  if (*s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
     // Fallback: once every lane has read the flag, clear the table, its
     // counts and the cross-wave counters (the flag with them), then run
     // classification and the scan again with the salted hash.
@@ -743,13 +877,15 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     const uint32_t salt = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*s_salt));
     classify_insert(std::true_type{}, salt);
     __syncthreads();
-    pending_n = sum_pending();
+    pending_n = *s_pending;
     run = probe(std::true_type{}, salt);
     if (lane > wave && lane <= kWaves && run) atomicAdd(&pre_hit[lane], run);
     __syncthreads();
     hits = pre_hit[kWaves];
     hits_before = pre_hit[wave];
   }
+  M = pending_n - hits;    // misses (<= E because K <= H)
+  }  // hashed plans
 
   // ---- 3. miss words, (host pools) early row loads, victims, new LRU order ---
   // New order: stale evictables, then the M victims (they receive the misses,
@@ -757,13 +893,14 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   // position's rank among hits is the hits of earlier waves, plus this wave's
   // earlier chunks, plus the hit lanes below it.
   const int E = H - hits;            // evictable slots
-  const int M = pending_n - hits;    // misses (<= E because K <= H)
-  // The fused copy's list (pool row, hot row) in miss order, kept in the key
-  // and index arrays, which are free since the probe phase (6T >= 12K bytes).
+  // The fused copy's list (pool row, hot row) in miss order, kept in the table
+  // region, which is free once the probe or the lookup is done (the layout
+  // gives it at least 12K bytes).
   int64_t* l_src = reinterpret_cast<int64_t*>(lds + lay.hash);
   int32_t* l_dst = reinterpret_cast<int32_t*>(lds + lay.hash + 8u * static_cast<uint32_t>(K));
-  // An id still pending after the probe is a miss: each wave records its
-  // segment's miss words and adds its miss total to the later waves' prefixes.
+  // Hashed plans: an id still pending after the probe is a miss. Each wave
+  // records its segment's miss words and adds its miss total to the later
+  // waves' prefixes (the direct plans' lookup has done so already).
   auto miss_words = [&]() {
     int mrun = 0;
     for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
@@ -797,8 +934,10 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   [[maybe_unused]] typename CE::T ev[kEarlyChunks > 0 ? kEarlyChunks : 1];
   if constexpr (kEarlyCopy) {
     if (early) {
-      miss_words();
-      __syncthreads();
+      if constexpr (!kDirect) {
+        miss_words();
+        __syncthreads();
+      }
       int mrun = pre_miss[wave];
       for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
         uint64_t wd[kKU];
@@ -808,8 +947,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
           const int q = k0 + c0 + u * kWave;
           const int i = q + lane;
           const bool in = in_seg_k(c0 + u * kWave) && in_k(q);
-          wd[u] = in ? missw[q >> 6] : 0;
-          t[u] = (in && in_k(i)) ? s_topk[i] : 0;
+          wd[u] = in ? ((kDirect && c0 == 0) ? vmw[u] : missw[q >> 6]) : 0;
+          t[u] = (in && in_k(i)) ? ((kDirect && c0 == 0) ? vi[u] : s_topk[i]) : 0;
         }
 #pragma unroll
         for (int u = 0; u < kKU; ++u) {
@@ -840,7 +979,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       }
     }
   }
-  run = hits_before;
+  int run = hits_before;
   int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
   for (int c0 = 0; c0 < segH && in_h(h0 + c0); c0 += 4 * kWave) {
     // The chunk's four hit words arrive in one LDS read (lanes 0-3) and are
@@ -883,7 +1022,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       run += __popcll(wd[u]);
     }
   }
-  if (!early) miss_words();
+  if (!kDirect && !early) miss_words();
   __syncthreads();
 
   // ---- 4. misses in top-k order take victims; outputs; copy list -----------
@@ -903,9 +1042,9 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       const int q = k0 + c0 + u * kWave;
       const int i = q + lane;
       const bool in = in_seg_k(c0 + u * kWave) && in_k(q);
-      wd[u] = in ? missw[q >> 6] : 0;
-      so[u] = (in && in_k(i)) ? s_out[i] : 0;
-      t[u] = (in && in_k(i)) ? s_topk[i] : 0;
+      wd[u] = in ? ((kDirect && c0 == 0) ? vmw[u] : missw[q >> 6]) : 0;
+      so[u] = (in && in_k(i)) ? ((kDirect && c0 == 0) ? vo[u] : s_out[i]) : 0;
+      t[u] = (in && in_k(i)) ? ((kDirect && c0 == 0) ? vi[u] : s_topk[i]) : 0;
     }
     int m[kKU], v[kKU];
 #pragma unroll

@@ -10,7 +10,8 @@ entries past the buffer or negative -- and check, after three calls, that the
 guard zones around the hot buffer, the state rows, the outputs and the miss
 counts still hold their fill pattern, that miss counts stay in [0, K], and
 (flat layout) that every output is -1 or a row of its own request's region.
-The oracle is not involved: it rejects such state."""
+Two cases also repeat top-k ids within a row (the ids of a row are unique by
+precondition). The oracle is not involved: it rejects such state."""
 
 import numpy as np
 import pytest
@@ -42,19 +43,22 @@ def _guards_hold(back, rows, fill, name):
     assert (b[:G] == fill).all() and (b[G + rows:] == fill).all(), f"{name}: a guard row was written"
 
 
-@pytest.mark.parametrize("ctx,kind,paged", [
-    (2000, "host", False),      # direct table, fused copy
-    (2000, "device", False),    # direct table, wide copy
-    (70000, "host", False),     # hashed plan
-    (3000, "host", True),       # paged: hot block table entries outside the buffer
-    (3000, "device", True),
-], ids=["direct_host", "direct_device", "hashed_host", "paged_host", "paged_device"])
-def test_broken_state_stays_in_bounds(ctx, kind, paged):
+@pytest.mark.parametrize("ctx,kind,paged,dup", [
+    (2000, "host", False, False),      # direct table, fused copy
+    (2000, "device", False, False),    # direct table, wide copy
+    (70000, "host", False, False),     # hashed plan
+    (3000, "host", True, False),       # paged: hot block table entries outside the buffer
+    (3000, "device", True, False),
+    (2000, "host", False, True),       # repeated top-k ids, direct table
+    (70000, "device", False, True),    # repeated top-k ids, hashed plan
+], ids=["direct_host", "direct_device", "hashed_host", "paged_host", "paged_device",
+        "direct_dup_ids", "hashed_dup_ids"])
+def test_broken_state_stays_in_bounds(ctx, kind, paged, dup):
     import sparse_attention_kv_hisparse_amd as hs
     R, B, H, K, rb = 6, 4, 256, 64, 32
     S_r = H + 1
-    print(f"  broken state: ctx={ctx} pool={kind} paged={paged}", flush=True)
-    rng = np.random.default_rng(ctx + 7 * paged + (kind == "device"))
+    print(f"  broken state: ctx={ctx} pool={kind} paged={paged} dup={dup}", flush=True)
+    rng = np.random.default_rng(ctx + 7 * paged + (kind == "device") + 13 * dup)
     hot_nrows = R * S_r
     hot_back, hot = _guarded(hot_nrows, rb, torch.uint8, 0xA5)
     tok_back, tokens = _guarded(R, S_r, torch.int32, 0x5A5A5A5A)
@@ -93,6 +97,8 @@ def test_broken_state_stays_in_bounds(ctx, kind, paged):
             if len(row) < K:
                 row = np.concatenate([row, np.setdiff1d(np.arange(ctx), row)[:K - len(row)]])
             topk[b] = rng.permutation(row)
+            if dup:   # an eighth of the row repeats other entries of it
+                topk[b][K // 2:K // 2 + K // 8] = topk[b][:K // 8]
         hs.hisparse_swap_in(topk=torch.as_tensor(topk).cuda(), req_rows=req_rows,
                             seq_lens=None if paged else seq, slot_tokens=tokens, lru=lru,
                             pool=pool, hot=hot, out_rows=out, ctx_stride=0 if paged else ctx,

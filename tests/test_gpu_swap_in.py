@@ -87,9 +87,15 @@ def _small(**kw):
     dict(H=4096, K=4096, ctx=70000, B=2, steps=3, row_bytes=16),
     # a direct table that fits only with the slot-token row left in HBM
     dict(H=16384, K=2048, ctx=32768, B=2, steps=3),
+    # direct tables with the guard-free (exact) tiles past one pass: more LRU
+    # positions and slot tokens than one pass of the workgroup stages, and
+    # more top-k entries than a wave keeps in registers
+    dict(H=8192, K=2048, ctx=16384, B=2, steps=3),
+    dict(H=8192, K=4096, ctx=16384, B=2, steps=3, row_bytes=16, pool_kind="device"),
 ], ids=["base", "K_eq_H", "ragged", "bigH", "degenerate", "rb4", "rb132", "devpool", "single",
         "unstaged_host", "unstaged_dev", "many_host", "many_dev", "max_H", "max_K",
-        "hashed_two_passes", "hashed_max_K", "direct_unstaged"])
+        "hashed_two_passes", "hashed_max_K", "direct_unstaged", "direct_exact_bigH",
+        "direct_exact_K4096"])
 def test_edge_traces(kw):
     h = _harness()
     cfg = _small(**kw)
