@@ -594,11 +594,40 @@ def run_scatter(torch, hs, n=8192, rb=656, cache_rows=1 << 20, reps=5):
     return res
 
 
+def code_text(src):
+    """C++ source with its comments removed and every run of white space
+    collapsed to one blank: what the compiler sees of it, so that an edit to a
+    comment does not count as a change of the kernel. Comment markers inside
+    string and character literals are not comments."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_hash(files):
+    """Hash of the code (comments and layout aside) of the given sources."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, f), encoding="utf-8").read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

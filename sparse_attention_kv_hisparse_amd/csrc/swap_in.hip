@@ -32,7 +32,7 @@
 //  * With a pinned-host pool the resolve kernel copies its own request's rows
 //    as well (phase 5): the host link is full with one workgroup per request.
 //    Each lane issues its first chunk's read as soon as the misses are known,
-//    while the victims and outputs are still being worked out.
+//    before the victims and outputs are worked out.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -924,8 +924,12 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   };
   // Host pools: the pool row of every miss is known now; only its hot row
   // waits for the victims. The first kEarlyChunks chunks of every lane are
-  // loaded here, in the fused copy's order, so the host link is already busy
-  // while the victims and outputs are worked out. One per lane: with a whole
+  // loaded here, in the fused copy's order, so the host link gets this
+  // request's first reads before the victims and outputs are worked out. The
+  // workgroup pauses until they are back: the generated code waits for each
+  // load at once (under its branch the loaded value and the no-load path
+  // share a register), and with no branch phase 4's global stores queue
+  // behind the outstanding host reads instead. One per lane: with a whole
   // round (kFuseUnroll per lane) outstanding the link moved less and the
   // call got no faster; one per lane saves ~2% on the DeepSeek-V3.2-like step.
   constexpr bool kEarlyCopy = kEarlyChunks > 0 && kCopyW != 0 && !kSlotRows && !kPoolRows;

@@ -47,3 +47,16 @@ def test_traffic_is_reported_only_for_the_sources_it_was_measured_on():
         want = w["bytes_per_launch"] if w["kernel_sources_sha256_16"] == bench.sources_hash(
             w["kernel_sources"]) else None
         assert bench.measured_traffic(name) == want
+
+
+def test_source_hash_ignores_comments_and_layout_but_not_code(tmp_path, monkeypatch):
+    src = 'int f(int x) {  // doubles x\n  /* note */ return 2 * x; }\nconst char* s = "a // b";\n'
+    (tmp_path / "a.hip").write_text(src)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.sources_hash(["a.hip"])
+    (tmp_path / "a.hip").write_text(src.replace("doubles x", "twice x").replace("  /* note */", ""))
+    assert bench.sources_hash(["a.hip"]) == h0
+    (tmp_path / "a.hip").write_text(src.replace('"a // b"', '"a // c"'))
+    assert bench.sources_hash(["a.hip"]) != h0      # text inside a literal is code
+    (tmp_path / "a.hip").write_text(src.replace("2 * x", "3 * x"))
+    assert bench.sources_hash(["a.hip"]) != h0
