@@ -2,8 +2,8 @@
 oracle, bit for bit: random hot, source and resident block tables (null
 blocks, ids past the pool, padding rows), global-id slot keys, attention
 indices, host and device pools, the fused and the split paths, K+V, a hot
-block table too long to stage in LDS, and hisparse_invalidate_written between
-calls."""
+block table too long to stage in LDS, hisparse_invalidate_written between
+calls, and a dozen cases with sizes and options drawn from fixed seeds."""
 
 import zlib
 
@@ -40,6 +40,27 @@ CASES = [
     # LDS, so slot rows are read from HBM and the fused copy loads no chunk early
     ("host_fused_hbt_in_hbm", 4, 3, 3000, 500, 6000, 656, "host", False, False, 1),
 ]
+
+
+def _random_cases(n):
+    """Cases drawn from fixed seeds: sizes off the 64-slot and 1024-lane grids,
+    random block sizes (the tables come from _random_tables), pool kind, the
+    split path and K+V."""
+    out = []
+    for i in range(n):
+        rng = np.random.default_rng(9_100 + i)
+        H = int(rng.choice([1, 5, 63, 64, 100, 300, 1000, 2047]))
+        K = int(rng.integers(1, H + 1))
+        R = int(rng.integers(1, 9))
+        B = int(rng.integers(1, R + 1))
+        ctx = int(rng.integers(K + 2, 4 * K + 2_000))
+        rb = int(rng.choice([4, 16, 132, 656]))
+        out.append((f"rand{i}", R, B, H, K, ctx, rb, str(rng.choice(["host", "device"])),
+                    bool(rng.random() < 0.3), bool(rng.random() < 0.3), None))
+    return out
+
+
+CASES += _random_cases(12)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
