@@ -207,6 +207,16 @@ __device__ __forceinline__ bool any_of(const bool (&v)[N]) {
   return r;
 }
 
+// A read of LDS through an address-space-3 pointer. Where one branch reads a
+// table staged in LDS and the other the same table in HBM, plain (generic)
+// loads let the compiler merge the two into one flat load through a selected
+// address: a vector-memory round trip for the LDS side as well, waited for
+// with the global loads. Typed LDS loads keep the two branches apart.
+template <class T>
+__device__ __forceinline__ T lds_read(const T* p) {
+  return *(const __attribute__((address_space(3))) T*)p;
+}
+
 // popcount of the bits of a 64-bit wave mask held by lanes below this one.
 __device__ __forceinline__ int rank_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -310,7 +320,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   auto row_of = [&](int32_t s) -> int32_t {
     if constexpr (kPaged) {
       const int32_t q = static_cast<int32_t>(fdiv(static_cast<uint32_t>(s), a.hbs_div));
-      const int32_t blk = a.hbt_n ? s_hbt[q] : a.hbt[r * a.hbt_stride + q];
+      const int32_t blk = a.hbt_n ? lds_read(&s_hbt[q]) : a.hbt[r * a.hbt_stride + q];
       // In 64 bits: a table entry too large for an int32 row gives no row.
       const int64_t row = static_cast<int64_t>(blk) * a.hbs + (s - q * a.hbs);
       return (row < 0 || row > INT32_MAX) ? -1 : static_cast<int32_t>(row);
@@ -398,7 +408,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
             if (a.sbt) {
               g = -1;
               if (tt >= 0 && sq < a.sbt_nblocks) {
-                const int32_t pb = a.sbt_n ? reinterpret_cast<const int32_t*>(lds + lay.sbt)[sq]
+                const int32_t pb = a.sbt_n ? lds_read(reinterpret_cast<const int32_t*>(lds + lay.sbt) + sq)
                                            : a.sbt[r * a.sbt_stride + sq];
                 if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
               }
@@ -502,7 +512,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       for (int u = 0; u < 4; ++u) okl[u] = sl[u] >= 0 && sl[u] < H;
       if (a.stage_tokens) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) key[u] = s_tok[okl[u] ? sl[u] : 0];
+        for (int u = 0; u < 4; ++u) key[u] = lds_read(&s_tok[okl[u] ? sl[u] : 0]);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) key[u] = tokens[okl[u] ? sl[u] : 0];
@@ -704,7 +714,7 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
       for (int u = 0; u < kKU; ++u) ok[u] = pend[u] && static_cast<uint32_t>(sl[u]) < static_cast<uint32_t>(H);
       if (a.stage_tokens) {
 #pragma unroll
-        for (int u = 0; u < kKU; ++u) tk[u] = s_tok[ok[u] ? sl[u] : 0];
+        for (int u = 0; u < kKU; ++u) tk[u] = lds_read(&s_tok[ok[u] ? sl[u] : 0]);
       } else {
 #pragma unroll
         for (int u = 0; u < kKU; ++u) tk[u] = tokens[ok[u] ? sl[u] : 0];
