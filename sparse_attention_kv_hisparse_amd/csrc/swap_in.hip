@@ -139,7 +139,7 @@ struct SwapArgs {
   int32_t* dst;       // [B, K] hot row of miss m (-1 = skip)
   int32_t B, K, H;
   int64_t S_r, R;
-  uint32_t T;         // hash entries, power of two >= 2K (0 with a direct table)
+  uint32_t T;         // hash entries, power of two >= 2K, or >= 2H for the slots' keys (0 with a direct table)
   uint32_t dtab;      // direct-address table entries (ctx_stride), or 0 for the hash
   uint32_t shift;     // 32 - log2(T)
   int32_t stage_tokens;
@@ -375,6 +375,35 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     if (L >= 1 && L - 1 < l64) newest_t = static_cast<int32_t>(L - 1);
     row_newest = row_of(H);
   }
+  // vLLM page, first phase (paged addressing): position tt -> global id g
+  // through the source block table (a physical block of 0 or below has no
+  // row, nor has a global id past the pool), and the resident row res when
+  // the resident table serves the position; -1 for none. Block and offset by
+  // multiply-shift division (a negative tt lands past every table).
+  [[maybe_unused]] auto translate = [&](int32_t tt, int64_t& g, int64_t& res) {
+    g = tt;
+    res = -1;
+    if (a.sbt) {
+      g = -1;
+      const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
+      if (tt >= 0 && sq < a.sbt_nblocks) {
+        const int32_t pb = a.sbt_n ? lds_read(reinterpret_cast<const int32_t*>(lds + lay.sbt) + sq)
+                                   : a.sbt[r * a.sbt_stride + sq];
+        if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
+      }
+    }
+    if (g >= a.pool_nrows) g = -1;
+    if (a.rbt) {
+      const int32_t rq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.rbs_div));
+      if (tt >= 0 && rq < a.rbt_nblocks) {
+        const int32_t pb = a.rbt[r * a.rbt_stride + rq];
+        if (pb != a.r_null && pb >= 0) {
+          res = static_cast<int64_t>(pb) * a.rbs + (tt - rq * a.rbs);
+          if (res > INT32_MAX) res = -1;
+        }
+      }
+    }
+  };
   // Classification + inserts (1) and the LRU scan (2), written once and run
   // with Knuth's hash. If an insert or a lookup runs past kTripLimit buckets,
   // the workgroup clears the table and its counts and runs both again with
@@ -398,30 +427,8 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
           // vLLM page, first phase: position -> global id through the source
           // block table (a physical block of 0 or below has no row), and a
           // resident row when the resident table holds the position.
-          const int32_t tt = t[u];
           int64_t g = -1, res = -1;
-          if (in_k(i)) {
-            g = tt;
-            // Block and offset by multiply-shift division (tt < 2^31).
-            const int32_t sq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.sbs_div));
-            const int32_t rq = static_cast<int32_t>(fdiv(static_cast<uint32_t>(tt), a.rbs_div));
-            if (a.sbt) {
-              g = -1;
-              if (tt >= 0 && sq < a.sbt_nblocks) {
-                const int32_t pb = a.sbt_n ? lds_read(reinterpret_cast<const int32_t*>(lds + lay.sbt) + sq)
-                                           : a.sbt[r * a.sbt_stride + sq];
-                if (pb > 0) g = static_cast<int64_t>(pb) * a.sbs + (tt - sq * a.sbs);
-              }
-            }
-            if (g >= a.pool_nrows) g = -1;
-            if (a.rbt && tt >= 0 && rq < a.rbt_nblocks) {
-              const int32_t pb = a.rbt[r * a.rbt_stride + rq];
-              if (pb != a.r_null && pb >= 0) {
-                res = static_cast<int64_t>(pb) * a.rbs + (tt - rq * a.rbs);
-                if (res > INT32_MAX) res = -1;
-              }
-            }
-          }
+          if (in_k(i)) translate(t[u], g, res);
           ins[u] = in_k(i) && res < 0 && g >= 0;
           o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
           t[u] = static_cast<int32_t>(g);            // the key from here on
@@ -595,15 +602,21 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
   [[maybe_unused]] int32_t vo[kKU];
   [[maybe_unused]] uint64_t vmw[kKU];
   if constexpr (kDirect) {
-    // ---- 1-2, direct plans: tables of the resident tokens, one lookup per id --
-    // While the rows land, every slot 0..H-1 writes its index into the table
-    // entry of the position it holds, and every LRU position its index into
-    // the entry of the slot it names (pos_of). A pending id is then a hit when
-    // its entry names a slot that holds it: two dependent LDS reads (entry,
-    // then the slot's token and LRU position side by side) per id, K lookups
-    // instead of H probes. Neither table is cleared; the token check rejects
-    // stale entries. The hit sets its LRU position's bit in the hit words, so
-    // the victim step finds hits in LRU order without another pass.
+    // ---- 1-2, lookup plans: a table of the resident slots, one lookup per id --
+    // Flat layout (the direct table): while the rows land, every slot 0..H-1
+    // writes its index into the table entry of the position it holds. A
+    // pending id is then a hit when its entry names a slot that holds it: two
+    // dependent LDS reads (entry, then the slot's token and LRU position side
+    // by side) per id, K lookups instead of H probes. The table is never
+    // cleared; the token check rejects stale entries.
+    // Paged addressing (keys are global ids, which span the whole pool): the
+    // slots' keys go into the bucketed hash instead (key -> slot), and each
+    // pending id's global id is looked up there. A chain past kTripLimit
+    // buckets, in an insert or a lookup, rebuilds the hash with the salted
+    // hash, as the hashed plans do.
+    // Either way every LRU position writes its index into the entry of the
+    // slot it names (pos_of), and a hit sets its LRU position's bit in the hit
+    // words, so the victim step finds hits in LRU order without another pass.
     int16_t* pos_of = nlru;   // free until the new order is built
     int16_t* sink16 = reinterpret_cast<int16_t*>(sink64);
     int32_t vt[kHU];
@@ -625,6 +638,17 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
     const int nwh = (H + kWave - 1) / kWave;    // hit words
     for (int i = tid; i < nwh; i += kThreads) hitpos[i] = 0;
     if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
+    if constexpr (kPaged) {
+      // The request's hot and source block table rows (every slot -> row and
+      // position -> global id translation then stays in LDS), and the
+      // bucket counts of the key hash, cleared before the first insert.
+      int32_t* hb = reinterpret_cast<int32_t*>(lds + lay.hbt);
+      for (int i = tid; i < a.hbt_n; i += kThreads) hb[i] = a.hbt[r * a.hbt_stride + i];
+      int32_t* sb = reinterpret_cast<int32_t*>(lds + lay.sbt);
+      for (int i = tid; i < a.sbt_n; i += kThreads) sb[i] = a.sbt[r * a.sbt_stride + i];
+      u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+      for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     for (int c0 = kKU * kWave; c0 < segK; c0 += kKU * kWave) {   // K > 2048
       int32_t w[kKU];
 #pragma unroll
@@ -645,12 +669,14 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         *((static_cast<uint16_t>(vl[u]) < static_cast<uint32_t>(H)) ? &pos_of[vl[u]] : sink16) =
             static_cast<int16_t>(p);
     }
+    if constexpr (!kPaged) {
 #pragma unroll
-    for (int u = 0; u < kHU; ++u) {
-      const int x = u * kThreads + tid;
-      if (in_h(x)) {
-        if (a.stage_tokens) s_tok[x] = vt[u];
-        *((static_cast<uint32_t>(vt[u]) < a.dtab) ? &dtab[vt[u]] : sink16) = static_cast<int16_t>(x);
+      for (int u = 0; u < kHU; ++u) {
+        const int x = u * kThreads + tid;
+        if (in_h(x)) {
+          if (a.stage_tokens) s_tok[x] = vt[u];
+          *((static_cast<uint32_t>(vt[u]) < a.dtab) ? &dtab[vt[u]] : sink16) = static_cast<int16_t>(x);
+        }
       }
     }
     for (int c0 = 4 * kWave; c0 < segH; c0 += 4 * kWave) {    // H > 4096
@@ -670,84 +696,220 @@ __device__ void resolve(const SwapArgs& a, int b, unsigned char* lds, const LdsL
         }
       }
     }
-    for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
-      int32_t wt[4];
+    if constexpr (!kPaged) {
+      for (int base = kHU * kThreads; base < H; base += 4 * kThreads) {
+        int32_t wt[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = base + u * kThreads + tid;
-        wt[u] = in_h(x) ? tokens[x] : -1;
-      }
+        for (int u = 0; u < 4; ++u) {
+          const int x = base + u * kThreads + tid;
+          wt[u] = in_h(x) ? tokens[x] : -1;
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = base + u * kThreads + tid;
-        if (in_h(x)) {
-          if (a.stage_tokens) s_tok[x] = wt[u];
-          *((static_cast<uint32_t>(wt[u]) < a.dtab) ? &dtab[wt[u]] : sink16) = static_cast<int16_t>(x);
+        for (int u = 0; u < 4; ++u) {
+          const int x = base + u * kThreads + tid;
+          if (in_h(x)) {
+            if (a.stage_tokens) s_tok[x] = wt[u];
+            *((static_cast<uint32_t>(wt[u]) < a.dtab) ? &dtab[wt[u]] : sink16) = static_cast<int16_t>(x);
+          }
         }
       }
     }
     __syncthreads();
 
+    // Paged: every slot's key into the hash. A slot takes the next entry of
+    // its key's home bucket with one LDS atomicAdd on the bucket's count; a
+    // full bucket passes the key on to the next bucket.
+    [[maybe_unused]] auto insert_keys = [&](auto salted_tag, uint32_t salt) {
+      constexpr bool kSalted = decltype(salted_tag)::value;
+      for (int base = 0; base < H; base += kHU * kThreads) {
+        int32_t key[kHU];
+        uint32_t bk[kHU];
+        bool ins[kHU];
+#pragma unroll
+        for (int u = 0; u < kHU; ++u) {
+          const int x = base + u * kThreads + tid;
+          key[u] = (!kSalted && base == 0) ? vt[u] : (in_h(x) ? tokens[x] : -1);
+          ins[u] = in_h(x) && key[u] >= 0;
+          bk[u] = kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift);
+        }
+        int trips = 0;
+        while (__ballot(any_of(ins)) != 0) {
+          if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
+            if (lane == 0) *s_retry = 1;
+            break;
+          }
+          uint32_t pq[kHU];
+#pragma unroll
+          for (int u = 0; u < kHU; ++u) pq[u] = atomicAdd(ins[u] ? &bcnt[bk[u]] : sinku, 1u);
+#pragma unroll
+          for (int u = 0; u < kHU; ++u) {
+            if (ins[u] && pq[u] < 4) {
+              hkey[4 * bk[u] + pq[u]] = key[u];
+              hidx[4 * bk[u] + pq[u]] = static_cast<int16_t>(base + u * kThreads + tid);
+            }
+            const bool full = ins[u] && pq[u] >= 4;
+            bk[u] = full ? ((bk[u] + 1) & bmask) : bk[u];
+            ins[u] = full;
+          }
+        }
+      }
+    };
+
     // Lookup: each wave classifies and looks up its own segment of top-k
     // entries, records its miss words and adds its miss total to the later
-    // waves' prefixes.
-    int mrun = 0;
-    for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
-      int32_t t[kKU], o[kKU], sl[kKU], tk[kKU], pp[kKU];
-      bool inr[kKU], pend[kKU], ok[kKU], hit[kKU];
+    // waves' prefixes. Paged: the ids come from global memory again on the
+    // salted pass, and the key (global id) replaces the id in vi / s_topk
+    // for the write-out.
+    auto lookup = [&](auto salted_tag, uint32_t salt) {
+      constexpr bool kSalted = decltype(salted_tag)::value;
+      int mrun = 0;
+      for (int c0 = 0; c0 < segK && in_k(k0 + c0); c0 += kKU * kWave) {
+        int32_t t[kKU], key[kKU], o[kKU], sl[kKU], tk[kKU], pp[kKU];
+        bool inr[kKU], pend[kKU], ok[kKU], hit[kKU];
 #pragma unroll
-      for (int u = 0; u < kKU; ++u) {
-        const int i = k0 + c0 + u * kWave + lane;
-        inr[u] = in_seg_k(c0 + u * kWave) && in_k(i);
-        t[u] = c0 == 0 ? vi[u] : (inr[u] ? s_topk[i] : 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) {
-        const bool valid = inr[u] && static_cast<uint32_t>(t[u]) < lim;
-        const bool newest = valid && t[u] == newest_t;
-        pend[u] = valid && !newest;
-        o[u] = !valid ? -1 : (newest ? row_newest : kPending);
-      }
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) sl[u] = dtab[pend[u] ? t[u] : 0];
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) ok[u] = pend[u] && static_cast<uint32_t>(sl[u]) < static_cast<uint32_t>(H);
-      if (a.stage_tokens) {
-#pragma unroll
-        for (int u = 0; u < kKU; ++u) tk[u] = lds_read(&s_tok[ok[u] ? sl[u] : 0]);
-      } else {
-#pragma unroll
-        for (int u = 0; u < kKU; ++u) tk[u] = tokens[ok[u] ? sl[u] : 0];
-      }
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) pp[u] = pos_of[ok[u] ? sl[u] : 0];
-#pragma unroll
-      for (int u = 0; u < kKU; ++u)
-        hit[u] = ok[u] && tk[u] == t[u] && static_cast<uint32_t>(pp[u]) < static_cast<uint32_t>(H);
-#pragma unroll
-      for (int u = 0; u < kKU; ++u)
-        atomicOr(hit[u] ? reinterpret_cast<unsigned long long*>(&hitpos[pp[u] >> 6]) : sink64,
-                 hit[u] ? 1ull << (pp[u] & 63) : 0ull);
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) o[u] = hit[u] ? row_of(sl[u]) : o[u];
-#pragma unroll
-      for (int u = 0; u < kKU; ++u) {
-        const uint64_t mm = __ballot(pend[u] && !hit[u]);
-        const int q = k0 + c0 + u * kWave;
-        if (in_seg_k(c0 + u * kWave) && in_k(q)) {   // uniform
-          if (lane == 0) missw[q >> 6] = mm;
-          mrun += __popcll(mm);
+        for (int u = 0; u < kKU; ++u) {
+          const int i = k0 + c0 + u * kWave + lane;
+          inr[u] = in_seg_k(c0 + u * kWave) && in_k(i);
+          t[u] = kSalted ? (inr[u] ? ids[i] : 0) : (c0 == 0 ? vi[u] : (inr[u] ? s_topk[i] : 0));
         }
-        if (c0 == 0) {
-          vo[u] = o[u];
-          vmw[u] = mm;
-        } else if (inr[u]) {
-          s_out[q + lane] = o[u];
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          if constexpr (kPaged) {
+            int64_t g = -1, res = -1;
+            if (inr[u]) translate(t[u], g, res);
+            pend[u] = inr[u] && res < 0 && g >= 0;
+            o[u] = res >= 0 ? static_cast<int32_t>(res) : (g >= 0 ? kPending : -1);
+            key[u] = static_cast<int32_t>(g);
+          } else {
+            const bool valid = inr[u] && static_cast<uint32_t>(t[u]) < lim;
+            const bool newest = valid && t[u] == newest_t;
+            pend[u] = valid && !newest;
+            o[u] = !valid ? -1 : (newest ? row_newest : kPending);
+            key[u] = t[u];
+          }
+        }
+        if constexpr (kPaged) {
+          // Branch-free steps over one bucket per query: its four keys, its
+          // count (entries past the count are not this call's) and its four
+          // slot indices, read side by side. Ends when no lane of the wave is
+          // still searching.
+          bool act[kKU];
+          uint32_t bk[kKU];
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) {
+            act[u] = pend[u];
+            sl[u] = -1;
+            bk[u] = kSalted ? bucket_salted(key[u], salt, bshift) : bucket_knuth(key[u], bshift);
+          }
+          int trips = 0;
+          while (__ballot(any_of(act)) != 0) {
+            if (!kSalted && ++trips > kTripLimit) {   // clustered: fall back (uniform per wave)
+              if (lane == 0) *s_retry = 1;
+              break;
+            }
+            u32x4 kv[kKU];
+            uint64_t iv[kKU];
+            uint32_t cn[kKU];
+#pragma unroll
+            for (int u = 0; u < kKU; ++u) {
+              kv[u] = reinterpret_cast<const u32x4*>(hkey)[bk[u]];
+              iv[u] = reinterpret_cast<const uint64_t*>(hidx)[bk[u]];
+              cn[u] = bcnt[bk[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < kKU; ++u) {
+              const int32_t kk = key[u];
+              const bool m0 = cn[u] > 0 && static_cast<int32_t>(kv[u].x) == kk;
+              const bool m1 = cn[u] > 1 && static_cast<int32_t>(kv[u].y) == kk;
+              const bool m2 = cn[u] > 2 && static_cast<int32_t>(kv[u].z) == kk;
+              const bool m3 = cn[u] > 3 && static_cast<int32_t>(kv[u].w) == kk;
+              const bool found = m0 | m1 | m2 | m3;
+              const uint32_t j = m0 ? 0u : (m1 ? 1u : (m2 ? 2u : 3u));
+              const int ii = static_cast<int16_t>(static_cast<uint32_t>(iv[u] >> (16 * j)) & 0xffffu);
+              sl[u] = (act[u] && found) ? ii : sl[u];
+              act[u] = act[u] && !found && cn[u] >= 4;
+              bk[u] = act[u] ? ((bk[u] + 1) & bmask) : bk[u];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) {
+            ok[u] = pend[u] && static_cast<uint32_t>(sl[u]) < static_cast<uint32_t>(H);
+            tk[u] = key[u];   // the hash holds exact keys: no token check
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) sl[u] = dtab[pend[u] ? t[u] : 0];
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) ok[u] = pend[u] && static_cast<uint32_t>(sl[u]) < static_cast<uint32_t>(H);
+          if (a.stage_tokens) {
+#pragma unroll
+            for (int u = 0; u < kKU; ++u) tk[u] = lds_read(&s_tok[ok[u] ? sl[u] : 0]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < kKU; ++u) tk[u] = tokens[ok[u] ? sl[u] : 0];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) pp[u] = pos_of[ok[u] ? sl[u] : 0];
+#pragma unroll
+        for (int u = 0; u < kKU; ++u)
+          hit[u] = ok[u] && tk[u] == key[u] && static_cast<uint32_t>(pp[u]) < static_cast<uint32_t>(H);
+#pragma unroll
+        for (int u = 0; u < kKU; ++u)
+          atomicOr(hit[u] ? reinterpret_cast<unsigned long long*>(&hitpos[pp[u] >> 6]) : sink64,
+                   hit[u] ? 1ull << (pp[u] & 63) : 0ull);
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) o[u] = hit[u] ? row_of(sl[u]) : o[u];
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          const uint64_t mm = __ballot(pend[u] && !hit[u]);
+          const int q = k0 + c0 + u * kWave;
+          if (in_seg_k(c0 + u * kWave) && in_k(q)) {   // uniform
+            if (lane == 0) missw[q >> 6] = mm;
+            mrun += __popcll(mm);
+          }
+          if (c0 == 0) {
+            vo[u] = o[u];
+            vmw[u] = mm;
+            if constexpr (kPaged) vi[u] = key[u];
+          } else if (inr[u]) {
+            s_out[q + lane] = o[u];
+            if constexpr (kPaged) s_topk[q + lane] = key[u];
+          }
         }
       }
+      if (lane > wave && lane <= kWaves && mrun) atomicAdd(&pre_miss[lane], mrun);
+    };
+
+    if constexpr (kPaged) {
+      insert_keys(std::false_type{}, 0u);
+      __syncthreads();
+      if (*s_retry == 0) lookup(std::false_type{}, 0u);
+      __syncthreads();
+      if (*s_retry != 0) {   // uniform: nothing writes the flag before the barrier below
+        // Fallback: once every lane has read the flag, clear the counts, the
+        // hit words and the cross-wave counters (the flag with them), then
+        // insert and look up again with the salted hash.
+        __syncthreads();
+        u32x4* c4 = reinterpret_cast<u32x4*>(bcnt);
+        for (uint32_t i = tid; i < a.T / 16; i += kThreads) c4[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = tid; i < nwh; i += kThreads) hitpos[i] = 0;
+        if (tid < 2 * (kWaves + 1) + 2) wtot[tid] = 0;
+        if (tid == 0) {   // the salt, fresh per workgroup and call
+          const uint64_t z = static_cast<uint64_t>(clock64()) ^ (static_cast<uint64_t>(b) << 40);
+          *s_salt = static_cast<uint32_t>(mix64(z + 0x9E3779B97F4A7C15ull));
+        }
+        __syncthreads();
+        const uint32_t salt = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*s_salt));
+        insert_keys(std::true_type{}, salt);
+        __syncthreads();
+        lookup(std::true_type{}, salt);
+        __syncthreads();
+      }
+    } else {
+      lookup(std::false_type{}, 0u);
+      __syncthreads();
     }
-    if (lane > wave && lane <= kWaves && mrun) atomicAdd(&pre_miss[lane], mrun);
-    __syncthreads();
     // Hits before this wave's LRU segment, and in all, from the hit words:
     // both counts packed in one word (each at most H <= 32768) and summed
     // over the wave.
@@ -1244,9 +1406,13 @@ int allow_lds(int device, const void* fn, uint32_t bytes) {
 // The resolve kernel for the given tables and fused copy width (0 = none).
 // `exact` (K a multiple of kKU * 1024, H of kHU * 1024) selects the
 // instantiation without tile guards, for the flat and the paged layouts;
-// `direct` the direct-address table instead of the hash, for the flat layout.
+// `direct` a lookup per id instead of a probe per slot: the direct-address
+// table for the flat layout, the hash of the slots' keys for paged addressing.
 template <int kW>
 const void* pick_resolve(bool slot_rows, bool pool_rows, bool paged, bool exact, bool direct) {
+  if (paged && direct)   // the paged key hash, looked up once per id
+    return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, true, true>)
+                 : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, false, true>);
   if (paged)
     return exact ? reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, true, false>)
                  : reinterpret_cast<const void*>(&resolve_kernel<false, false, kW, true, false, false>);
@@ -1366,12 +1532,15 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   if (rc != HS_OK) return rc;
   // LDS plan, best first. Flat layout with positions below ctx_stride as
   // keys: a direct-address table of ctx_stride int16 entries when it fits,
-  // with the slot-token row staged, then without. Otherwise a quarter-full
-  // hash table with the slot-token row staged; a half-full table with the row
-  // staged; then the same without staging (tokens gathered from HBM). Shorter
-  // probe chains matter most: a wave's probe loop runs as long as its longest
+  // with the slot-token row staged, then without. Paged addressing: a hash
+  // of the slots' keys, a quarter full, then half full (both looked up once
+  // per id). Otherwise a quarter-full hash of the pending ids with the
+  // slot-token row staged; a half-full one with the row staged; then the same
+  // without staging (tokens gathered from HBM), each probed with every slot.
+  // Shorter chains matter most: a wave's loop runs as long as its longest
   // chain.
   const uint32_t k2 = 2u * static_cast<uint32_t>(a->K) < 64u ? 64u : 2u * static_cast<uint32_t>(a->K);
+  const uint32_t h2 = 2u * static_cast<uint32_t>(a->H) < 64u ? 64u : 2u * static_cast<uint32_t>(a->H);
   // Paged: the request's hot block table row (one entry per block of slots)
   // and source block table row go to LDS when they are small; larger rows
   // are read from HBM.
@@ -1383,14 +1552,16 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   }
   const bool flat = !pg && !a->slot_rows && !a->pool_rows;
   const uint32_t dtab_n = (flat && a->ctx_stride <= (1 << 16)) ? static_cast<uint32_t>(a->ctx_stride) : 0u;
-  const uint32_t plans_T[6] = {0u, 0u, pow2_at_least(2 * k2), pow2_at_least(k2), pow2_at_least(2 * k2),
-                               pow2_at_least(k2)};
-  const uint32_t plans_D[6] = {dtab_n, dtab_n, 0u, 0u, 0u, 0u};
-  const bool plans_stage[6] = {true, false, true, true, false, false};
+  constexpr int kPlans = 8;
+  const uint32_t plans_T[kPlans] = {0u, 0u, pow2_at_least(2 * h2), pow2_at_least(h2), pow2_at_least(2 * k2),
+                                    pow2_at_least(k2), pow2_at_least(2 * k2), pow2_at_least(k2)};
+  const uint32_t plans_D[kPlans] = {dtab_n, dtab_n, 0u, 0u, 0u, 0u, 0u, 0u};
+  const bool plans_stage[kPlans] = {true, false, false, false, true, true, false, false};
   int plan = -1;
   LdsLayout lay{};
-  for (int i = 0; i < 6 && plan < 0; ++i) {
+  for (int i = 0; i < kPlans && plan < 0; ++i) {
     if (i < 2 && dtab_n == 0) continue;
+    if ((i == 2 || i == 3) && !pg) continue;
     lay = lds_layout(a->K, a->H, plans_T[i], plans_stage[i], hbt_n, sbt_n, plans_D[i]);
     if (static_cast<int>(lay.total) <= di.max_lds) plan = i;
   }
@@ -1400,11 +1571,12 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   const uint32_t T = plans_T[plan];
   const uint32_t dtab = plans_D[plan];
   const bool stage = plans_stage[plan];
+  const bool lookup = plan < 4;   // the direct table or the paged key hash
   uint32_t log2T = 0;
   while ((1u << log2T) < T) ++log2T;
   const bool sr = a->slot_rows != nullptr, prw = a->pool_rows != nullptr;
   const bool exact = a->K % (kKU * kThreads) == 0 && a->H % (kHU * kThreads) == 0;
-  const void* resolve_fn = pick_resolve<0>(sr, prw, pg, exact, dtab != 0);
+  const void* resolve_fn = pick_resolve<0>(sr, prw, pg, exact, lookup);
   if (lay.total > 65536) {
     rc = allow_lds(di.device, resolve_fn, lay.total);
     if (rc != HS_OK) return rc;
@@ -1443,8 +1615,8 @@ int prepare(const hs_swap_in_args* a, void* workspace, size_t workspace_bytes, P
   // kernel, which spreads every request over many CUs.
   const void* fused_fn = nullptr;
   if (attr.type == hipMemoryTypeHost) {
-    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg, exact, dtab != 0)
-                       : pick_resolve<4>(sr, prw, pg, exact, dtab != 0);
+    fused_fn = W == 16 ? pick_resolve<16>(sr, prw, pg, exact, lookup)
+                       : pick_resolve<4>(sr, prw, pg, exact, lookup);
     if (lay.total > 65536) {
       rc = allow_lds(di.device, fused_fn, lay.total);
       if (rc != HS_OK) return rc;

@@ -61,6 +61,8 @@ def _random_cases(n):
 
 
 CASES += _random_cases(12)
+# more slots than one pass of the workgroup inserts into the paged key hash
+CASES.append(("host_key_hash_two_passes", 2, 2, 4500, 200, 12000, 16, "host", False, False, None))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -194,6 +196,62 @@ def test_paged_full_size_dsv32():
         assert np.array_equal(_np(out), o_out), f"step {t}: out_rows"
         assert np.array_equal(_np(counts), o_cnt), f"step {t}: miss_counts"
         assert np.array_equal(_np(att), o_att), f"step {t}: attention_indices"
+        assert np.array_equal(_np(keys), o_keys), f"step {t}: slot keys"
+        assert np.array_equal(_np(lru), o_lru), f"step {t}: lru"
+        assert np.array_equal(_np(hot), o_hot), f"step {t}: hot buffer"
+
+
+def test_paged_keys_clustered_in_the_kernel_hash():
+    """Paged addressing without a source table (a position is its global id),
+    with ids that share the top bits of Knuth's multiplicative hash: the slots'
+    keys then crowd a few buckets of the key hash, inserts and lookups run past
+    the kernel's trip limit, the workgroup rebuilds the hash with the salted
+    hash, and every call still matches the oracle."""
+    import sparse_attention_kv_hisparse_amd as hs
+    R = B = 2
+    H, K, hb, rb = 1024, 512, 16, 16
+    ids = np.arange(200_000, dtype=np.uint64)
+    # the key hash has pow2(4H) entries in buckets of four: H buckets, picked
+    # by the top log2(H) = 10 bits of id * 2654435761 (mod 2^32)
+    home = ((ids * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - 10)
+    cand = ids[home < 8].astype(np.int64)          # ids in 8 of the 1024 buckets
+    pool_nrows = int(cand.max()) + 1
+    rng = np.random.default_rng(5)
+    nhb = H // hb
+    hot_tab = rng.permutation(R * nhb).astype(np.int32).reshape(R, nhb)
+    cfg = gen.SwapConfig("paged_cluster", B=1, H=H, K=K, ctx=pool_nrows, row_bytes=rb, steps=1,
+                         rho=0.5, dist="uniform", pool_kind="host", seed=63)
+    pool = wdev.make_pool(cfg)
+    keys = torch.full((R, H + 1), -1, dtype=torch.int32, device="cuda")
+    lru = torch.tensor(np.tile(np.arange(H, dtype=np.int16), (R, 1)), device="cuda")
+    hot = torch.zeros((R * nhb * hb, rb), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
+    paged = {"hot_block_table": torch.as_tensor(hot_tab).cuda(), "hot_block_size": hb}
+    o_keys = np.full((R, H + 1), -1, np.int32)
+    o_lru = np.tile(np.arange(H, dtype=np.int16), (R, 1))
+    o_hot = np.zeros((R * nhb * hb, rb), np.uint8)
+    rows = np.arange(B, dtype=np.int64)
+    prev = None
+    for t in range(4):
+        topk = np.stack([rng.choice(cand, size=K, replace=False) for _ in range(B)]).astype(np.int32)
+        if prev is not None:
+            topk[:, :K // 2] = prev[:, :K // 2]
+            for b in range(B):
+                fresh = np.setdiff1d(cand, prev[b])
+                topk[b, K // 2:] = rng.choice(fresh, size=K - K // 2, replace=False)
+        prev = topk.copy()
+        hs.hisparse_swap_in(topk=torch.as_tensor(topk).cuda(), req_rows=torch.as_tensor(rows).cuda(),
+                            seq_lens=None, slot_tokens=keys, lru=lru, pool=pool, hot=hot,
+                            out_rows=out, ctx_stride=0, workspace=ws, miss_counts=counts, paged=paged)
+        o_out, o_cnt = oracle.swap_in(topk=topk, req_rows=rows, seq_lens=None, slot_tokens=o_keys,
+                                      lru=o_lru, pool=pool.numpy(), hot=o_hot, ctx_stride=0,
+                                      paged={"hot_block_table": hot_tab, "hot_block_size": hb})
+        torch.cuda.synchronize()
+        print(f"  paged cluster step {t}: {int(o_cnt.sum())} misses", flush=True)
+        assert np.array_equal(_np(out), o_out), f"step {t}: out_rows"
+        assert np.array_equal(_np(counts), o_cnt), f"step {t}: miss_counts"
         assert np.array_equal(_np(keys), o_keys), f"step {t}: slot keys"
         assert np.array_equal(_np(lru), o_lru), f"step {t}: lru"
         assert np.array_equal(_np(hot), o_hot), f"step {t}: hot buffer"
