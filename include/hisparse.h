@@ -211,10 +211,11 @@ size_t hs_swap_in_workspace_bytes(int32_t B, int32_t K);
  * table, the staged ids and outputs, and the old and new LRU rows all live
  * there). With the flat layout (no slot_rows, pool_rows or paged) and
  * ctx_stride <= 65536 the table is a direct-address table of ctx_stride int16
- * entries (the slot holding each position) when that fits; otherwise it is a
- * hash table of the top-k ids with 2K to 4K entries, and with 160 KB per
- * workgroup that allows K <= 4096 for H <= 8192, K <= 3016 at H = 16384 and
- * K <= 584 at H = 32768.
+ * entries (the slot holding each position) when that fits; with paged
+ * addressing it is a hash of the slots' keys with 2H to 4H entries when that
+ * fits; otherwise it is a hash table of the top-k ids with 2K to 4K entries,
+ * and with 160 KB per workgroup that allows K <= 4096 for H <= 8192,
+ * K <= 3016 at H = 16384 and K <= 584 at H = 32768.
  */
 int hisparse_swap_in(const hs_swap_in_args* args, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);

@@ -20,10 +20,11 @@
 //  * Membership (which top-k ids some slot holds) goes through an LDS table
 //    built per call. When the layout is flat and the table fits, it is a
 //    direct-address table over positions naming the slot that holds each
-//    one, and every id is looked up once. Otherwise the pending ids go into a
-//    bucketed hash (Knuth's multiplicative hash, rebuilt with a salted hash
-//    when a chain runs long) and every slot's token is probed. No result
-//    depends on which one runs.
+//    one, and every id is looked up once. With paged addressing the slots'
+//    keys go into a bucketed hash (Knuth's multiplicative hash, rebuilt with
+//    a salted hash when a chain runs long) and every id is looked up once
+//    there. Otherwise the pending ids go into that hash and every slot's
+//    token is probed. No result depends on which one runs.
 //  * swap_copy_kernel: the misses, published as a compact (pool row, hot row)
 //    list in the caller's workspace, are copied by many workgroups per
 //    request (1024-lane ones, two per CU, from an HBM pool; 256-lane ones
