@@ -63,6 +63,16 @@ def _random_cases(n):
 CASES += _random_cases(12)
 # more slots than one pass of the workgroup inserts into the paged key hash
 CASES.append(("host_key_hash_two_passes", 2, 2, 4500, 200, 12000, 16, "host", False, False, None))
+# Hot sizes whose key hash does not fit LDS beside the LRU row: a hash of the
+# pending global ids, probed with every slot's key. By the LDS arithmetic of
+# the plans: a quarter-full hash with the slot keys staged (H 8192, K 2048);
+# half full, staged, with K+V (H 12000); a quarter-full hash with the keys
+# read from HBM, on the split path (H 16384).
+CASES += [
+    ("host_pending_hash", 2, 2, 8192, 2048, 12000, 16, "host", False, False, 8),
+    ("host_pending_hash_half_full_kv", 2, 2, 12000, 2048, 16000, 16, "host", False, True, 4),
+    ("device_pending_hash_unstaged_split", 2, 1, 16384, 1024, 24000, 16, "device", True, False, 16),
+]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -201,20 +211,28 @@ def test_paged_full_size_dsv32():
         assert np.array_equal(_np(hot), o_hot), f"step {t}: hot buffer"
 
 
-def test_paged_keys_clustered_in_the_kernel_hash():
+@pytest.mark.parametrize("H,K,hb,bits,span,steps", [
+    # the key hash of the slots' keys: pow2(4H) entries in buckets of four, H
+    # buckets, picked by the top log2(H) = 10 bits of id * 2654435761 (mod 2^32)
+    (1024, 512, 16, 10, 200_000, 4),
+    # H 8192 leaves no room for the key hash: a quarter-full hash of the
+    # pending ids, pow2(4K) entries, 2048 buckets (top 11 bits), probed with
+    # every slot's key; eight steps, so that the last ones evict
+    (8192, 2048, 64, 11, 1_200_000, 8),
+], ids=["key_hash", "pending_id_hash"])
+def test_paged_keys_clustered_in_the_kernel_hash(H, K, hb, bits, span, steps):
     """Paged addressing without a source table (a position is its global id),
-    with ids that share the top bits of Knuth's multiplicative hash: the slots'
-    keys then crowd a few buckets of the key hash, inserts and lookups run past
-    the kernel's trip limit, the workgroup rebuilds the hash with the salted
-    hash, and every call still matches the oracle."""
+    with ids that share the top bits of Knuth's multiplicative hash: the keys
+    then crowd a few buckets of the table, inserts and lookups (or the probes)
+    run past the kernel's trip limit, the workgroup rebuilds the table with the
+    salted hash, and every call still matches the oracle."""
     import sparse_attention_kv_hisparse_amd as hs
     R = B = 2
-    H, K, hb, rb = 1024, 512, 16, 16
-    ids = np.arange(200_000, dtype=np.uint64)
-    # the key hash has pow2(4H) entries in buckets of four: H buckets, picked
-    # by the top log2(H) = 10 bits of id * 2654435761 (mod 2^32)
-    home = ((ids * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - 10)
-    cand = ids[home < 8].astype(np.int64)          # ids in 8 of the 1024 buckets
+    rb = 16
+    ids = np.arange(span, dtype=np.uint64)
+    home = ((ids * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - bits)
+    cand = ids[home < 8].astype(np.int64)          # ids in 8 of the 2^bits buckets
+    assert len(cand) >= 2 * K
     pool_nrows = int(cand.max()) + 1
     rng = np.random.default_rng(5)
     nhb = H // hb
@@ -234,7 +252,7 @@ def test_paged_keys_clustered_in_the_kernel_hash():
     o_hot = np.zeros((R * nhb * hb, rb), np.uint8)
     rows = np.arange(B, dtype=np.int64)
     prev = None
-    for t in range(4):
+    for t in range(steps):
         topk = np.stack([rng.choice(cand, size=K, replace=False) for _ in range(B)]).astype(np.int32)
         if prev is not None:
             topk[:, :K // 2] = prev[:, :K // 2]
