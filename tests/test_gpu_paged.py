@@ -77,12 +77,22 @@ CASES += [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_paged_swap_in_matches_oracle(case):
-    import sparse_attention_kv_hisparse_amd as hs
     name, R, B, H, K, ctx, rb, kind, split, kv, hb = case
     print(f"  paged {name}: R={R} B={B} H={H} K={K} rb={rb}", flush=True)
     rng = np.random.default_rng(zlib.crc32(name.encode()))   # the same tables in every process
-    S_r = H + 1
     paged_np, hot_nrows, pool_nrows = _random_tables(rng, R, H, ctx, hb)
+    run_paged_case(rng, name, R, B, H, K, ctx, rb, kind, split, kv, paged_np, hot_nrows, pool_nrows)
+
+
+def run_paged_case(rng, name, R, B, H, K, ctx, rb, kind, split, kv, paged_np, hot_nrows, pool_nrows,
+                   calls=8):
+    """`calls` calls on fresh state (every fourth an invalidation of random
+    written rows instead), each through the fused or the split path, with
+    random top-k rows over positions -3 .. ctx+4, a padded batch on the third
+    call, attention indices and the running counters; everything the call
+    writes is compared with the oracle after each call."""
+    import sparse_attention_kv_hisparse_amd as hs
+    S_r = H + 1
     cfg = gen.SwapConfig(name, B=B, H=H, K=K, ctx=pool_nrows, row_bytes=rb, steps=1, rho=0.5,
                          dist="uniform", pool_kind=kind, seed=61)
     pool = wdev.make_pool(cfg.with_(B=1), kind=kind)[:pool_nrows]
@@ -107,7 +117,7 @@ def test_paged_swap_in_matches_oracle(case):
     o_hot_v = np.zeros_like(o_hot) if kv else None
     stats = torch.zeros(2, dtype=torch.int64, device="cuda")
     o_stats = np.zeros(2, np.uint64)
-    for call in range(8):
+    for call in range(calls):
         if call % 4 == 3:
             rows = rng.integers(-1, R + 1, 40).astype(np.int64)
             written = np.array([o_keys[r % R, rng.integers(0, H)] for r in rows], np.int64)
