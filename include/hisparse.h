@@ -90,7 +90,8 @@ typedef enum {
  *   - with resident_block_table, a position whose block maps to p >= 0,
  *     p != resident_null_block, is resident in the device cache at row
  *     p * resident_block_size + t % resident_block_size and is output as is,
- *     with no slot or copy. As the vLLM page's host checks require, a
+ *     with no slot or copy (a row past INT32_MAX, which no int32 output can
+ *     hold, counts as not resident). As the vLLM page's host checks require, a
  *     resident table needs src_block_table, resident_block_size ==
  *     hot_block_size and resident_null_block >= 0 (HS_EINVAL otherwise);
  *   - an id with no row outputs -1; there is no newest-token slot and no

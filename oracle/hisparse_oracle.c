@@ -80,6 +80,9 @@ static void paged_translate(const oracle_swap_in_args *a, int64_t r, int64_t t, 
       if (pb != p->resident_null_block && pb >= 0)
         *res = pb * p->resident_block_size + t % p->resident_block_size;
     }
+    /* Rows are output as int32 (both pages store int32 rows): a resident row
+     * past INT32_MAX cannot be output, so its position is not resident. */
+    if (*res > INT32_MAX) *res = -1;
   }
 }
 

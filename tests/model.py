@@ -71,6 +71,8 @@ def lru_model_swap_in(*, topk, req_rows, seq_lens, slot_tokens, lru, pool, hot, 
             p = _paged_lookup(paged["resident_block_table"], bs, r, t)
             if p is not None and p >= 0 and p != paged["resident_null_block"]:
                 res = p * bs + t % bs
+            if res is not None and res >= 2**31:      # no int32 output can hold it
+                res = None
         return g, res
 
     def pool_of(r, t):

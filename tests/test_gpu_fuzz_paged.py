@@ -35,7 +35,8 @@ def paged_tables(rng, R, H, ctx, hb, sb, resident):
     source table of sb-row blocks (about 10% null or negative, block 0 never
     used as a real block, the pool's last block cut short) or none, and a
     resident table with the hot block size whose entries are mostly the null
-    block, some negative, some real blocks. Returns (paged, hot_nrows, pool_nrows)."""
+    block, some negative, some real blocks and a few blocks whose rows reach
+    or pass INT32_MAX. Returns (paged, hot_nrows, pool_nrows)."""
     nhb = -(-H // hb)
     extra = int(rng.integers(0, 4))
     hot_blocks = rng.permutation(R * nhb + extra)[:R * nhb].reshape(R, nhb).astype(np.int32)
@@ -56,6 +57,9 @@ def paged_tables(rng, R, H, ctx, hb, sb, resident):
         res[rng.random((R, nrb)) < 0.1] = -1
         hit = rng.random((R, nrb)) < 0.15
         res[hit] = rng.integers(0, 50, int(hit.sum()))
+        # blocks whose rows reach INT32_MAX or pass it (no int32 output can
+        # hold those: not resident)
+        res[rng.random((R, nrb)) < 0.05] = int(rng.choice([2**30, 2**31 - 1]))
         paged.update(resident_block_table=res, resident_block_size=hb, resident_null_block=null)
     return paged, hot_nrows, pool_nrows
 

@@ -159,6 +159,21 @@ def run_paged_case(rng, name, R, B, H, K, ctx, rb, kind, split, kv, paged_np, ho
             assert np.array_equal(_np(hot_v), o_hot_v), f"call {call}: V hot buffer"
 
 
+@pytest.mark.parametrize("hb,block", [(1, 2**31 - 1), (2, 2**30)], ids=["row_int32_max", "row_past_int32"])
+def test_paged_resident_rows_at_the_int32_limit(hb, block):
+    """Every fourth resident block names a row of exactly INT32_MAX (one-row
+    blocks: served as is) or rows past it (no int32 output can hold them: the
+    positions are looked up and copied like any other)."""
+    rng = np.random.default_rng(41 + hb)
+    R, B, H, K, ctx, rb = 3, 2, 16, 8, 120, 16
+    paged, hot_nrows, pool_nrows = _random_tables(rng, R, H, ctx, hb)
+    tab = paged["resident_block_table"].copy()
+    tab[:, ::4] = block
+    paged["resident_block_table"] = tab
+    run_paged_case(rng, f"resident_limit_{hb}", R, B, H, K, ctx, rb, "host", False, False, paged,
+                   hot_nrows, pool_nrows)
+
+
 def test_paged_full_size_dsv32():
     """The DeepSeek-V3.2-like shape (B=32, H=4096, K=2048, 32,768-token contexts,
     pinned-host pool) with vLLM-style addressing: 64-row source blocks (a seeded

@@ -67,6 +67,7 @@ MUTANTS = {
     "negative_pool_row_accepted": ("if (pr < 0 || pr >= a->pool_nrows) { out[i] = -1; continue; }",
                                    "if (pr >= a->pool_nrows) { out[i] = -1; continue; }"),
     "state_row_past_R_processed": ("if (b >= nreal || r < 0 || r >= a->R) {", "if (b >= nreal || r < 0) {"),
+    "resident_row_past_int32_served": ("    if (*res > INT32_MAX) *res = -1;\n", ""),
     "replay_negative_source_zeroed": ("if (s < 0 || d < 0 || d >= hot_nrows) continue;",
                                       "if (d < 0 || d >= hot_nrows) continue;\n        if (s < 0) { memset(hot_layers[l] + d * row_bytes, 0, (size_t)row_bytes); continue; }"),
 }
@@ -97,6 +98,7 @@ def _pins():
         ("paged_golden", pgt.test_paged_worked_example),
         ("paged_model", lambda: pgt.test_paged_matches_model(0)),
         ("state_row_past_R", ce.test_state_row_past_R_is_padding_with_otherwise_valid_ids),
+        ("resident_past_int32", pgt.test_resident_row_past_int32_is_not_resident),
     ]
     for name, fn in checks:
         try:

@@ -207,6 +207,57 @@ def test_paged_rejects_resident_tables_the_page_rejects(change):
     assert e.value.code == -1
 
 
+def _run_calls(paged, R, H, K, ctx, rb, pool_nrows, hot_nrows, seed, calls=4):
+    rng = np.random.default_rng(seed)
+    st, lru = gen.initial_state(R, H, H + 1)
+    pool = rng.integers(0, 256, (pool_nrows, rb), dtype=np.uint8)
+    hot = np.zeros((hot_nrows, rb), np.uint8)
+    seen = []
+    for _ in range(calls):
+        topk = np.stack([rng.permutation(np.arange(-2, ctx + 2))[:K] for _ in range(R)]).astype(np.int32)
+        att = np.zeros((R, K), np.int32)
+        out, cnt = oracle.swap_in(topk=topk, req_rows=np.arange(R, dtype=np.int64), seq_lens=None,
+                                  slot_tokens=st, lru=lru, pool=pool, hot=hot, ctx_stride=0,
+                                  paged=dict(paged, attention_indices=att, attention_block_stride=9))
+        seen.append((topk, out.copy(), cnt.copy(), att, st.copy(), lru.copy(), hot.copy()))
+    return seen
+
+
+def test_resident_row_past_int32_is_not_resident():
+    """A resident row that no int32 output can hold counts as no resident row:
+    every call gives exactly what it gives with the null block in those table
+    entries. A row of exactly INT32_MAX (one-row blocks) is still served."""
+    R, H, K, ctx, rb = 3, 16, 8, 120, 4
+    rng = np.random.default_rng(31)
+    paged, hot_nrows, pool_nrows = _random_tables(rng, R, H, ctx, hb=2)
+    res = paged["resident_block_table"]
+    huge = np.zeros_like(res, dtype=bool)
+    huge[:, ::3] = True                                  # every third block of each row
+    big = dict(paged, resident_block_table=np.where(huge, np.int32(2**30), res))   # rows >= 2^31
+    null = dict(paged, resident_block_table=np.where(huge, np.int32(paged["resident_null_block"]), res))
+    a = _run_calls(big, R, H, K, ctx, rb, pool_nrows, hot_nrows, seed=3)
+    b = _run_calls(null, R, H, K, ctx, rb, pool_nrows, hot_nrows, seed=3)
+    hit_huge = 0
+    for x, y in zip(a, b):
+        for u, v in zip(x[1:], y[1:]):
+            assert np.array_equal(u, v)
+        t = x[0]
+        hit_huge += int(sum(huge[r, t[r][(t[r] >= 0) & (t[r] < ctx)] // 2].sum() for r in range(R)))
+    assert hit_huge > 0                                  # the calls did name those blocks
+
+    # One-row blocks: block INT32_MAX is row INT32_MAX, an int32 output.
+    paged1, hot_nrows1, pool_nrows1 = _random_tables(np.random.default_rng(32), R, H, ctx, hb=1)
+    tab = paged1["resident_block_table"].copy()
+    tab[0, 5] = 2**31 - 1
+    st, lru = gen.initial_state(R, H, H + 1)
+    topk = np.tile(np.arange(5, 5 + K, dtype=np.int32), (R, 1))
+    out, _ = oracle.swap_in(topk=topk, req_rows=np.arange(R, dtype=np.int64), seq_lens=None,
+                            slot_tokens=st, lru=lru, pool=np.zeros((pool_nrows1, rb), np.uint8),
+                            hot=np.zeros((hot_nrows1, rb), np.uint8), ctx_stride=0,
+                            paged=dict(paged1, resident_block_table=tab))
+    assert out[0, 0] == 2**31 - 1
+
+
 def test_invalidate_matches_numpy():
     rng = np.random.default_rng(7)
     R, S_r, n = 6, 20, 40
