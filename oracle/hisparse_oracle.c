@@ -432,7 +432,7 @@ int64_t oracle_invalidate_written(int32_t *slot_keys, int64_t R, int64_t S_r, co
 
 int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,
                        int32_t H, int64_t S_r, int64_t R) {
-  if (!slot_tokens || !lru || !rows || n_rows < 0 || H < 0 || S_r < H) return ORACLE_EARG;
+  if (!slot_tokens || !lru || !rows || n_rows < 0 || H < 0 || S_r < (int64_t)H + 1) return ORACLE_EARG;
   for (int64_t j = 0; j < n_rows; ++j) {
     const int64_t r = rows[j];
     if (r < 0 || r >= R) return ORACLE_EARG;

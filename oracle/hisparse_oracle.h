@@ -167,7 +167,9 @@ int64_t oracle_store_kv_scatter(const uint8_t *src, int64_t src_row_stride_bytes
 int64_t oracle_invalidate_written(int32_t *slot_keys, int64_t R, int64_t S_r, const int64_t *rows,
                                   const int64_t *written, int64_t n);
 
-/* Initial state of the listed state rows: every token -1, LRU = 0..H-1. */
+/* Initial state of the listed state rows: every token -1, LRU = 0..H-1. Each
+ * row has its H LRU slots and the newest slot (S_r >= H + 1); rows outside
+ * [0, R) are an error. */
 int oracle_state_reset(int32_t *slot_tokens, int16_t *lru, const int64_t *rows, int64_t n_rows,
                        int32_t H, int64_t S_r, int64_t R);
 

@@ -105,7 +105,7 @@ def run_paged_case(rng, name, R, B, H, K, ctx, rb, kind, split, kv, paged_np, ho
     hot_v = torch.zeros_like(hot) if kv else None
     out = torch.empty((B, K), dtype=torch.int32, device="cuda")
     counts = torch.empty(B, dtype=torch.int32, device="cuda")
-    att = torch.empty((B, K + 3), dtype=torch.int32, device="cuda")
+    att = torch.full((B, K + 3), 7777, dtype=torch.int32, device="cuda")   # a tail past K
     ws = torch.zeros(hs.swap_in_workspace_bytes(B, K), dtype=torch.uint8, device="cuda")
     paged_dev = {k: (torch.as_tensor(v).cuda() if isinstance(v, np.ndarray) else v)
                  for k, v in paged_np.items()}
@@ -152,6 +152,7 @@ def run_paged_case(rng, name, R, B, H, K, ctx, rb, kind, split, kv, paged_np, ho
         assert np.array_equal(_np(out), o_out), f"call {call}: out_rows"
         assert np.array_equal(_np(counts), o_cnt), f"call {call}: miss_counts"
         assert np.array_equal(_np(att)[:, :K], o_att[:, :K]), f"call {call}: attention_indices"
+        assert (_np(att)[:, K:] == 7777).all(), f"call {call}: attention row tail written"
         assert np.array_equal(_np(keys), o_keys), f"call {call}: slot keys"
         assert np.array_equal(_np(lru), o_lru), f"call {call}: lru"
         assert np.array_equal(_np(hot), o_hot), f"call {call}: hot buffer"

@@ -166,6 +166,24 @@ def test_negative_pool_row_entries_are_invalid():
     assert seen_neg > 0
 
 
+def test_seq_len_past_the_row_stride():
+    """seq_len beyond ctx_stride: ids at or past the stride (the newest token
+    among them) have no pool row of their request and output -1, although the
+    pool has rows there (the next request's); the rest swap in as usual."""
+    h = _harness()
+    rng = np.random.default_rng(13)
+    cfg = _small(B=3, H=40, K=12, ctx=100, row_bytes=16)
+    run = h.ParityRun(cfg, R=3, pool_nrows=4 * cfg.ctx)
+    L = cfg.ctx + 7
+    for _ in range(4):
+        seq = np.full(3, L, np.int64)
+        rest = np.delete(np.arange(L), cfg.ctx)
+        topk = np.stack([np.concatenate([[cfg.ctx], rng.choice(rest, cfg.K - 1, replace=False)])
+                         for _ in range(3)]).astype(np.int32)
+        out, _ = run.step(topk, seq, check_invariants=True)
+        assert (out[:, 0] == -1).all()
+
+
 def test_strided_topk_rows():
     h = _harness()
     cfg = _small(B=5, H=70, K=33, ctx=400)
