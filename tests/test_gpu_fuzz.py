@@ -10,6 +10,8 @@ tables. Every call is compared with the oracle on outputs, counts, state, the
 running counters and the whole hot buffer (gpu_harness.ParityRun).
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -17,7 +19,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = int(os.environ.get("HS_FUZZ_CASES", 64))   # more seeds of the same draw on request
 H_CHOICES = [1, 2, 3, 7, 31, 63, 64, 65, 100, 255, 256, 1000, 1023, 1024, 2047, 4096, 4100, 5000]
 RB_CHOICES = [4, 8, 16, 48, 132, 656, 1152]
 POOL_CAP = 48 << 20   # bytes of pool per case

@@ -15,6 +15,8 @@ hot buffer (test_gpu_paged.run_paged_case), with an invalidation of written
 rows between calls.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -22,7 +24,7 @@ from test_gpu_paged import run_paged_case
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = int(os.environ.get("HS_FUZZ_PAGED_CASES", 32))   # more seeds of the same draw on request
 H_CHOICES = [1, 2, 7, 63, 64, 65, 255, 1000, 2047, 4096, 4500, 6000, 8192]
 HB_CHOICES = [1, 2, 3, 5, 7, 16, 64, 100]
 SB_CHOICES = [0, 1, 3, 4, 16, 64, 128]      # 0: no source block table
