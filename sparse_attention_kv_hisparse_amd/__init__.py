@@ -105,6 +105,8 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
             raise ValueError("pool_v / hot_v must be contiguous uint8 shaped like pool / hot")
         if not hot_v.is_cuda:
             raise ValueError("hot_v must be a device tensor")
+    if out_rows.dim() != 2:
+        raise ValueError("out_rows must be [B, K]")
     B, K = out_rows.shape
     if topk.dim() != 2 or topk.shape[0] != B or topk.shape[1] < K or topk.stride(1) != 1:
         raise ValueError("topk must be [B, >=K] with contiguous columns")
@@ -122,8 +124,6 @@ def hisparse_swap_in(*, topk: torch.Tensor, req_rows: torch.Tensor, seq_lens: to
     H = lru.shape[1]
     if lru.shape[0] != R:
         raise ValueError(f"lru has {lru.shape[0]} rows, slot_tokens {R}")
-    if tuple(out_rows.shape) != (B, K) or out_rows.dim() != 2:
-        raise ValueError("out_rows must be [B, K]")
     _vec(req_rows, B, "req_rows")
     _vec(seq_lens, B, "seq_lens")
     _vec(miss_counts, B, "miss_counts")
